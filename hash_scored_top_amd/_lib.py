@@ -1,0 +1,316 @@
+"""ctypes binding of libhst (the C ABI declared in include/hst.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libhst.so.  PyTorch supplies device memory (outputs and
+workspace) and the current stream.  If the library is missing this module
+raises at import time; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhst.so")
+
+HST_OK, HST_ERR_INVALID_ARG, HST_ERR_UNSUPPORTED, HST_ERR_WORKSPACE, HST_ERR_HIP = 0, -1, -2, -3, -4
+HST_F32, HST_BF16, HST_F16, HST_I32 = 0, 1, 2, 3
+(HST_OP_HASH_SOFTLSH, HST_OP_HASH_BINARY, HST_OP_SCORE_SOFTLSH, HST_OP_SCORE_HAMMING,
+ HST_OP_SELECT_TOPK, HST_OP_SPARSE_ATTENTION, HST_OP_DECODE_SOFTLSH,
+ HST_OP_DECODE_HAMMING) = range(8)
+
+EXPORTED = (
+    "hst_version", "hst_status_string", "hst_last_hip_error", "hst_workspace_size",
+    "hst_hash_keys_softlsh", "hst_hash_keys_binary", "hst_score_keys_softlsh",
+    "hst_score_keys_hamming", "hst_select_topk", "hst_sparse_decode_attention",
+    "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
+    "hst_score_scan_softlsh",
+)
+
+
+class HstShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("Nmax", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+class HstError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _C.hst_status_string(status).decode()
+        if status == HST_ERR_HIP:
+            msg += f" (hipError {_C.hst_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    SH = ctypes.POINTER(HstShape)
+    sig = {
+        "hst_version": ([], I),
+        "hst_status_string": ([I], ctypes.c_char_p),
+        "hst_last_hip_error": ([], I),
+        "hst_workspace_size": ([I, SH, I, I, I, I, ctypes.POINTER(SZ)], I),
+        "hst_hash_keys_softlsh": ([SH, P, P, P, I, I, I, P, P, P], I),
+        "hst_hash_keys_binary": ([SH, P, P, I, P, P], I),
+        "hst_score_keys_softlsh": ([SH, P, P, I, I, F, P, P, I, P, P, SZ, P], I),
+        "hst_score_keys_hamming": ([SH, P, P, I, P, P, P, SZ, P], I),
+        "hst_query_tables_softlsh": ([SH, P, P, I, I, F, P, P], I),
+        "hst_score_scan_softlsh": ([SH, P, I, I, P, P, I, P, P], I),
+        "hst_select_topk": ([SH, I, P, I, P, P, P, SZ, P], I),
+        "hst_sparse_decode_attention": ([SH, P, P, P, P, I, F, P, P, P, SZ, P], I),
+        "hst_decode_step_softlsh": ([SH, P, P, P, P, I, I, F, P, P, I, I, P, F, P, P, P, P, SZ, P], I),
+        "hst_decode_step_hamming": ([SH, P, P, P, P, I, P, I, P, F, P, P, P, P, SZ, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_C = _load()
+
+
+# --------------------------------------------------------------------- helpers
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libhst must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> Optional[int]:
+    if device.type != "cuda":
+        return None
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _kv_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return HST_F32
+    if dtype == torch.bfloat16:
+        return HST_BF16
+    raise ValueError(f"unsupported K/V dtype {dtype}")
+
+
+def _norm_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float16:
+        return HST_F16
+    if dtype == torch.float32:
+        return HST_F32
+    raise ValueError(f"unsupported value-norm dtype {dtype}")
+
+
+def make_shape(K: torch.Tensor, Hq: int, seq_lens: Optional[torch.Tensor] = None) -> HstShape:
+    """Shape descriptor from a [B, Hkv, Nmax, d] key cache."""
+    B, Hkv, Nmax, d = K.shape
+    if seq_lens is not None and seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    return HstShape(B, Hq, Hkv, d, Nmax, _kv_code(K.dtype), _ptr(seq_lens))
+
+
+def _check(status: int, where: str) -> None:
+    if status != HST_OK:
+        raise HstError(status, where)
+
+
+def workspace_size(op: int, shape: HstShape, L: int = 0, P: int = 0, code_bits: int = 128,
+                   k: int = 1) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_C.hst_workspace_size(op, ctypes.byref(shape), L, P, code_bits, k, ctypes.byref(out)),
+           "hst_workspace_size")
+    return out.value
+
+
+def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- entry points
+
+def hst_hash_keys_softlsh(K, V, W, L: int, P: int, norm_dtype=torch.float16,
+                          seq_lens=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bucket ids [B,Hkv,Nmax,L] uint8 and value norms [B,Hkv,Nmax]."""
+    B, Hkv, Nmax, d = K.shape
+    shape = make_shape(K, Hkv, seq_lens)
+    ids = torch.zeros((B, Hkv, Nmax, L), dtype=torch.uint8, device=K.device)
+    vnorm = torch.zeros((B, Hkv, Nmax), dtype=norm_dtype, device=K.device)
+    _check(_C.hst_hash_keys_softlsh(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(W), L, P,
+                                    _norm_code(norm_dtype), _ptr(ids), _ptr(vnorm),
+                                    _stream(K.device)), "hst_hash_keys_softlsh")
+    return ids, vnorm
+
+
+def hst_hash_keys_binary(K, R, code_bits: int = 128, seq_lens=None) -> torch.Tensor:
+    """Binary codes [B,Hkv,Nmax,code_bits/32] int32 (uint32 bit patterns)."""
+    B, Hkv, Nmax, d = K.shape
+    shape = make_shape(K, Hkv, seq_lens)
+    codes = torch.zeros((B, Hkv, Nmax, code_bits // 32), dtype=torch.int32, device=K.device)
+    _check(_C.hst_hash_keys_binary(ctypes.byref(shape), _ptr(K), _ptr(R), code_bits,
+                                   _ptr(codes), _stream(K.device)), "hst_hash_keys_binary")
+    return codes
+
+
+def hst_score_keys_softlsh(q, W, L: int, P: int, tau: float, ids, vnorm, Nmax_like,
+                           seq_lens=None) -> torch.Tensor:
+    """Soft-collision scores [B,Hkv,Nmax] float32; Nmax_like is the K cache."""
+    B, Hq, d = q.shape
+    shape = make_shape(Nmax_like, Hq, seq_lens)
+    scores = torch.zeros((shape.B, shape.Hkv, shape.Nmax), dtype=torch.float32, device=q.device)
+    ws = _workspace(workspace_size(HST_OP_SCORE_SOFTLSH, shape, L, P), q.device)
+    _check(_C.hst_score_keys_softlsh(ctypes.byref(shape), _ptr(q), _ptr(W), L, P, float(tau),
+                                     _ptr(ids), _ptr(vnorm), _norm_code(vnorm.dtype),
+                                     _ptr(scores), _ptr(ws), ws.numel(), _stream(q.device)),
+           "hst_score_keys_softlsh")
+    return scores
+
+
+def hst_query_tables_softlsh(q, W, L: int, P: int, tau: float, Nmax_like,
+                             seq_lens=None) -> torch.Tensor:
+    """Bucket-probability tables [B,Hkv,L,2^P] float32."""
+    B, Hq, d = q.shape
+    shape = make_shape(Nmax_like, Hq, seq_lens)
+    tables = torch.empty((shape.B, shape.Hkv, L, 1 << P), dtype=torch.float32, device=q.device)
+    _check(_C.hst_query_tables_softlsh(ctypes.byref(shape), _ptr(q), _ptr(W), L, P, float(tau),
+                                       _ptr(tables), _stream(q.device)),
+           "hst_query_tables_softlsh")
+    return tables
+
+
+def hst_score_scan_softlsh(tables, ids, vnorm, Nmax_like, Hq: int, seq_lens=None,
+                           scores=None, stream=None) -> torch.Tensor:
+    """Score scan over precomputed tables: [B,Hkv,Nmax] float32."""
+    B, Hkv, L, nb = tables.shape
+    shape = make_shape(Nmax_like, Hq, seq_lens)
+    if scores is None:
+        scores = torch.zeros((shape.B, shape.Hkv, shape.Nmax), dtype=torch.float32,
+                             device=tables.device)
+    st = _stream(tables.device) if stream is None else stream
+    _check(_C.hst_score_scan_softlsh(ctypes.byref(shape), _ptr(tables), L, nb.bit_length() - 1,
+                                     _ptr(ids), _ptr(vnorm), _norm_code(vnorm.dtype),
+                                     _ptr(scores), st), "hst_score_scan_softlsh")
+    return scores
+
+
+def hst_score_keys_hamming(q, R, codes, Nmax_like, code_bits: int = 128,
+                           seq_lens=None) -> torch.Tensor:
+    """Code-similarity scores [B,Hkv,Nmax] int32."""
+    B, Hq, d = q.shape
+    shape = make_shape(Nmax_like, Hq, seq_lens)
+    scores = torch.zeros((shape.B, shape.Hkv, shape.Nmax), dtype=torch.int32, device=q.device)
+    ws = _workspace(workspace_size(HST_OP_SCORE_HAMMING, shape), q.device)
+    _check(_C.hst_score_keys_hamming(ctypes.byref(shape), _ptr(q), _ptr(R), code_bits,
+                                     _ptr(codes), _ptr(scores), _ptr(ws), ws.numel(),
+                                     _stream(q.device)), "hst_score_keys_hamming")
+    return scores
+
+
+def hst_select_topk(scores, k: int, Hq: int, d: int, kv_dtype=torch.bfloat16,
+                    k_per_seq=None, seq_lens=None) -> torch.Tensor:
+    """Top-k indices [B,Hkv,k] int32, ascending, -1 padded."""
+    B, Hkv, Nmax = scores.shape
+    shape = HstShape(B, Hq, Hkv, d, Nmax, _kv_code(kv_dtype), _ptr(seq_lens))
+    sd = HST_F32 if scores.dtype == torch.float32 else HST_I32
+    if scores.dtype not in (torch.float32, torch.int32):
+        raise ValueError("scores must be float32 or int32")
+    idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=scores.device)
+    ws = _workspace(workspace_size(HST_OP_SELECT_TOPK, shape, k=k), scores.device)
+    _check(_C.hst_select_topk(ctypes.byref(shape), sd, _ptr(scores), k, _ptr(k_per_seq),
+                              _ptr(idx), _ptr(ws), ws.numel(), _stream(scores.device)),
+           "hst_select_topk")
+    return idx
+
+
+def hst_sparse_decode_attention(q, K, V, idx, scale: Optional[float] = None, seq_lens=None,
+                                want_lse: bool = True):
+    """Attention over selected rows: out [B,Hq,d] float32, lse [B,Hq] float32."""
+    B, Hq, d = q.shape
+    shape = make_shape(K, Hq, seq_lens)
+    k = idx.shape[-1]
+    if scale is None:
+        scale = d ** -0.5
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = _workspace(workspace_size(HST_OP_SPARSE_ATTENTION, shape, k=k), q.device)
+    _check(_C.hst_sparse_decode_attention(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V),
+                                          _ptr(idx), k, float(scale), _ptr(out), _ptr(lse),
+                                          _ptr(ws), ws.numel(), _stream(q.device)),
+           "hst_sparse_decode_attention")
+    return out, lse
+
+
+class DecodeSoftLSH:
+    """Pre-sized soft-LSH decode step: outputs and workspace allocated once."""
+
+    def __init__(self, K, Hq: int, L: int, P: int, tau: float, k: int, norm_dtype,
+                 seq_lens=None, k_per_seq=None, scale: Optional[float] = None):
+        B, Hkv, Nmax, d = K.shape
+        self.shape = make_shape(K, Hq, seq_lens)
+        self._keep = (seq_lens, k_per_seq)
+        self.L, self.P, self.tau, self.k = L, P, float(tau), k
+        self.norm_code = _norm_code(norm_dtype)
+        self.scale = float(d ** -0.5 if scale is None else scale)
+        dev = K.device
+        self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.ws = _workspace(workspace_size(HST_OP_DECODE_SOFTLSH, self.shape, L, P, k=k), dev)
+        self.k_per_seq = k_per_seq
+
+    def __call__(self, q, K, V, W, ids, vnorm, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_step_softlsh(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), _ptr(W), self.L, self.P,
+            self.tau, _ptr(ids), _ptr(vnorm), self.norm_code, self.k, _ptr(self.k_per_seq),
+            self.scale, _ptr(self.idx), _ptr(self.out), _ptr(self.lse), _ptr(self.ws),
+            self.ws.numel(), st), "hst_decode_step_softlsh")
+        return self.idx, self.out, self.lse
+
+
+class DecodeHamming:
+    """Pre-sized binary-code decode step."""
+
+    def __init__(self, K, Hq: int, k: int, code_bits: int = 128, seq_lens=None, k_per_seq=None,
+                 scale: Optional[float] = None):
+        B, Hkv, Nmax, d = K.shape
+        self.shape = make_shape(K, Hq, seq_lens)
+        self._keep = (seq_lens, k_per_seq)
+        self.k, self.code_bits = k, code_bits
+        self.scale = float(d ** -0.5 if scale is None else scale)
+        dev = K.device
+        self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.ws = _workspace(workspace_size(HST_OP_DECODE_HAMMING, self.shape, k=k), dev)
+        self.k_per_seq = k_per_seq
+
+    def __call__(self, q, K, V, R, codes, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_step_hamming(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), _ptr(R), self.code_bits,
+            _ptr(codes), self.k, _ptr(self.k_per_seq), self.scale, _ptr(self.idx),
+            _ptr(self.out), _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st),
+            "hst_decode_step_hamming")
+        return self.idx, self.out, self.lse
+
+
+def hst_decode_step_softlsh(q, K, V, W, ids, vnorm, L: int, P: int, tau: float, k: int,
+                            seq_lens=None, k_per_seq=None, scale=None):
+    step = DecodeSoftLSH(K, q.shape[1], L, P, tau, k, vnorm.dtype, seq_lens, k_per_seq, scale)
+    return step(q, K, V, W, ids, vnorm)
+
+
+def hst_decode_step_hamming(q, K, V, R, codes, k: int, seq_lens=None, k_per_seq=None,
+                            scale=None):
+    step = DecodeHamming(K, q.shape[1], k, 128, seq_lens, k_per_seq, scale)
+    return step(q, K, V, R, codes)

@@ -1,0 +1,311 @@
+// C ABI of libhst: argument validation, workspace layout and launch order.
+// Validation is pure host logic and finishes before anything is enqueued.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "hst.h"
+#include "hst_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+hst_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return HST_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return HST_ERR_HIP;
+}
+
+hst_status check_shape(const hst_shape* s) {
+  if (s == nullptr) return HST_ERR_INVALID_ARG;
+  if (s->B < 1 || s->Hkv < 1 || s->Hq < 1 || s->Nmax < 1 || s->d < 1) return HST_ERR_INVALID_ARG;
+  if (s->Hq % s->Hkv != 0) return HST_ERR_INVALID_ARG;
+  if (s->kv_dtype != HST_F32 && s->kv_dtype != HST_BF16) return HST_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 128) return HST_ERR_UNSUPPORTED;
+  if (static_cast<long long>(s->B) * s->Hkv > 65535) return HST_ERR_UNSUPPORTED;
+  if (static_cast<long long>(s->B) * s->Hq > 0x7fffffffLL) return HST_ERR_UNSUPPORTED;
+  if (s->Nmax > (1 << 30)) return HST_ERR_UNSUPPORTED;
+  if (s->seq_lens != nullptr && !aligned16(s->seq_lens)) return HST_ERR_INVALID_ARG;
+  return HST_OK;
+}
+
+hst_status check_lp(int L, int P) {
+  if (L < 1 || P < 1) return HST_ERR_INVALID_ARG;
+  if (P > 8 || L > 128 || (static_cast<long long>(L) << P) > 16384) return HST_ERR_UNSUPPORTED;
+  return HST_OK;
+}
+
+hst_status check_norm_dtype(int nd) {
+  if (nd != HST_F16 && nd != HST_F32) return HST_ERR_UNSUPPORTED;
+  return HST_OK;
+}
+
+int group(const hst_shape* s) { return s->Hq / s->Hkv; }
+
+size_t tables_bytes(const hst_shape* s, int L, int P) {
+  return static_cast<size_t>(s->B) * s->Hkv * (static_cast<size_t>(L) << P) * sizeof(float);
+}
+size_t qcodes_bytes(const hst_shape* s) {
+  return static_cast<size_t>(s->B) * s->Hq * 4 * sizeof(uint32_t);
+}
+size_t scores_bytes(const hst_shape* s) {
+  return static_cast<size_t>(s->B) * s->Hkv * s->Nmax * sizeof(float);
+}
+
+#define HST_TRY(x)                       \
+  do {                                   \
+    hst_status _st = (x);                \
+    if (_st != HST_OK) return _st;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int hst_version(void) { return 100; }
+
+const char* hst_status_string(int status) {
+  switch (status) {
+    case HST_OK: return "HST_OK";
+    case HST_ERR_INVALID_ARG: return "HST_ERR_INVALID_ARG: invalid argument";
+    case HST_ERR_UNSUPPORTED: return "HST_ERR_UNSUPPORTED: unsupported shape or dtype";
+    case HST_ERR_WORKSPACE: return "HST_ERR_WORKSPACE: workspace too small";
+    case HST_ERR_HIP: return "HST_ERR_HIP: HIP launch failed";
+    default: return "unknown hst_status";
+  }
+}
+
+int hst_last_hip_error(void) { return g_last_hip_error; }
+
+hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int code_bits, int k,
+                              size_t* bytes) {
+  if (bytes == nullptr) return HST_ERR_INVALID_ARG;
+  HST_TRY(check_shape(shape));
+  const bool soft = op == HST_OP_SCORE_SOFTLSH || op == HST_OP_DECODE_SOFTLSH ||
+                    op == HST_OP_HASH_SOFTLSH;
+  const bool bin = op == HST_OP_SCORE_HAMMING || op == HST_OP_DECODE_HAMMING ||
+                   op == HST_OP_HASH_BINARY;
+  if (soft) HST_TRY(check_lp(L, P));
+  if (bin && code_bits != 128) return HST_ERR_UNSUPPORTED;
+  const bool needk = op == HST_OP_SELECT_TOPK || op == HST_OP_SPARSE_ATTENTION ||
+                     op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING;
+  if (needk && k < 1) return HST_ERR_INVALID_ARG;
+  size_t b = 0;
+  switch (op) {
+    case HST_OP_HASH_SOFTLSH:
+    case HST_OP_HASH_BINARY: b = 0; break;
+    case HST_OP_SCORE_SOFTLSH: b = align_up(tables_bytes(shape, L, P)); break;
+    case HST_OP_SCORE_HAMMING: b = align_up(qcodes_bytes(shape)); break;
+    case HST_OP_SELECT_TOPK: b = align_up(hst::select_ws_bytes(*shape)); break;
+    case HST_OP_SPARSE_ATTENTION: b = align_up(hst::attention_ws_bytes(*shape, k)); break;
+    case HST_OP_DECODE_SOFTLSH:
+      b = align_up(tables_bytes(shape, L, P)) + align_up(scores_bytes(shape)) +
+          align_up(hst::select_ws_bytes(*shape)) + align_up(hst::attention_ws_bytes(*shape, k));
+      break;
+    case HST_OP_DECODE_HAMMING:
+      b = align_up(qcodes_bytes(shape)) + align_up(scores_bytes(shape)) +
+          align_up(hst::select_ws_bytes(*shape)) + align_up(hst::attention_ws_bytes(*shape, k));
+      break;
+    default: return HST_ERR_INVALID_ARG;
+  }
+  *bytes = b;
+  return HST_OK;
+}
+
+hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K, const void* V,
+                                 const void* W, int L, int P, int norm_dtype, uint8_t* ids,
+                                 void* vnorm, void* stream) {
+  HST_TRY(check_shape(shape));
+  HST_TRY(check_lp(L, P));
+  HST_TRY(check_norm_dtype(norm_dtype));
+  if (!ptr_ok(K) || !ptr_ok(V) || !ptr_ok(W) || !ptr_ok(ids) || !ptr_ok(vnorm))
+    return HST_ERR_INVALID_ARG;
+  return hip_status(hst::launch_hash_softlsh(*shape, K, V, W, L, P, norm_dtype, ids, vnorm,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K, const void* R,
+                                int code_bits, uint32_t* codes, void* stream) {
+  HST_TRY(check_shape(shape));
+  if (code_bits != 128) return HST_ERR_UNSUPPORTED;
+  if (!ptr_ok(K) || !ptr_ok(R) || !ptr_ok(codes)) return HST_ERR_INVALID_ARG;
+  return hip_status(
+      hst::launch_hash_binary(*shape, K, R, codes, static_cast<hipStream_t>(stream)));
+}
+
+static hst_status score_softlsh_checks(const hst_shape* shape, const void* q, const void* W, int L,
+                                       int P, float tau, const uint8_t* ids, const void* vnorm,
+                                       int norm_dtype) {
+  HST_TRY(check_shape(shape));
+  HST_TRY(check_lp(L, P));
+  HST_TRY(check_norm_dtype(norm_dtype));
+  if (!(tau > 0.f) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
+  if (group(shape) * shape->d > 4096) return HST_ERR_UNSUPPORTED;
+  if (!ptr_ok(q) || !ptr_ok(W) || !ptr_ok(ids) || !ptr_ok(vnorm)) return HST_ERR_INVALID_ARG;
+  return HST_OK;
+}
+
+static hst_status score_hamming_checks(const hst_shape* shape, const void* q, const void* R,
+                                       int code_bits, const uint32_t* codes) {
+  HST_TRY(check_shape(shape));
+  if (code_bits != 128) return HST_ERR_UNSUPPORTED;
+  if (group(shape) > 64) return HST_ERR_UNSUPPORTED;
+  if (!ptr_ok(q) || !ptr_ok(R) || !ptr_ok(codes)) return HST_ERR_INVALID_ARG;
+  return HST_OK;
+}
+
+static hst_status attention_checks(const hst_shape* shape, const void* q, const void* K,
+                                   const void* V, int k, float scale, float* out, float* lse) {
+  HST_TRY(check_shape(shape));
+  if (group(shape) > 8) return HST_ERR_UNSUPPORTED;
+  if (k < 1 || !isfinite(scale)) return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(q) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(out)) return HST_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned16(lse)) return HST_ERR_INVALID_ARG;
+  return HST_OK;
+}
+
+static hst_status workspace_check(int op, const hst_shape* shape, int L, int P, int k, void* ws,
+                                  size_t ws_bytes) {
+  size_t need = 0;
+  HST_TRY(hst_workspace_size(op, shape, L, P, 128, k, &need));
+  if (ws_bytes < need) return HST_ERR_WORKSPACE;
+  if (need > 0 && (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0))
+    return HST_ERR_INVALID_ARG;
+  return HST_OK;
+}
+
+hst_status hst_score_keys_softlsh(const hst_shape* shape, const void* q, const void* W, int L,
+                                  int P, float tau, const uint8_t* ids, const void* vnorm,
+                                  int norm_dtype, float* scores, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  if (!ptr_ok(scores)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_SCORE_SOFTLSH, shape, L, P, 1, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* tables = static_cast<float*>(ws);
+  HST_TRY(hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables, st)));
+  return hip_status(
+      hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype, scores, st));
+}
+
+hst_status hst_query_tables_softlsh(const hst_shape* shape, const void* q, const void* W, int L,
+                                    int P, float tau, float* tables, void* stream) {
+  HST_TRY(check_shape(shape));
+  HST_TRY(check_lp(L, P));
+  if (!(tau > 0.f) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
+  if (group(shape) * shape->d > 4096) return HST_ERR_UNSUPPORTED;
+  if (!ptr_ok(q) || !ptr_ok(W) || !ptr_ok(tables)) return HST_ERR_INVALID_ARG;
+  return hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_score_scan_softlsh(const hst_shape* shape, const float* tables, int L, int P,
+                                  const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                  float* scores, void* stream) {
+  HST_TRY(check_shape(shape));
+  HST_TRY(check_lp(L, P));
+  HST_TRY(check_norm_dtype(norm_dtype));
+  if (!ptr_ok(tables) || !ptr_ok(ids) || !ptr_ok(vnorm) || !ptr_ok(scores))
+    return HST_ERR_INVALID_ARG;
+  return hip_status(hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype,
+                                              scores, static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_score_keys_hamming(const hst_shape* shape, const void* q, const void* R,
+                                  int code_bits, const uint32_t* codes, int32_t* scores, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  HST_TRY(score_hamming_checks(shape, q, R, code_bits, codes));
+  if (!ptr_ok(scores)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_SCORE_HAMMING, shape, 0, 0, 1, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* qc = static_cast<uint32_t*>(ws);
+  HST_TRY(hip_status(hst::launch_query_codes(*shape, q, R, qc, st)));
+  return hip_status(hst::launch_score_hamming(*shape, qc, codes, scores, st));
+}
+
+hst_status hst_select_topk(const hst_shape* shape, int score_dtype, const void* scores, int k,
+                           const int32_t* k_per_seq, int32_t* idx, void* ws, size_t ws_bytes,
+                           void* stream) {
+  HST_TRY(check_shape(shape));
+  if (score_dtype != HST_F32 && score_dtype != HST_I32) return HST_ERR_UNSUPPORTED;
+  if (k < 1) return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(scores) || !ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_SELECT_TOPK, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::launch_select(*shape, score_dtype, scores, k, k_per_seq, idx, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q, const void* K,
+                                       const void* V, const int32_t* idx, int k, float scale,
+                                       float* out, float* lse, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_SPARSE_ATTENTION, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, ws,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q, const void* K,
+                                   const void* V, const void* W, int L, int P, float tau,
+                                   const uint8_t* ids, const void* vnorm, int norm_dtype, int k,
+                                   const int32_t* k_per_seq, float scale, int32_t* idx,
+                                   float* out, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH, shape, L, P, k, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* p = static_cast<char*>(ws);
+  float* tables = reinterpret_cast<float*>(p);
+  p += align_up(tables_bytes(shape, L, P));
+  float* scores = reinterpret_cast<float*>(p);
+  p += align_up(scores_bytes(shape));
+  void* sel_ws = p;
+  p += align_up(hst::select_ws_bytes(*shape));
+  void* attn_ws = p;
+  HST_TRY(hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables, st)));
+  HST_TRY(hip_status(
+      hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype, scores, st)));
+  HST_TRY(hip_status(hst::launch_select(*shape, HST_F32, scores, k, k_per_seq, idx, sel_ws, st)));
+  return hip_status(
+      hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, attn_ws, st));
+}
+
+hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const void* K,
+                                   const void* V, const void* R, int code_bits,
+                                   const uint32_t* codes, int k, const int32_t* k_per_seq,
+                                   float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  HST_TRY(score_hamming_checks(shape, q, R, code_bits, codes));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* p = static_cast<char*>(ws);
+  uint32_t* qc = reinterpret_cast<uint32_t*>(p);
+  p += align_up(qcodes_bytes(shape));
+  int32_t* scores = reinterpret_cast<int32_t*>(p);
+  p += align_up(scores_bytes(shape));
+  void* sel_ws = p;
+  p += align_up(hst::select_ws_bytes(*shape));
+  void* attn_ws = p;
+  HST_TRY(hip_status(hst::launch_query_codes(*shape, q, R, qc, st)));
+  HST_TRY(hip_status(hst::launch_score_hamming(*shape, qc, codes, scores, st)));
+  HST_TRY(hip_status(hst::launch_select(*shape, HST_I32, scores, k, k_per_seq, idx, sel_ws, st)));
+  return hip_status(
+      hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, attn_ws, st));
+}
+
+}  // extern "C"

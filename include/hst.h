@@ -1,0 +1,236 @@
+/*
+ * hst.h - C ABI of the hash-scored top-k sparse decode attention library
+ * (libhst.so, MI355X / gfx950).
+ *
+ * One decode step of one attention layer: every cached key is scored cheaply
+ * against the query from metadata computed once at prefill, the top-k keys of
+ * each kv head are selected, and exact softmax attention runs over the
+ * gathered K/V rows of that subset only.
+ *
+ * Method sources (web pages, cited by title and section):
+ *   [SOCKET] "SOCKET - SOft Collision Kernel EsTimator" technical overview
+ *            (gist.science), section "Core mechanism: soft LSH", items 1-4,
+ *            and section "Experimental results" (metadata = bucket ids plus
+ *            value norms, about 15% over the KV cache).
+ *   [HATA]   "HATA: Hash-Aware Top-k Attention" explainer (aibr.jp),
+ *            section 3 "core technical elements": binary codes for queries
+ *            and keys, ranking by code comparison.  The learned hash is
+ *            replaced by the sign of a caller-supplied projection.
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them.  Memory needed beyond
+ *     inputs and outputs is a caller-owned workspace whose size
+ *     hst_workspace_size() reports.
+ *   - Layouts are dense row-major C arrays:
+ *       K, V     [B][Hkv][Nmax][d]   element type shape->kv_dtype
+ *       q        [B][Hq][d]          element type shape->kv_dtype
+ *       W        [Hkv][L*P][d]       soft-LSH hyperplanes, row l*P + p
+ *       R        [Hkv][code_bits][d] binary-code projections
+ *       ids      [B][Hkv][Nmax][L]   uint8 bucket ids (bit p = hyperplane p)
+ *       vnorm    [B][Hkv][Nmax]      value norms, norm_dtype (F16 or F32)
+ *       codes    [B][Hkv][Nmax][code_bits/32] uint32 (bit i in word i/32,
+ *                                    position i%32)
+ *       scores   [B][Hkv][Nmax]      F32 (soft) or I32 (binary)
+ *       idx      [B][Hkv][k]         int32, ascending, -1 after the count
+ *       out      [B][Hq][d]          float32
+ *       lse      [B][Hq]             float32 (natural log), nullable
+ *     Query head hq reads kv head hq / (Hq / Hkv) (grouped-query attention).
+ *   - shape->seq_lens is an optional DEVICE array [B] of context lengths
+ *     N_b in [0, Nmax]; NULL means every N_b = Nmax.  Rows j >= N_b are
+ *     never read or written by any call.
+ *   - Pointers must be 16-byte aligned.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and never synchronizes.  Arguments are validated on the
+ *     host before anything is enqueued; on error nothing is launched.
+ *   - Calls are reentrant; the library holds no mutable global state except
+ *     the thread-local last HIP error.
+ */
+#ifndef HST_H_
+#define HST_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HST_OK = 0,
+  HST_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment        */
+  HST_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, d, P ...)  */
+  HST_ERR_WORKSPACE = -3,   /* workspace smaller than hst_workspace_size() */
+  HST_ERR_HIP = -4          /* a HIP launch failed: see hst_last_hip_error */
+} hst_status;
+
+typedef enum { HST_F32 = 0, HST_BF16 = 1, HST_F16 = 2, HST_I32 = 3 } hst_dtype;
+
+typedef struct {
+  int32_t B;                /* sequences in the batch, >= 1                */
+  int32_t Hq;               /* query heads, multiple of Hkv                */
+  int32_t Hkv;              /* kv heads, >= 1                              */
+  int32_t d;                /* head dim: 64 or 128                         */
+  int32_t Nmax;             /* cache capacity per sequence, >= 1           */
+  int32_t kv_dtype;         /* hst_dtype of K, V, q, W, R: F32 or BF16     */
+  const int32_t* seq_lens;  /* device [B] or NULL                          */
+} hst_shape;
+
+typedef enum {
+  HST_OP_HASH_SOFTLSH = 0,
+  HST_OP_HASH_BINARY = 1,
+  HST_OP_SCORE_SOFTLSH = 2,
+  HST_OP_SCORE_HAMMING = 3,
+  HST_OP_SELECT_TOPK = 4,
+  HST_OP_SPARSE_ATTENTION = 5,
+  HST_OP_DECODE_SOFTLSH = 6,
+  HST_OP_DECODE_HAMMING = 7
+} hst_op;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int hst_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* hst_status_string(int status);
+
+/* hipError_t of the last HST_ERR_HIP on the calling thread (0 if none). */
+int hst_last_hip_error(void);
+
+/*
+ * Workspace bytes the given op needs for this shape.  L, P describe the
+ * soft-LSH tables (ignored otherwise), code_bits the binary codes (ignored
+ * otherwise), k the idx row capacity (select, attention, decode).
+ * Returns HST_ERR_INVALID_ARG / HST_ERR_UNSUPPORTED for shapes the op rejects.
+ */
+hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P,
+                              int code_bits, int k, size_t* bytes);
+
+/*
+ * Prefill hashing of keys into soft-LSH bucket ids and cached value norms
+ * [SOCKET, core mechanism item 1].
+ *   ids[b][h][j][l] = sum_p [ W[h][l*P+p] . K[b][h][j] >= 0 ] << p
+ * The sign is that of the exact real dot product of the stored values (a
+ * zero projection sets the bit).  vnorm[b][h][j] = ||V[b][h][j]||_2 rounded
+ * to nearest-even in norm_dtype (F16 or F32).
+ * Requires 1 <= P <= 8, 1 <= L <= 128, L * 2^P <= 16384.  No workspace.
+ */
+hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K,
+                                 const void* V, const void* W, int L, int P,
+                                 int norm_dtype, uint8_t* ids, void* vnorm,
+                                 void* stream);
+
+/*
+ * Prefill binary codes of keys [HATA, section 3; random-projection stand-in
+ * for the learned hash]:
+ *   bit i of codes[b][h][j] = [ R[h][i] . K[b][h][j] >= 0 ]  (exact sign)
+ * code_bits must be 128.  No workspace.
+ */
+hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K,
+                                const void* R, int code_bits, uint32_t* codes,
+                                void* stream);
+
+/*
+ * Soft-collision scores of all keys [SOCKET, core mechanism items 2-3].
+ * For each query head: q_hat = q/||q||, z_{l,p} = W[h][l*P+p] . q_hat; the
+ * probability of bucket c in table l is the softmax over all 2^P buckets of
+ * sum_p s_p(c) z_{l,p} / tau with s_p(c) = +1 if bit p of c is set, else -1
+ * (a zero query gives uniform probabilities).  Summing the probabilities
+ * of the G = Hq/Hkv query heads of kv head h gives a table T[b][h][l][c],
+ * and
+ *   scores[b][h][j] = vnorm[b][h][j] * sum_l T[b][h][l][ ids[b][h][j][l] ]
+ * in float32 for j < N_b.  tau > 0.  Workspace holds the tables.
+ */
+hst_status hst_score_keys_softlsh(const hst_shape* shape, const void* q,
+                                  const void* W, int L, int P, float tau,
+                                  const uint8_t* ids, const void* vnorm,
+                                  int norm_dtype, float* scores, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * The two steps of hst_score_keys_softlsh as separate calls.
+ * hst_query_tables_softlsh writes the per-(sequence, kv head) bucket
+ * probability tables T [B][Hkv][L][2^P] float32 (the soft assignment of the
+ * query, summed over the G query heads of the kv head).
+ * hst_score_scan_softlsh streams the bucket ids and value norms of every key
+ * once and writes scores[b][h][j] = vnorm * sum_l T[b][h][l][ids[b][h][j][l]]
+ * for j < N_b.  No workspace.
+ */
+hst_status hst_query_tables_softlsh(const hst_shape* shape, const void* q,
+                                    const void* W, int L, int P, float tau,
+                                    float* tables, void* stream);
+hst_status hst_score_scan_softlsh(const hst_shape* shape, const float* tables,
+                                  int L, int P, const uint8_t* ids,
+                                  const void* vnorm, int norm_dtype,
+                                  float* scores, void* stream);
+
+/*
+ * Binary-code similarity scores [HATA, section 3]:
+ *   scores[b][h][j] = sum over query heads hq of kv head h of
+ *                     (code_bits - popcount(qcode_hq XOR codes[b][h][j]))
+ * with qcode_hq the code of q[b][hq] under R[h] (exact sign, as above).
+ * int32, range [0, code_bits * G].  Workspace holds the query codes.
+ */
+hst_status hst_score_keys_hamming(const hst_shape* shape, const void* q,
+                                  const void* R, int code_bits,
+                                  const uint32_t* codes, int32_t* scores,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Deterministic top-k per (sequence, kv head) [SOCKET, core mechanism
+ * item 4]: among j < N_b, the keys first in the order (score descending,
+ * index ascending), count k_b = min(k, N_b) or, with k_per_seq (device [B]),
+ * min(max(k_per_seq[b], 0), k, N_b).  idx rows have capacity k; the k_b
+ * selected indices are written in ascending order and the rest of the row
+ * is -1.  score_dtype is F32 (-0 equals +0; NaN unsupported) or I32.
+ * k >= 1.
+ */
+hst_status hst_select_topk(const hst_shape* shape, int score_dtype,
+                           const void* scores, int k,
+                           const int32_t* k_per_seq, int32_t* idx, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Exact softmax attention over selected keys [SOCKET, core mechanism
+ * item 4]: for query head hq of kv head h and S = { idx[b][h][i] : i < k,
+ * 0 <= idx[b][h][i] < N_b } (other entries are padding and are skipped),
+ *   a_j = scale * q[b][hq] . K[b][h][j],
+ *   out[b][hq] = sum_{j in S} softmax(a)_j V[b][h][j],
+ *   lse[b][hq] = log sum_{j in S} exp(a_j)
+ * accumulated in float32.  An empty S gives out = 0, lse = -inf.
+ * Repeated indices count once per occurrence.
+ */
+hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q,
+                                       const void* K, const void* V,
+                                       const int32_t* idx, int k, float scale,
+                                       float* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/*
+ * One soft-LSH decode step: hst_score_keys_softlsh, hst_select_topk and
+ * hst_sparse_decode_attention in sequence on the same stream, with the
+ * scores kept in the workspace.  idx (the selection, as hst_select_topk
+ * writes it) is an output.  lse nullable.
+ */
+hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q,
+                                   const void* K, const void* V,
+                                   const void* W, int L, int P, float tau,
+                                   const uint8_t* ids, const void* vnorm,
+                                   int norm_dtype, int k,
+                                   const int32_t* k_per_seq, float scale,
+                                   int32_t* idx, float* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* One binary-code decode step: score (Hamming), select, attend. */
+hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q,
+                                   const void* K, const void* V,
+                                   const void* R, int code_bits,
+                                   const uint32_t* codes, int k,
+                                   const int32_t* k_per_seq, float scale,
+                                   int32_t* idx, float* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HST_H_ */

@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports what include/hst.h declares, and rejects
+invalid arguments before anything is enqueued (host logic only; no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from hash_scored_top_amd import _lib
+    return _lib
+
+
+def test_header_symbols_exported():
+    L = _lib()
+    with open(os.path.join(ROOT, "include", "hst.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"\b(hst_[a-z_]+)\s*\(", text))
+    assert declared, "no declarations found"
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(L.EXPORTED)
+
+
+def _shape(L, **kw):
+    base = dict(B=2, Hq=8, Hkv=2, d=128, Nmax=1024, kv_dtype=L.HST_BF16, seq_lens=None)
+    base.update(kw)
+    return L.HstShape(**base)
+
+
+def test_status_strings_and_version():
+    L = _lib()
+    C = L._C
+    assert C.hst_version() >= 100
+    for s in (0, -1, -2, -3, -4):
+        assert C.hst_status_string(s).startswith(b"HST_")
+    assert C.hst_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=0), -1), (dict(Hq=7), -1), (dict(d=96), -2), (dict(kv_dtype=2), -2),
+    (dict(Nmax=0), -1), (dict(Hkv=0), -1),
+])
+def test_workspace_size_rejects_bad_shapes(kw, want):
+    L = _lib()
+    out = ctypes.c_size_t(0)
+    sh = _shape(L, **kw)
+    st = L._C.hst_workspace_size(L.HST_OP_DECODE_SOFTLSH, ctypes.byref(sh), 64, 8, 128, 10,
+                                 ctypes.byref(out))
+    assert st == want
+
+
+def test_workspace_sizes_monotone():
+    L = _lib()
+    sh = _shape(L)
+    a = L.workspace_size(L.HST_OP_DECODE_SOFTLSH, sh, 64, 8, k=10)
+    b = L.workspace_size(L.HST_OP_DECODE_SOFTLSH, sh, 64, 8, k=1000)
+    assert 0 < a <= b
+    assert L.workspace_size(L.HST_OP_HASH_SOFTLSH, sh, 64, 8) == 0
+    with pytest.raises(L.HstError):
+        L.workspace_size(L.HST_OP_DECODE_SOFTLSH, sh, 64, 9)   # P > 8
+    with pytest.raises(L.HstError):
+        L.workspace_size(L.HST_OP_SELECT_TOPK, sh, k=0)
+
+
+FAKE = 1 << 20  # aligned non-null "device" address; never dereferenced on these paths
+
+
+def test_entry_points_validate_before_launch():
+    L = _lib()
+    C = L._C
+    sh = _shape(L)
+    by = ctypes.byref(sh)
+    # null pointers
+    assert C.hst_hash_keys_softlsh(by, None, FAKE, FAKE, 64, 8, L.HST_F16, FAKE, FAKE, None) == -1
+    # misaligned pointer
+    assert C.hst_hash_keys_softlsh(by, FAKE + 2, FAKE, FAKE, 64, 8, L.HST_F16, FAKE, FAKE,
+                                   None) == -1
+    # unsupported P / norm dtype / code bits
+    assert C.hst_hash_keys_softlsh(by, FAKE, FAKE, FAKE, 64, 9, L.HST_F16, FAKE, FAKE, None) == -2
+    assert C.hst_hash_keys_softlsh(by, FAKE, FAKE, FAKE, 64, 8, L.HST_BF16, FAKE, FAKE, None) == -2
+    assert C.hst_hash_keys_binary(by, FAKE, FAKE, 64, FAKE, None) == -2
+    # tau must be positive and finite
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert C.hst_score_keys_softlsh(by, FAKE, FAKE, 64, 8, tau, FAKE, FAKE, L.HST_F16, FAKE,
+                                        FAKE, 1 << 30, None) == -1
+    # workspace too small
+    assert C.hst_score_keys_softlsh(by, FAKE, FAKE, 64, 8, 0.3, FAKE, FAKE, L.HST_F16, FAKE,
+                                    FAKE, 16, None) == -3
+    # k < 1, bad score dtype
+    assert C.hst_select_topk(by, L.HST_F32, FAKE, 0, None, FAKE, FAKE, 1 << 30, None) == -1
+    assert C.hst_select_topk(by, L.HST_F16, FAKE, 5, None, FAKE, FAKE, 1 << 30, None) == -2
+    # attention: group too large, non-finite scale
+    big = _shape(L, Hq=32, Hkv=2)
+    assert C.hst_sparse_decode_attention(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE,
+                                         None, FAKE, 1 << 30, None) == -2
+    assert C.hst_sparse_decode_attention(by, FAKE, FAKE, FAKE, FAKE, 8, float("nan"), FAKE, None,
+                                         FAKE, 1 << 30, None) == -1
+    # decode step: workspace too small
+    assert C.hst_decode_step_softlsh(by, FAKE, FAKE, FAKE, FAKE, 64, 8, 0.3, FAKE, FAKE,
+                                     L.HST_F16, 10, None, 0.1, FAKE, FAKE, None, FAKE, 100,
+                                     None) == -3
+    assert C.hst_decode_step_hamming(by, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 10, None, 0.1, FAKE,
+                                     FAKE, None, FAKE, 100, None) == -3
+    assert C.hst_last_hip_error() == 0

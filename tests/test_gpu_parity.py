@@ -1,0 +1,351 @@
+"""GPU parity of every stage against the CPU oracle, through the C ABI.
+
+Bars: bucket ids, value norms, binary codes, Hamming scores and selected
+index sets are bit-exact; soft-LSH scores agree to 1e-5 relative; attention
+outputs agree to 1e-5 of the output scale (fp32 K/V) or 2e-2 absolute (bf16
+K/V).  Stage-isolated tests feed both sides the same oracle-made inputs.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _hst():
+    import hash_scored_top_amd as hst
+    return hst
+
+
+def f64(x, dt):
+    return WL.storage_to_f64(x, dt)
+
+
+MED_SOFT = dataclasses.replace(
+    WL.WORKLOADS["llama8b_softlsh_b8_n32k"], name="med_soft", B=2, Hq=8, Hkv=2, N=6000,
+    needles=8, ragged=(3000, 6000), seed=99)
+MED_HAM = dataclasses.replace(
+    WL.WORKLOADS["hata_hamming_b16_n64k"], name="med_ham", B=3, Hq=8, Hkv=2, N=9000,
+    needles=8, ragged=(4000, 9000), seed=98)
+TINY = WL.WORKLOADS["tiny_softlsh_fp32"]
+
+_CACHE = {}
+
+
+def inputs(w):
+    if w.name not in _CACHE:
+        from tests.gpu_helpers import to_dev
+        x = WL.make_full(w)
+        dev = {n: to_dev(x[n], w.kv_dtype, DEV) for n in ("K", "V", "q")}
+        dev["W" if w.scheme == "softlsh" else "R"] = to_dev(
+            x["W" if w.scheme == "softlsh" else "R"], w.kv_dtype, DEV)
+        dev["seq_lens"] = torch.from_numpy(x["seq_lens"]).to(DEV)
+        dev["k_per_seq"] = torch.from_numpy(x["k_per_seq"]).to(DEV)
+        _CACHE[w.name] = (x, dev)
+    return _CACHE[w.name]
+
+
+def slab64(w, x, b, h):
+    G = w.G
+    n = int(x["seq_lens"][b])
+    return (f64(x["q"][b, h * G:(h + 1) * G], w.kv_dtype), f64(x["K"][b, h, :n], w.kv_dtype),
+            f64(x["V"][b, h, :n], w.kv_dtype))
+
+
+# ---------------------------------------------------------------- hashing
+
+@pytest.mark.parametrize("w", [TINY, MED_SOFT], ids=lambda w: w.name)
+def test_hash_softlsh_bit_exact(w):
+    hst = _hst()
+    x, d = inputs(w)
+    from tests.gpu_helpers import norm_torch_dtype
+    sl = d["seq_lens"] if w.ragged else None
+    ids, vn = hst.hst_hash_keys_softlsh(d["K"], d["V"], d["W"], w.L, w.P,
+                                        norm_torch_dtype(w.norm_dtype), seq_lens=sl)
+    ids, vn = ids.cpu().numpy(), vn.cpu().numpy()
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            _, K64, V64 = slab64(w, x, b, h)
+            ref = O.hash_keys_softlsh(K64, f64(x["W"][h], w.kv_dtype), w.L, w.P)
+            np.testing.assert_array_equal(ids[b, h, :n], ref)
+            np.testing.assert_array_equal(vn[b, h, :n].astype(np.float64),
+                                          O.value_norms(V64, w.norm_dtype))
+            assert not ids[b, h, n:].any()  # rows past N_b untouched
+
+
+def test_hash_binary_bit_exact():
+    hst = _hst()
+    w = MED_HAM
+    x, d = inputs(w)
+    codes = hst.hst_hash_keys_binary(d["K"], d["R"], seq_lens=d["seq_lens"]).cpu().numpy()
+    codes = codes.view(np.uint32)
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            _, K64, _ = slab64(w, x, b, h)
+            np.testing.assert_array_equal(codes[b, h, :n],
+                                          O.binary_codes(K64, f64(x["R"][h], w.kv_dtype)))
+
+
+def test_hash_sign_exact_under_cancellation():
+    # fp32 keys whose projection is -1 exactly while a plain float sum gives 0
+    hst = _hst()
+    d = 64
+    K = torch.zeros((1, 1, 3, d), dtype=torch.float32)
+    W = torch.zeros((1, 1, d), dtype=torch.float32)
+    K[0, 0, 0, :3] = torch.tensor([2.0 ** 30, -1.0, -(2.0 ** 30)])
+    K[0, 0, 1, :3] = -K[0, 0, 0, :3]
+    W[0, 0, :3] = torch.tensor([2.0 ** 30, 1.0, 2.0 ** 30])
+    ids, _ = hst.hst_hash_keys_softlsh(K.to(DEV), K.to(DEV), W.to(DEV), 1, 1, torch.float32)
+    assert ids.cpu().flatten().tolist() == [0, 1, 1]
+
+
+# ---------------------------------------------------------------- scores
+
+@pytest.mark.parametrize("w", [TINY, MED_SOFT], ids=lambda w: w.name)
+def test_score_softlsh_rel_1e5(w):
+    hst = _hst()
+    from tests.gpu_helpers import norms_to_dev
+    x, d = inputs(w)
+    ids = np.zeros((w.B, w.Hkv, w.N, w.L), dtype=np.uint8)
+    vn = np.zeros((w.B, w.Hkv, w.N))
+    refs = {}
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            q64, K64, V64 = slab64(w, x, b, h)
+            W64 = f64(x["W"][h], w.kv_dtype)
+            ids[b, h, :n] = O.hash_keys_softlsh(K64, W64, w.L, w.P)
+            vn[b, h, :n] = O.value_norms(V64, w.norm_dtype)
+            T = O.query_tables(q64, W64, w.L, w.P, w.tau)
+            refs[(b, h)] = O.score_softlsh(T, ids[b, h, :n], vn[b, h, :n])
+    sl = d["seq_lens"] if w.ragged else None
+    got = hst.hst_score_keys_softlsh(d["q"], d["W"], w.L, w.P, w.tau,
+                                     torch.from_numpy(ids).to(DEV),
+                                     norms_to_dev(vn, w.norm_dtype, DEV), d["K"],
+                                     seq_lens=sl).cpu().numpy()
+    for (b, h), ref in refs.items():
+        n = ref.shape[0]
+        rel = np.abs(got[b, h, :n] - ref) / np.abs(ref)
+        assert rel.max() <= 1e-5, (b, h, rel.max())
+
+
+def test_score_hamming_bit_exact():
+    hst = _hst()
+    w = MED_HAM
+    x, d = inputs(w)
+    codes = np.zeros((w.B, w.Hkv, w.N, 4), dtype=np.uint32)
+    refs = {}
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            q64, K64, _ = slab64(w, x, b, h)
+            R64 = f64(x["R"][h], w.kv_dtype)
+            codes[b, h, :n] = O.binary_codes(K64, R64)
+            refs[(b, h)] = O.score_hamming(O.binary_codes(q64, R64), codes[b, h, :n])
+    got = hst.hst_score_keys_hamming(d["q"], d["R"], torch.from_numpy(codes.view(np.int32)).to(DEV),
+                                     d["K"], seq_lens=d["seq_lens"]).cpu().numpy()
+    for (b, h), ref in refs.items():
+        np.testing.assert_array_equal(got[b, h, :ref.shape[0]], ref)
+
+
+# ---------------------------------------------------------------- select
+
+def _select_gpu(scores_np, k, seq_lens=None, k_per_seq=None):
+    hst = _hst()
+    B, H, N = scores_np.shape
+    t = torch.from_numpy(np.ascontiguousarray(scores_np)).to(DEV)
+    sl = None if seq_lens is None else torch.from_numpy(np.asarray(seq_lens, np.int32)).to(DEV)
+    kp = None if k_per_seq is None else torch.from_numpy(np.asarray(k_per_seq, np.int32)).to(DEV)
+    return hst.hst_select_topk(t, k, Hq=H, d=128, k_per_seq=kp, seq_lens=sl).cpu().numpy()
+
+
+def _check_select(scores_np, k, seq_lens=None, k_per_seq=None):
+    got = _select_gpu(scores_np, k, seq_lens, k_per_seq)
+    B, H, N = scores_np.shape
+    for b in range(B):
+        n = N if seq_lens is None else int(seq_lens[b])
+        kb = k if k_per_seq is None else max(0, min(int(k_per_seq[b]), k))
+        for h in range(H):
+            ref = O.select_topk(scores_np[b, h, :n].astype(np.float64), kb)
+            row = got[b, h]
+            np.testing.assert_array_equal(row[:len(ref)], ref, err_msg=f"b={b} h={h}")
+            assert (row[len(ref):] == -1).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_select_float_random_ragged(seed):
+    rng = np.random.default_rng(seed)
+    B, H, N = 3, 2, 20000
+    s = rng.random((B, H, N)).astype(np.float32)
+    lens = [20000, 7777, 4097]
+    _check_select(s, 700, seq_lens=lens)
+    _check_select(s, 1, seq_lens=lens)
+    _check_select(s, 5000, seq_lens=lens, k_per_seq=[5000, 0, 4097])
+
+
+def test_select_heavy_ties_int_and_float():
+    rng = np.random.default_rng(5)
+    B, H, N = 2, 3, 12345
+    si = rng.integers(0, 6, size=(B, H, N)).astype(np.int32)
+    _check_select(si, 2500)
+    _check_select(si.astype(np.float32), 2500)
+    _check_select(np.zeros((1, 1, 9000), np.float32), 4000)   # all equal
+    _check_select(np.full((1, 1, 9000), 3, np.int32), 9000)  # k = N
+    _check_select(si, 20000)  # k > N selects everything
+
+
+def test_select_signs_zero_and_narrow_band():
+    rng = np.random.default_rng(6)
+    s = (rng.standard_normal((1, 2, 10000)) * 3).astype(np.float32)
+    s[0, 0, ::7] = 0.0
+    s[0, 0, 3::7] = -0.0
+    _check_select(s, 3000)
+    band = (1.0 + rng.integers(0, 50, size=(1, 2, 10000)) * 2.0 ** -23).astype(np.float32)
+    _check_select(band, 1234)
+    tiny = (rng.integers(1, 9, size=(1, 1, 5000)) * 2.0 ** -140).astype(np.float32)  # subnormal
+    _check_select(tiny, 777)
+
+
+def test_select_empty_sequence():
+    s = np.random.default_rng(1).random((2, 1, 5000)).astype(np.float32)
+    _check_select(s, 10, seq_lens=[0, 5000])
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(w, ks):
+    hst = _hst()
+    x, d = inputs(w)
+    kcap = max(ks)
+    idx = np.full((w.B, w.Hkv, kcap), -1, dtype=np.int32)
+    refs = {}
+    rng = np.random.default_rng(3)
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            kk = min(ks[(b * w.Hkv + h) % len(ks)], n)
+            sel = np.sort(rng.choice(n, size=kk, replace=False))
+            idx[b, h, :kk] = sel
+            q64, K64, V64 = slab64(w, x, b, h)
+            refs[(b, h)] = O.attend(q64, K64, V64, sel, 1 / math.sqrt(w.d))
+    sl = d["seq_lens"] if w.ragged else None
+    out, lse = hst.hst_sparse_decode_attention(d["q"], d["K"], d["V"],
+                                               torch.from_numpy(idx).to(DEV), seq_lens=sl)
+    return out.cpu().numpy(), lse.cpu().numpy(), refs
+
+
+@pytest.mark.parametrize("w,ks", [(TINY, [128]), (TINY, [4096]), (TINY, [1]),
+                                  (MED_SOFT, [182, 1, 999]), (MED_HAM, [3000, 17])],
+                         ids=["tiny_k128", "tiny_dense", "tiny_k1", "med_soft", "med_ham"])
+def test_attention_parity(w, ks):
+    out, lse, refs = _attn_case(w, ks)
+    G = w.G
+    for (b, h), (ro, rl) in refs.items():
+        go = out[b, h * G:(h + 1) * G]
+        if w.kv_dtype == "f32":
+            assert np.abs(go - ro).max() <= 1e-5 * np.abs(ro).max()
+            np.testing.assert_allclose(lse[b, h * G:(h + 1) * G], rl, rtol=1e-5)
+        else:
+            assert np.abs(go - ro).max() <= 2e-2
+            np.testing.assert_allclose(lse[b, h * G:(h + 1) * G], rl, rtol=1e-4, atol=1e-4)
+
+
+def test_attention_padding_and_empty():
+    hst = _hst()
+    w = TINY
+    x, d = inputs(w)
+    idx = np.full((1, 1, 64), -1, dtype=np.int32)
+    out, lse = hst.hst_sparse_decode_attention(d["q"], d["K"], d["V"],
+                                               torch.from_numpy(idx).to(DEV))
+    assert (out.cpu().numpy() == 0).all() and np.isneginf(lse.cpu().numpy()).all()
+    # out-of-range and negative entries are padding
+    idx[0, 0, :5] = [3, 4096, 10, -7, 99999]
+    out, lse = hst.hst_sparse_decode_attention(d["q"], d["K"], d["V"],
+                                               torch.from_numpy(idx).to(DEV))
+    q64, K64, V64 = slab64(w, x, 0, 0)
+    ro, rl = O.attend(q64, K64, V64, np.array([3, 10]), 1 / math.sqrt(w.d))
+    assert np.abs(out.cpu().numpy()[0] - ro).max() <= 1e-5 * np.abs(ro).max()
+
+
+# ---------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("w", [TINY, MED_SOFT], ids=lambda w: w.name)
+def test_decode_softlsh_end_to_end(w):
+    hst = _hst()
+    from tests.gpu_helpers import norm_torch_dtype
+    x, d = inputs(w)
+    sl = d["seq_lens"] if w.ragged else None
+    kp = d["k_per_seq"] if w.ragged else None
+    ids, vn = hst.hst_hash_keys_softlsh(d["K"], d["V"], d["W"], w.L, w.P,
+                                        norm_torch_dtype(w.norm_dtype), seq_lens=sl)
+    idx, out, lse = hst.hst_decode_step_softlsh(d["q"], d["K"], d["V"], d["W"], ids, vn, w.L,
+                                                w.P, w.tau, w.k_max(), seq_lens=sl, k_per_seq=kp)
+    idx, out = idx.cpu().numpy(), out.cpu().numpy()
+    G = w.G
+    exact_sets = 0
+    for b in range(w.B):
+        kb = int(x["k_per_seq"][b])
+        for h in range(w.Hkv):
+            q64, K64, V64 = slab64(w, x, b, h)
+            r = O.decode_slab_softlsh(q64, K64, V64, f64(x["W"][h], w.kv_dtype), w.L, w.P, w.tau,
+                                      kb, w.norm_dtype)
+            got = idx[b, h, :kb]
+            assert (idx[b, h, kb:] == -1).all()
+            diff = set(got.tolist()) ^ set(r["idx"].tolist())
+            if not diff:
+                exact_sets += 1
+                go = out[b, h * G:(h + 1) * G]
+                tol = 1e-5 * np.abs(r["out"]).max() if w.kv_dtype == "f32" else 2e-2
+                assert np.abs(go - r["out"]).max() <= tol
+            else:
+                # only near-ties of the k-th score may differ
+                kth = np.sort(r["scores"])[::-1][kb - 1]
+                for j in diff:
+                    assert abs(r["scores"][j] - kth) <= 2e-5 * kth, (b, h, j)
+            # the planted needles are found
+            nd = x["needles"][(b, h)]
+            assert np.isin(nd, got).mean() >= 0.5
+    assert exact_sets >= 1
+
+
+def test_decode_hamming_end_to_end_bit_exact():
+    hst = _hst()
+    w = MED_HAM
+    x, d = inputs(w)
+    codes = hst.hst_hash_keys_binary(d["K"], d["R"], seq_lens=d["seq_lens"])
+    idx, out, lse = hst.hst_decode_step_hamming(d["q"], d["K"], d["V"], d["R"], codes, w.k_max(),
+                                                seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
+    idx, out = idx.cpu().numpy(), out.cpu().numpy()
+    G = w.G
+    for b in range(w.B):
+        kb = int(x["k_per_seq"][b])
+        for h in range(w.Hkv):
+            q64, K64, V64 = slab64(w, x, b, h)
+            r = O.decode_slab_hamming(q64, K64, V64, f64(x["R"][h], w.kv_dtype), kb)
+            np.testing.assert_array_equal(idx[b, h, :kb], r["idx"])
+            assert (idx[b, h, kb:] == -1).all()
+            assert np.abs(out[b, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2
+
+
+def test_decode_is_deterministic():
+    hst = _hst()
+    w = MED_SOFT
+    x, d = inputs(w)
+    from tests.gpu_helpers import norm_torch_dtype
+    ids, vn = hst.hst_hash_keys_softlsh(d["K"], d["V"], d["W"], w.L, w.P,
+                                        norm_torch_dtype(w.norm_dtype), seq_lens=d["seq_lens"])
+    step = hst.DecodeSoftLSH(d["K"], w.Hq, w.L, w.P, w.tau, w.k_max(), vn.dtype,
+                             seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
+    i1, o1, l1 = (t.clone() for t in step(d["q"], d["K"], d["V"], d["W"], ids, vn))
+    i2, o2, l2 = step(d["q"], d["K"], d["V"], d["W"], ids, vn)
+    assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
