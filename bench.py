@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of hash-scored top-k sparse attention on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch and
+all heads: query soft assignment (or query codes), the score scan over every
+cached key, exact top-k per kv head, and exact attention over the gathered
+rows.  The prefill hashing is timed separately.
+
+Inputs are resident in HBM before timing.  Each timed step reads a different
+copy of the key metadata and K/V (``--rotate`` copies, enough to exceed twice
+the 256 MB Infinity Cache), so repeated steps cannot be served from cache.
+
+Prints one JSON line: decode tokens/s (= batch / step time), the roofline of
+the dominant kernel (HBM bytes per launch / event-timed duration), the whole
+step's fraction of the HBM roofline, and the CPU oracle's rate on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "decode tokens/s and % of HBM roofline for hash score+top-k+sparse attn"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="longctx_softlsh_b1_n128k")
+    ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
+    ap.add_argument("--kernel-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device copy first (HBM counter scale)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(w, lens, ks):
+    """Algorithmic HBM bytes of one step: metadata of every key, the k gathered
+    K/V rows per kv head, q in and out/lse out."""
+    e = 4 if w.kv_dtype == "f32" else 2
+    if w.scheme == "softlsh":
+        m = w.L + (2 if w.norm_dtype == "f16" else 4)
+    else:
+        m = w.code_bits // 8
+    meta = sum(int(n) for n in lens) * w.Hkv * m
+    gathered = sum(int(k) for k in ks) * w.Hkv * 2 * w.d * e
+    qo = w.B * w.Hq * w.d * (e + 4) + w.B * w.Hq * 4
+    return meta, gathered, qo
+
+
+def traffic_record(kernel: str, workload: str, src: str):
+    """Measured HBM bytes per launch from a committed counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, seconds):
+    """The float64 oracle's decode step on a sample of (b, kv head) slabs."""
+    import numpy as np
+    import oracle as O
+    import workloads as WL
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    lens, ks = x["seq_lens"], x["k_per_seq"]
+    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)][:2]
+    prepared = []
+    for (b, h) in slabs:
+        n = int(lens[b])
+        q64 = WL.storage_to_f64(x["q"][b, h * w.G:(h + 1) * w.G], w.kv_dtype)
+        K64 = WL.storage_to_f64(x["K"][b, h, :n], w.kv_dtype)
+        V64 = WL.storage_to_f64(x["V"][b, h, :n], w.kv_dtype)
+        if w.scheme == "softlsh":
+            W64 = WL.storage_to_f64(x["W"][h], w.kv_dtype)
+            meta = (O.hash_keys_softlsh(K64, W64, w.L, w.P), O.value_norms(V64, w.norm_dtype), W64)
+        else:
+            R64 = WL.storage_to_f64(x["R"][h], w.kv_dtype)
+            meta = (O.binary_codes(K64, R64), None, R64)
+        prepared.append((b, h, q64, K64, V64, meta))
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for (b, h, q64, K64, V64, meta) in prepared:
+                kb = int(ks[b])
+                if w.scheme == "softlsh":
+                    O.decode_slab_softlsh(q64, K64, V64, meta[2], w.L, w.P, w.tau, kb,
+                                          w.norm_dtype, ids=meta[0], vnorm=meta[1])
+                else:
+                    O.decode_slab_hamming(q64, K64, V64, meta[2], kb, kcodes=meta[0])
+            reps += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    per_slab = dt / (reps * len(prepared))
+    t_step = per_slab * w.B * w.Hkv
+    return {"value": w.B / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{len(prepared)} of {w.B * w.Hkv} (batch, kv head) slabs, decode step "
+                       f"(tables/codes, scores, top-k, attention) x{reps}, float64 numpy, one "
+                       f"thread; step time = mean slab time x {w.B * w.Hkv}"),
+            "seconds": round(dt, 2), "step_s": t_step}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU: the decode path has no multi-GPU mode "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hash_scored_top_amd as hst
+    import workloads as WL
+    from workloads.device import norm_torch_dtype, to_dev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = WL.WORKLOADS[args.workload]
+    log(f"workload {w.name}: generating inputs")
+    t0 = time.time()
+    x = WL.make_full(w)
+    lens, ks = x["seq_lens"], x["k_per_seq"]
+    kmax = int(ks.max())
+    log(f"generated in {time.time() - t0:.1f}s")
+
+    if args.copy_calibration:
+        a = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    K = to_dev(x["K"], w.kv_dtype, dev)
+    V = to_dev(x["V"], w.kv_dtype, dev)
+    q = to_dev(x["q"], w.kv_dtype, dev)
+    ragged = w.ragged is not None
+    sl = torch.from_numpy(lens).to(dev) if ragged else None
+    kp = torch.from_numpy(ks).to(dev) if ragged else None
+    stream = torch.cuda.current_stream(dev)
+
+    # prefill metadata, timed separately
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    if w.scheme == "softlsh":
+        Wp = to_dev(x["W"], w.kv_dtype, dev)
+        nd = norm_torch_dtype(w.norm_dtype)
+        hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd, seq_lens=sl)
+        ev[0].record(stream)
+        ids, vn = hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd, seq_lens=sl)
+        ev[1].record(stream)
+    else:
+        Rp = to_dev(x["R"], w.kv_dtype, dev)
+        hst.hst_hash_keys_binary(K, Rp, seq_lens=sl)
+        ev[0].record(stream)
+        codes = hst.hst_hash_keys_binary(K, Rp, seq_lens=sl)
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = ev[0].elapsed_time(ev[1])
+
+    meta_b, gath_b, qo_b = alg_bytes(w, lens, ks)
+    step_bytes = meta_b + gath_b + qo_b
+    R = args.rotate or max(2, min(16, math.ceil(2 * MALL_BYTES / step_bytes) + 1))
+    log(f"step algorithmic bytes {step_bytes / 1e6:.1f} MB; rotating over {R} input copies")
+    if w.scheme == "softlsh":
+        sets = [(K, V, ids, vn)] + [(K.clone(), V.clone(), ids.clone(), vn.clone())
+                                    for _ in range(R - 1)]
+        step = hst.DecodeSoftLSH(K, w.Hq, w.L, w.P, w.tau, kmax, vn.dtype, seq_lens=sl,
+                                 k_per_seq=kp)
+        run = lambda i: step(q, sets[i % R][0], sets[i % R][1], Wp, sets[i % R][2], sets[i % R][3])
+    else:
+        sets = [(K, V, codes)] + [(K.clone(), V.clone(), codes.clone()) for _ in range(R - 1)]
+        step = hst.DecodeHamming(K, w.Hq, kmax, seq_lens=sl, k_per_seq=kp)
+        run = lambda i: step(q, sets[i % R][0], sets[i % R][1], Rp, sets[i % R][2])
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        run(i)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
+    ms_per_step = total_ms / args.steps
+    log(f"step {ms_per_step * 1e3:.2f} us (p50 {np.percentile(per, 50):.2f} us)")
+
+    # dominant kernel, timed alone with events on the same stream
+    if w.scheme == "softlsh":
+        kname = "score_softlsh_kernel"
+        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "score.hip")
+        tables = hst.hst_query_tables_softlsh(q, Wp, w.L, w.P, w.tau, K, seq_lens=sl)
+        sc = torch.empty((w.B, w.Hkv, w.N), dtype=torch.float32, device=dev)
+        kbytes = meta_b
+        launch = lambda i: hst.hst_score_scan_softlsh(tables, sets[i % R][2], sets[i % R][3], K,
+                                                      w.Hq, seq_lens=sl, scores=sc)
+    else:
+        kname = "sparse_attn_split_kernel"
+        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "attention.hip")
+        kbytes = gath_b + qo_b
+        idx = step.idx.clone()
+        launch = lambda i: hst.hst_sparse_decode_attention(q, sets[i % R][0], sets[i % R][1], idx,
+                                                           seq_lens=sl)
+    for i in range(5):
+        launch(i)
+    kst = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
+    ken = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]
+    torch.cuda.synchronize()
+    for i in range(args.kernel_iters):
+        kst[i].record(stream)
+        launch(i)
+        ken[i].record(stream)
+    torch.cuda.synchronize()
+    kus = float(np.mean([s.elapsed_time(e) for s, e in zip(kst, ken)]) * 1e3)
+    achieved = kbytes / (kus * 1e-6) / 1e9
+    traffic = traffic_record(kname.replace("_kernel", ""), w.name, ksrc)
+
+    result = {
+        "metric": METRIC,
+        "value": w.B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "scheme": w.scheme, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "d": w.d, "N": w.N, "kv_dtype": w.kv_dtype,
+                   **({"L": w.L, "P": w.P, "tau": w.tau} if w.scheme == "softlsh"
+                      else {"code_bits": w.code_bits}),
+                   "k": kmax, "ragged": ragged},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "alg_bytes_per_launch": kbytes,
+                     "avg_launch_us": kus},
+        "step": {"alg_bytes": step_bytes, "meta_bytes": meta_b, "gathered_bytes": gath_b,
+                 "hbm_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "p10_us": float(np.percentile(per, 10)), "p50_us": float(np.percentile(per, 50)),
+                 "p90_us": float(np.percentile(per, 90)), "rotated_copies": R},
+        "prefill_hash_us": prefill_ms * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,7 +51,7 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(LIB_PATH)
-    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    P, I, F, D, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
     SH = ctypes.POINTER(HstShape)
     sig = {
         "hst_version": ([], I),
@@ -60,13 +60,13 @@ def _load() -> ctypes.CDLL:
         "hst_workspace_size": ([I, SH, I, I, I, I, ctypes.POINTER(SZ)], I),
         "hst_hash_keys_softlsh": ([SH, P, P, P, I, I, I, P, P, P], I),
         "hst_hash_keys_binary": ([SH, P, P, I, P, P], I),
-        "hst_score_keys_softlsh": ([SH, P, P, I, I, F, P, P, I, P, P, SZ, P], I),
+        "hst_score_keys_softlsh": ([SH, P, P, I, I, D, P, P, I, P, P, SZ, P], I),
         "hst_score_keys_hamming": ([SH, P, P, I, P, P, P, SZ, P], I),
-        "hst_query_tables_softlsh": ([SH, P, P, I, I, F, P, P], I),
+        "hst_query_tables_softlsh": ([SH, P, P, I, I, D, P, P], I),
         "hst_score_scan_softlsh": ([SH, P, I, I, P, P, I, P, P], I),
         "hst_select_topk": ([SH, I, P, I, P, P, P, SZ, P], I),
         "hst_sparse_decode_attention": ([SH, P, P, P, P, I, F, P, P, P, SZ, P], I),
-        "hst_decode_step_softlsh": ([SH, P, P, P, P, I, I, F, P, P, I, I, P, F, P, P, P, P, SZ, P], I),
+        "hst_decode_step_softlsh": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, F, P, P, P, P, SZ, P], I),
         "hst_decode_step_hamming": ([SH, P, P, P, P, I, P, I, P, F, P, P, P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
@@ -177,10 +177,10 @@ def hst_score_keys_softlsh(q, W, L: int, P: int, tau: float, ids, vnorm, Nmax_li
 
 def hst_query_tables_softlsh(q, W, L: int, P: int, tau: float, Nmax_like,
                              seq_lens=None) -> torch.Tensor:
-    """Bucket-probability tables [B,Hkv,L,2^P] float32."""
+    """Bucket-probability tables, bucket-major: [B,Hkv,2^P,L] float32."""
     B, Hq, d = q.shape
     shape = make_shape(Nmax_like, Hq, seq_lens)
-    tables = torch.empty((shape.B, shape.Hkv, L, 1 << P), dtype=torch.float32, device=q.device)
+    tables = torch.empty((shape.B, shape.Hkv, 1 << P, L), dtype=torch.float32, device=q.device)
     _check(_C.hst_query_tables_softlsh(ctypes.byref(shape), _ptr(q), _ptr(W), L, P, float(tau),
                                        _ptr(tables), _stream(q.device)),
            "hst_query_tables_softlsh")
@@ -190,7 +190,7 @@ def hst_query_tables_softlsh(q, W, L: int, P: int, tau: float, Nmax_like,
 def hst_score_scan_softlsh(tables, ids, vnorm, Nmax_like, Hq: int, seq_lens=None,
                            scores=None, stream=None) -> torch.Tensor:
     """Score scan over precomputed tables: [B,Hkv,Nmax] float32."""
-    B, Hkv, L, nb = tables.shape
+    B, Hkv, nb, L = tables.shape
     shape = make_shape(Nmax_like, Hq, seq_lens)
     if scores is None:
         scores = torch.zeros((shape.B, shape.Hkv, shape.Nmax), dtype=torch.float32,

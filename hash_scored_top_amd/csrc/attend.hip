@@ -1,0 +1,383 @@
+// Selection and exact attention over the selected keys.
+//  * Top-k (SOCKET overview page, "Core mechanism: soft LSH", item 4: the
+//    top-k keys by soft score, chosen deterministically; ties go to the lower
+//    index): each workgroup derives the head's selection from the candidate
+//    slots itself and keeps the part of the ascending index row that falls in
+//    its split, so no workgroup waits for another.
+//  * Attention (same item: exact attention on that subset): a split-K flash
+//    decode; each gathered K/V row is read once per kv head and used for all G
+//    query heads of the group (grouped-query attention), with an online
+//    softmax in the base-2 exponent domain.  A second kernel merges the split
+//    states through their log-sum-exp.
+#include "fused_device.h"
+#include "hst_launch.h"
+
+namespace hst {
+
+constexpr int kAttNT = 512;
+constexpr int kSelNT = 1024;
+
+template <typename T, int EPL>
+struct RowLd;
+template <>
+struct RowLd<bf16, 8> {
+  static __device__ __forceinline__ void ld(const bf16* p, float (&x)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+};
+template <>
+struct RowLd<bf16, 4> {
+  static __device__ __forceinline__ void ld(const bf16* p, float (&x)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  }
+};
+template <>
+struct RowLd<float, 8> {
+  static __device__ __forceinline__ void ld(const float* p, float (&x)[8]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    const float4 v = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  }
+};
+template <>
+struct RowLd<float, 4> {
+  static __device__ __forceinline__ void ld(const float* p, float (&x)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  }
+};
+
+// LDS of the attend kernel: [64 KB: candidates, later the wave partials]
+// [hist 8 KB][chunk offsets][rows of this split]
+size_t attend_smem(int nchunks, int rps) {
+  return 65536 + 8192 + static_cast<size_t>(nchunks + 1) * 4 + static_cast<size_t>(rps) * 4;
+}
+
+// grid (nsplit, B*Hkv).  SELECT: rows come from the head's selection (and
+// the split's part of the index row is written to idx); otherwise rows are
+// read from idx.  Rows outside [0, N_b) are skipped.
+template <typename T, int D, int GMAX, bool SELECT>
+__global__ void __launch_bounds__(kAttNT)
+attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
+              int32_t* __restrict__ idx, const void* __restrict__ scores, int scores_int, int chunk,
+              const int32_t* __restrict__ seq_lens, float scale_log2, FusedArgs a) {
+  constexpr int NT = kAttNT;
+  constexpr int EPL = D / 16;
+  constexpr int NW = NT / 64;
+  constexpr int NG = NT / 16;
+  constexpr int U = 4;
+  extern __shared__ __align__(16) unsigned char sm[];
+  __shared__ BlockScratch<NT> sc;
+  __shared__ float red_ml[NW][GMAX][2];
+  float* red_o = reinterpret_cast<float*>(sm);  // [NW][GMAX][D], after the selection
+  const int nchunks = a.nchunks;
+  int* offs = reinterpret_cast<int*>(sm + 65536 + 8192);
+  int32_t* rows = reinterpret_cast<int32_t*>(sm + 65536 + 8192 + (nchunks + 1) * 4);
+  const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  const int n = seq_len(seq_lens, b, a.Nmax);
+  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int r0 = split * a.rps, r1 = min(r0 + a.rps, a.kcap);
+  const int t = threadIdx.x, sub = t & 15, grp = t >> 4, lane = t & 63, wave = t >> 6;
+  int32_t* irow = idx + static_cast<long long>(bh) * a.kcap;
+  int nrows;
+  if (SELECT) {
+    const int k_eff = a.heads[bh].k_eff;
+    SelectScratch ws{reinterpret_cast<uint2*>(sm), 65536 / 8, reinterpret_cast<uint32_t*>(sm + 65536), offs};
+    int M = 0;
+    const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
+    const int path = select_range<NT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, r0, r1, irow,
+                                      rows, sc, &M);
+    nrows = max(0, min(k_eff, r1) - r0);
+    if (split == 0 && t == 0) {
+      a.heads[bh].path = static_cast<uint32_t>(path);
+      a.heads[bh].cand_total = static_cast<uint32_t>(M);
+    }
+  } else {
+    nrows = max(0, r1 - r0);
+    for (int i = t; i < nrows; i += NT) rows[i] = irow[r0 + i];
+  }
+  __syncthreads();
+
+  float qv[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g < G) {
+      RowLd<T, EPL>::ld(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL, qv[g]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
+    }
+  }
+  float m[GMAX], l[GMAX], o[GMAX][EPL];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+  }
+  const long long kvb = static_cast<long long>(bh) * a.Nmax;
+  for (int rb = grp; rb < nrows; rb += NG * U) {
+    float kx[U][EPL], vx[U][EPL];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * NG;
+      const int j = r < nrows ? rows[r] : -1;
+      ok[u] = j >= 0 && j < n;
+      if (ok[u]) {
+        RowLd<T, EPL>::ld(K + (kvb + j) * D + sub * EPL, kx[u]);
+        RowLd<T, EPL>::ld(V + (kvb + j) * D + sub * EPL, vx[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;  // uniform over the 16 lanes of a row group
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[u][e];
+        s += __shfl_xor(s, 8, 16);
+        s += __shfl_xor(s, 4, 16);
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, true));
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, true));
+        const float mn = fmaxf(m[g], s);
+        const float c = exp2f(m[g] - mn);
+        const float p = exp2f(s - mn);
+        l[g] = l[g] * c + p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * c + p * vx[u][e];
+        m[g] = mn;
+      }
+    }
+  }
+  // merge the row groups of a wave (lanes xor 16, 32), then the waves
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) break;
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+      const float m2 = __shfl_xor(m[g], x, 64);
+      const float l2 = __shfl_xor(l[g], x, 64);
+      const float mn = fmaxf(m[g], m2);
+      const float c1 = mn == -INFINITY ? 0.f : exp2f(m[g] - mn);
+      const float c2 = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
+      l[g] = l[g] * c1 + l2 * c2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float o2 = __shfl_xor(o[g][e], x, 64);
+        o[g][e] = o[g][e] * c1 + o2 * c2;
+      }
+      m[g] = mn;
+    }
+  }
+  __syncthreads();  // the candidate region becomes red_o
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      if (g >= G) break;
+      if (lane == 0) {
+        red_ml[wave][g][0] = m[g];
+        red_ml[wave][g][1] = l[g];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_o[(wave * GMAX + g) * D + lane * EPL + e] = o[g][e];
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < G * D; i += NT) {
+    const int g = i / D, c = i % D;
+    float mm = -INFINITY;
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, red_ml[w][g][0]);
+    float ll = 0.f, oo = 0.f;
+    if (mm != -INFINITY) {
+      for (int w = 0; w < NW; ++w) {
+        const float wt = exp2f(red_ml[w][g][0] - mm);
+        ll += red_ml[w][g][1] * wt;
+        oo += red_o[(w * GMAX + g) * D + c] * wt;
+      }
+    }
+    const long long pi = (static_cast<long long>(b) * Hq + h * G + g) * nsplit + split;
+    a.part_o[pi * D + c] = oo;
+    if (c == 0) {
+      a.part_ml[pi * 2] = mm;
+      a.part_ml[pi * 2 + 1] = ll;
+    }
+  }
+}
+
+// Merge the split states of one kv head's G query heads.  grid (B*Hkv).
+template <int D, int GMAX>
+__global__ void __launch_bounds__(256)
+combine_kernel(int Hq, int Hkv, int nsplit, const float* __restrict__ part_o,
+               const float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NT = 256;
+  constexpr int C4 = D / 4;
+  __shared__ float wgt[GMAX][kMaxSplits];
+  __shared__ float accq[4][GMAX * D];
+  __shared__ float gM[GMAX], gL[GMAX];
+  const int G = Hq / Hkv;
+  const int bh = blockIdx.x, b = bh / Hkv, h = bh % Hkv;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const long long qb = static_cast<long long>(b) * Hq + h * G;
+  for (int g = wave; g < G; g += NT / 64) {
+    float M = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_ml[((qb + g) * nsplit + s) * 2]);
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float Ls = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float ms = part_ml[((qb + g) * nsplit + s) * 2];
+      const float wv = (ms == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ms - M);
+      Ls += part_ml[((qb + g) * nsplit + s) * 2 + 1] * wv;
+      wgt[g][s] = wv;
+    }
+    for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
+    if (lane == 0) {
+      gM[g] = M;
+      gL[g] = Ls;
+    }
+  }
+  __syncthreads();
+  // each thread: 4 output elements of one query head over a quarter of the splits
+  for (int i = t; i < 4 * GMAX * C4; i += NT) {
+    const int quarter = i / (GMAX * C4), gc = i % (GMAX * C4);
+    const int g = gc / C4, c4 = gc % C4;
+    if (g >= G) continue;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int sq = (nsplit + 3) / 4;
+    const int s_lo = quarter * sq, s_hi = min(nsplit, s_lo + sq);
+    for (int sb = s_lo; sb < s_hi; sb += 8) {  // eight independent loads in flight
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sb + u < s_hi) v[u] = reinterpret_cast<const float4*>(part_o + ((qb + g) * nsplit + sb + u) * D)[c4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (sb + u >= s_hi) continue;
+        const float wv = wgt[g][sb + u];
+        acc.x += v[u].x * wv;
+        acc.y += v[u].y * wv;
+        acc.z += v[u].z * wv;
+        acc.w += v[u].w * wv;
+      }
+    }
+    float* dst = &accq[quarter][g * D + c4 * 4];
+    dst[0] = acc.x;
+    dst[1] = acc.y;
+    dst[2] = acc.z;
+    dst[3] = acc.w;
+  }
+  __syncthreads();
+  for (int i = t; i < G * D; i += NT) {
+    const int g = i / D, c = i % D;
+    const float Ls = gL[g];
+    const float o = accq[0][i] + accq[1][i] + accq[2][i] + accq[3][i];
+    out[(qb + g) * D + c] = Ls > 0.f ? o / Ls : 0.f;
+    if (c == 0 && lse != nullptr) lse[qb + g] = Ls > 0.f ? (gM[g] + log2f(Ls)) * kLn2F : -INFINITY;
+  }
+}
+
+// Stand-alone top-k: one workgroup per (sequence, kv head) writes the row.
+__global__ void __launch_bounds__(kSelNT)
+select_kernel(int32_t* __restrict__ idx, const void* __restrict__ scores, int scores_int, int chunk,
+              const int32_t* __restrict__ seq_lens, FusedArgs a) {
+  extern __shared__ __align__(16) unsigned char sm[];
+  __shared__ BlockScratch<kSelNT> sc;
+  const int bh = blockIdx.x, b = bh / a.Hkv;
+  const int n = seq_len(seq_lens, b, a.Nmax);
+  const int k_eff = a.heads[bh].k_eff;
+  SelectScratch ws{reinterpret_cast<uint2*>(sm), 65536 / 8, reinterpret_cast<uint32_t*>(sm + 65536),
+                   reinterpret_cast<int*>(sm + 65536 + 8192)};
+  int M = 0;
+  const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
+  const int path = select_range<kSelNT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, 0, a.kcap,
+                                        idx + static_cast<long long>(bh) * a.kcap, nullptr, sc, &M);
+  if (threadIdx.x == 0) {
+    a.heads[bh].path = static_cast<uint32_t>(path);
+    a.heads[bh].cand_total = static_cast<uint32_t>(M);
+  }
+}
+
+template <typename T, int D, bool SELECT>
+static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
+                                  const void* V, int32_t* idx, const void* scores, int scores_int,
+                                  int chunk, float sl2, hipStream_t st) {
+  const int G = s.Hq / s.Hkv;
+  dim3 grid(a_nsplit(a), s.B * s.Hkv);
+  const size_t smem = attend_smem(a.nchunks, a.rps);
+#define HST_ATT(GM)                                                                             \
+  do {                                                                                          \
+    auto kern = attend_kernel<T, D, GM, SELECT>;                                                \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                     \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,              \
+                                       static_cast<int>(smem));                                 \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL(kern, grid, dim3(kAttNT), smem, st, static_cast<const T*>(q),            \
+                       static_cast<const T*>(K), static_cast<const T*>(V), idx, scores,         \
+                       scores_int, chunk, s.seq_lens, sl2, a);                                  \
+  } while (0)
+  if (G <= 1) HST_ATT(1);
+  else if (G <= 2) HST_ATT(2);
+  else if (G <= 4) HST_ATT(4);
+  else HST_ATT(8);
+#undef HST_ATT
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_combine_t(const hst_shape& s, const FusedArgs& a, float* out, float* lse,
+                                   hipStream_t st) {
+  const int G = s.Hq / s.Hkv;
+  dim3 grid(s.B * s.Hkv);
+  const int ns = a_nsplit(a);
+  if (G <= 1) hipLaunchKernelGGL((combine_kernel<D, 1>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
+  else if (G <= 2) hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
+  else if (G <= 4) hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
+  else hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
+                         const void* V, int32_t* idx, bool select, const void* scores, int scores_int,
+                         int chunk, float scale, float* out, float* lse, hipStream_t st) {
+  const float sl2 = scale * kLog2eF;
+  hipError_t e;
+  if (s.kv_dtype == HST_F32) {
+    if (s.d == 64)
+      e = select ? launch_attend_t<float, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
+                 : launch_attend_t<float, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+    else
+      e = select ? launch_attend_t<float, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
+                 : launch_attend_t<float, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+  } else {
+    if (s.d == 64)
+      e = select ? launch_attend_t<bf16, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
+                 : launch_attend_t<bf16, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+    else
+      e = select ? launch_attend_t<bf16, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
+                 : launch_attend_t<bf16, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+  }
+  if (e != hipSuccess) return e;
+  return s.d == 64 ? launch_combine_t<64>(s, a, out, lse, st) : launch_combine_t<128>(s, a, out, lse, st);
+}
+
+hipError_t launch_select_only(const hst_shape& s, const FusedArgs& a, int32_t* idx, const void* scores,
+                              int scores_int, int chunk, hipStream_t st) {
+  const size_t smem = 65536 + 8192 + static_cast<size_t>(a.nchunks + 1) * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_kernel, dim3(s.B * s.Hkv), dim3(kSelNT), smem, st, idx, scores, scores_int,
+                     chunk, s.seq_lens, a);
+  return hipGetLastError();
+}
+
+}  // namespace hst

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "hst.h"
+#include "hst_fused.h"
 #include "hst_launch.h"
 
 namespace {
@@ -49,15 +50,14 @@ hst_status check_norm_dtype(int nd) {
 
 int group(const hst_shape* s) { return s->Hq / s->Hkv; }
 
-size_t tables_bytes(const hst_shape* s, int L, int P) {
-  return static_cast<size_t>(s->B) * s->Hkv * (static_cast<size_t>(L) << P) * sizeof(float);
+// Limits of the per-head query preprocessing (its LDS holds G*L*P float64
+// projections and G*d float64 query components).
+hst_status check_soft_prep(const hst_shape* s, int L, int P) {
+  if (static_cast<long long>(group(s)) * L * P > 4096) return HST_ERR_UNSUPPORTED;
+  if (static_cast<long long>(group(s)) * s->d > 1024) return HST_ERR_UNSUPPORTED;
+  return HST_OK;
 }
-size_t qcodes_bytes(const hst_shape* s) {
-  return static_cast<size_t>(s->B) * s->Hq * 4 * sizeof(uint32_t);
-}
-size_t scores_bytes(const hst_shape* s) {
-  return static_cast<size_t>(s->B) * s->Hkv * s->Nmax * sizeof(float);
-}
+
 
 #define HST_TRY(x)                       \
   do {                                   \
@@ -97,22 +97,23 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
   const bool needk = op == HST_OP_SELECT_TOPK || op == HST_OP_SPARSE_ATTENTION ||
                      op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING;
   if (needk && k < 1) return HST_ERR_INVALID_ARG;
+  if (needk && k > hst::kMaxSplits * 1024) return HST_ERR_UNSUPPORTED;
+  if (soft && op != HST_OP_HASH_SOFTLSH) HST_TRY(check_soft_prep(shape, L, P));
   size_t b = 0;
   switch (op) {
     case HST_OP_HASH_SOFTLSH:
     case HST_OP_HASH_BINARY: b = 0; break;
-    case HST_OP_SCORE_SOFTLSH: b = align_up(tables_bytes(shape, L, P)); break;
-    case HST_OP_SCORE_HAMMING: b = align_up(qcodes_bytes(shape)); break;
-    case HST_OP_SELECT_TOPK: b = align_up(hst::select_ws_bytes(*shape)); break;
-    case HST_OP_SPARSE_ATTENTION: b = align_up(hst::attention_ws_bytes(*shape, k)); break;
+    case HST_OP_SCORE_SOFTLSH:
+    case HST_OP_SCORE_HAMMING:
+    case HST_OP_SELECT_TOPK:
+    case HST_OP_SPARSE_ATTENTION:
     case HST_OP_DECODE_SOFTLSH:
-      b = align_up(tables_bytes(shape, L, P)) + align_up(scores_bytes(shape)) +
-          align_up(hst::select_ws_bytes(*shape)) + align_up(hst::attention_ws_bytes(*shape, k));
+    case HST_OP_DECODE_HAMMING: {
+      const hst::FusedLayout f = hst::fused_layout(*shape, op, L, P, needk ? k : 1);
+      if (f.nchunks > hst::kMaxChunks) return HST_ERR_UNSUPPORTED;
+      b = align_up(f.bytes);
       break;
-    case HST_OP_DECODE_HAMMING:
-      b = align_up(qcodes_bytes(shape)) + align_up(scores_bytes(shape)) +
-          align_up(hst::select_ws_bytes(*shape)) + align_up(hst::attention_ws_bytes(*shape, k));
-      break;
+    }
     default: return HST_ERR_INVALID_ARG;
   }
   *bytes = b;
@@ -141,13 +142,13 @@ hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K, const voi
 }
 
 static hst_status score_softlsh_checks(const hst_shape* shape, const void* q, const void* W, int L,
-                                       int P, float tau, const uint8_t* ids, const void* vnorm,
+                                       int P, double tau, const uint8_t* ids, const void* vnorm,
                                        int norm_dtype) {
   HST_TRY(check_shape(shape));
   HST_TRY(check_lp(L, P));
   HST_TRY(check_norm_dtype(norm_dtype));
-  if (!(tau > 0.f) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
-  if (group(shape) * shape->d > 4096) return HST_ERR_UNSUPPORTED;
+  if (!(tau > 0.0) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
+  HST_TRY(check_soft_prep(shape, L, P));
   if (!ptr_ok(q) || !ptr_ok(W) || !ptr_ok(ids) || !ptr_ok(vnorm)) return HST_ERR_INVALID_ARG;
   return HST_OK;
 }
@@ -182,28 +183,25 @@ static hst_status workspace_check(int op, const hst_shape* shape, int L, int P, 
 }
 
 hst_status hst_score_keys_softlsh(const hst_shape* shape, const void* q, const void* W, int L,
-                                  int P, float tau, const uint8_t* ids, const void* vnorm,
+                                  int P, double tau, const uint8_t* ids, const void* vnorm,
                                   int norm_dtype, float* scores, void* ws, size_t ws_bytes,
                                   void* stream) {
   HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
   if (!ptr_ok(scores)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_SCORE_SOFTLSH, shape, L, P, 1, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  float* tables = static_cast<float*>(ws);
-  HST_TRY(hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables, st)));
-  return hip_status(
-      hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype, scores, st));
+  return hip_status(hst::fused_score_softlsh(*shape, q, W, L, P, tau, ids, vnorm, norm_dtype,
+                                             scores, ws, static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_query_tables_softlsh(const hst_shape* shape, const void* q, const void* W, int L,
-                                    int P, float tau, float* tables, void* stream) {
+                                    int P, double tau, float* tables, void* stream) {
   HST_TRY(check_shape(shape));
   HST_TRY(check_lp(L, P));
-  if (!(tau > 0.f) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
-  if (group(shape) * shape->d > 4096) return HST_ERR_UNSUPPORTED;
+  if (!(tau > 0.0) || !isfinite(tau)) return HST_ERR_INVALID_ARG;
+  HST_TRY(check_soft_prep(shape, L, P));
   if (!ptr_ok(q) || !ptr_ok(W) || !ptr_ok(tables)) return HST_ERR_INVALID_ARG;
-  return hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables,
-                                             static_cast<hipStream_t>(stream)));
+  return hip_status(hst::fused_tables_softlsh(*shape, q, W, L, P, tau, tables,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_score_scan_softlsh(const hst_shape* shape, const float* tables, int L, int P,
@@ -214,8 +212,8 @@ hst_status hst_score_scan_softlsh(const hst_shape* shape, const float* tables, i
   HST_TRY(check_norm_dtype(norm_dtype));
   if (!ptr_ok(tables) || !ptr_ok(ids) || !ptr_ok(vnorm) || !ptr_ok(scores))
     return HST_ERR_INVALID_ARG;
-  return hip_status(hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype,
-                                              scores, static_cast<hipStream_t>(stream)));
+  return hip_status(hst::fused_scan_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype, scores,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_score_keys_hamming(const hst_shape* shape, const void* q, const void* R,
@@ -224,10 +222,8 @@ hst_status hst_score_keys_hamming(const hst_shape* shape, const void* q, const v
   HST_TRY(score_hamming_checks(shape, q, R, code_bits, codes));
   if (!ptr_ok(scores)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_SCORE_HAMMING, shape, 0, 0, 1, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint32_t* qc = static_cast<uint32_t*>(ws);
-  HST_TRY(hip_status(hst::launch_query_codes(*shape, q, R, qc, st)));
-  return hip_status(hst::launch_score_hamming(*shape, qc, codes, scores, st));
+  return hip_status(hst::fused_score_hamming(*shape, q, R, codes, scores, ws,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_select_topk(const hst_shape* shape, int score_dtype, const void* scores, int k,
@@ -239,8 +235,8 @@ hst_status hst_select_topk(const hst_shape* shape, int score_dtype, const void* 
   if (!ptr_ok(scores) || !ptr_ok(idx)) return HST_ERR_INVALID_ARG;
   if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_SELECT_TOPK, shape, 0, 0, k, ws, ws_bytes));
-  return hip_status(hst::launch_select(*shape, score_dtype, scores, k, k_per_seq, idx, ws,
-                                       static_cast<hipStream_t>(stream)));
+  return hip_status(hst::fused_select(*shape, score_dtype, scores, k, k_per_seq, idx, ws,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q, const void* K,
@@ -250,12 +246,12 @@ hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q, co
   HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
   if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_SPARSE_ATTENTION, shape, 0, 0, k, ws, ws_bytes));
-  return hip_status(hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, ws,
-                                          static_cast<hipStream_t>(stream)));
+  return hip_status(hst::fused_attention(*shape, q, K, V, idx, k, scale, out, lse, ws,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q, const void* K,
-                                   const void* V, const void* W, int L, int P, float tau,
+                                   const void* V, const void* W, int L, int P, double tau,
                                    const uint8_t* ids, const void* vnorm, int norm_dtype, int k,
                                    const int32_t* k_per_seq, float scale, int32_t* idx,
                                    float* out, float* lse, void* ws, size_t ws_bytes,
@@ -265,21 +261,9 @@ hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q, const 
   if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
   if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH, shape, L, P, k, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* p = static_cast<char*>(ws);
-  float* tables = reinterpret_cast<float*>(p);
-  p += align_up(tables_bytes(shape, L, P));
-  float* scores = reinterpret_cast<float*>(p);
-  p += align_up(scores_bytes(shape));
-  void* sel_ws = p;
-  p += align_up(hst::select_ws_bytes(*shape));
-  void* attn_ws = p;
-  HST_TRY(hip_status(hst::launch_query_tables(*shape, q, W, L, P, tau, tables, st)));
-  HST_TRY(hip_status(
-      hst::launch_score_softlsh(*shape, tables, L, P, ids, vnorm, norm_dtype, scores, st)));
-  HST_TRY(hip_status(hst::launch_select(*shape, HST_F32, scores, k, k_per_seq, idx, sel_ws, st)));
-  return hip_status(
-      hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, attn_ws, st));
+  return hip_status(hst::fused_decode_softlsh(*shape, q, K, V, W, L, P, tau, ids, vnorm, norm_dtype,
+                                              k, k_per_seq, scale, idx, out, lse, ws,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const void* K,
@@ -292,20 +276,8 @@ hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const 
   if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
   if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
   HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* p = static_cast<char*>(ws);
-  uint32_t* qc = reinterpret_cast<uint32_t*>(p);
-  p += align_up(qcodes_bytes(shape));
-  int32_t* scores = reinterpret_cast<int32_t*>(p);
-  p += align_up(scores_bytes(shape));
-  void* sel_ws = p;
-  p += align_up(hst::select_ws_bytes(*shape));
-  void* attn_ws = p;
-  HST_TRY(hip_status(hst::launch_query_codes(*shape, q, R, qc, st)));
-  HST_TRY(hip_status(hst::launch_score_hamming(*shape, qc, codes, scores, st)));
-  HST_TRY(hip_status(hst::launch_select(*shape, HST_I32, scores, k, k_per_seq, idx, sel_ws, st)));
-  return hip_status(
-      hst::launch_attention(*shape, q, K, V, idx, k, scale, out, lse, attn_ws, st));
+  return hip_status(hst::fused_decode_hamming(*shape, q, K, V, R, codes, k, k_per_seq, scale, idx,
+                                              out, lse, ws, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

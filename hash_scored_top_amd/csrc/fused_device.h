@@ -1,0 +1,301 @@
+// Device helpers shared by the decode-path kernels (internal).
+#pragma once
+
+#include "block_select.h"
+#include "hst_common.h"
+#include "hst_fused.h"
+
+namespace hst {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  // integer finalizer ("lowbias32", C. Wellons): a fixed pseudo-random
+  // offset per stratum of the key sample
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// Position of sample i among n keys: one key per stratum [i*n/S, (i+1)*n/S).
+// S is kSample (a power of two) whenever n > kSample, else every key is taken.
+static_assert((kSample & (kSample - 1)) == 0, "sample size must be a power of two");
+__device__ __forceinline__ int sample_pos(int i, int S, int n) {
+  if (S >= n) return i;
+  constexpr int kShift = __builtin_ctz(kSample);
+  const unsigned long long nn = static_cast<unsigned long long>(n);
+  const uint32_t lo = static_cast<uint32_t>((static_cast<unsigned long long>(i) * nn) >> kShift);
+  const uint32_t hi = static_cast<uint32_t>((static_cast<unsigned long long>(i + 1) * nn) >> kShift);
+  const uint32_t w = hi - lo;
+  return static_cast<int>(lo + (w > 1 ? mix32(static_cast<uint32_t>(i) * 0x9e3779b9u + 0x632be5abu) % w : 0u));
+}
+
+__device__ __forceinline__ int keff_of(int kcap, const int32_t* k_per_seq, int b, int n) {
+  int k = kcap;
+  if (k_per_seq != nullptr) {
+    const int kb = k_per_seq[b];
+    k = kb < 0 ? 0 : (kb < kcap ? kb : kcap);
+  }
+  return k < n ? k : n;
+}
+
+// Rank in a sample of S_eff keys whose score bounds the top-k threshold from
+// below with a wide margin (mean + 4 sd of the binomial count + 8).
+__device__ __forceinline__ int sample_rank(int k, int n, int S_eff) {
+  if (n <= 0 || k <= 0) return 0;
+  const double f = static_cast<double>(k) / n;
+  const double mu = f * S_eff;
+  const double r = ceil(mu + 4.0 * sqrt(mu * (1.0 - f)) + 8.0);
+  return r >= S_eff ? S_eff : static_cast<int>(r);
+}
+
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+  if (LANES >= 2)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  if (LANES >= 4)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  if (LANES >= 8) v += __shfl_xor(v, 4, 8);
+  return v;
+}
+
+// Candidate slots of one head seen as one array in index order; entry i lives
+// in the chunk c with offs[c] <= i < offs[c+1].
+__device__ __forceinline__ int chunk_of(const int* offs, int nch, int i) {
+  int lo = 0, hi = nch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+struct SlotSrc {
+  const uint2* slots;
+  const int* offs;
+  int nch, chunk;
+  __device__ __forceinline__ uint2 at(int i) const {
+    const int c = chunk_of(offs, nch, i);
+    return slots[static_cast<long long>(c) * chunk + (i - offs[c])];
+  }
+  __device__ __forceinline__ uint32_t key(int i) const { return at(i).x; }
+  __device__ __forceinline__ int32_t idx(int i) const { return static_cast<int32_t>(at(i).y); }
+};
+
+// Stable compaction restricted to output positions [r0, r1): entry i of the
+// selection goes to out_g[p] (global, nullable) and out_l[p - r0] (LDS,
+// nullable) when its position p lies in the range.  Stops once r1 is passed.
+template <int NT, class Src>
+__device__ void block_compact_range(const Src& src, int M, const SelRule& rule, int r0, int r1,
+                                    int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc) {
+  int out_pos = 0, eq_seen = 0;
+  for (int base = 0; base < M && out_pos < r1; base += NT) {
+    const int i = base + threadIdx.x;
+    bool gt = false, eq = false;
+    if (i < M) {
+      const uint32_t m = src.key(i) & rule.mask;
+      gt = m > rule.prefix;
+      eq = m == rule.prefix;
+    }
+    int eqtot;
+    const int eqx = block_excl_scan<NT>(eq ? 1 : 0, sc, eqtot);
+    const bool sel = gt || (eq && eq_seen + eqx < rule.krem);
+    int seltot;
+    const int selx = block_excl_scan<NT>(sel ? 1 : 0, sc, seltot);
+    const int p = out_pos + selx;
+    if (sel && p >= r0 && p < r1) {
+      const int32_t v = src.idx(i);
+      if (out_g != nullptr) out_g[p] = v;
+      if (out_l != nullptr) out_l[p - r0] = v;
+    }
+    out_pos += seltot;
+    eq_seen += eqtot;
+  }
+}
+
+// Exact selection over M <= NT * PER (key, index) entries in LDS, stored in
+// index order.  Each thread keeps a contiguous segment of PER keys in
+// registers, so the radix passes and the final compaction need only a few
+// block-wide steps; the compaction is one scan of packed (greater, equal)
+// counts.  Writes the selected indices at output positions [r0, r1).
+template <int NT, int PER>
+__device__ void select_lds_segments(const uint2* cand, int M, int k, int r0, int r1, int32_t* out_g,
+                                    int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+  const int s0 = threadIdx.x * PER;
+  uint32_t key[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) key[e] = s0 + e < M ? cand[s0 + e].x : 0u;
+  uint32_t mask = 0u, prefix = 0u;
+  int krem = k >= M ? M : k;
+  if (k < M) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (s0 + e < M) {
+        mn = min(mn, key[e]);
+        mx = max(mx, key[e]);
+      }
+    block_minmax<NT>(mn, mx, sc);
+    if (mn != mx) {
+      const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
+      mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
+      prefix = mn & mask;
+      int lo = hb + 1;
+      while (lo > 0) {
+        const int width = lo < 11 ? lo : 11;
+        const int sh = lo - width;
+        const int nb = 1 << width;
+        for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if (s0 + e < M && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
+        __syncthreads();
+        const int per = (nb + NT - 1) / NT;  // bins per thread, from the top digit down
+        int mine = 0;
+        for (int i = 0; i < per; ++i) {
+          const int r = threadIdx.x * per + i;
+          if (r < nb) mine += static_cast<int>(hist[nb - 1 - r]);
+        }
+        int tot;
+        const int above = block_excl_scan<NT>(mine, sc, tot);
+        if (above < krem && krem <= above + mine) {
+          int cum = above;
+          for (int i = 0; i < per; ++i) {
+            const int digit = nb - 1 - (threadIdx.x * per + i);
+            const int c = static_cast<int>(hist[digit]);
+            if (cum + c >= krem) {
+              sc.found[0] = digit;
+              sc.found[1] = krem - cum;
+              sc.found[2] = c;
+              break;
+            }
+            cum += c;
+          }
+        }
+        __syncthreads();
+        const int digit = sc.found[0];
+        krem = sc.found[1];
+        const int cnt = sc.found[2];
+        __syncthreads();
+        prefix |= static_cast<uint32_t>(digit) << sh;
+        mask |= static_cast<uint32_t>(nb - 1) << sh;
+        lo = sh;
+        if (cnt == krem) break;  // the whole bin is taken
+      }
+    }
+  }
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (s0 + e < M) {
+      const uint32_t m = key[e] & mask;
+      gtc += m > prefix;
+      eqc += m == prefix;
+    }
+  int tot;
+  const int ex = block_excl_scan<NT>(gtc | (eqc << 16), sc, tot);
+  const int eq_before = ex >> 16;
+  int pos = (ex & 0xffff) + min(eq_before, krem);
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (s0 + e < M) {
+      const uint32_t m = key[e] & mask;
+      bool sel = m > prefix;
+      if (m == prefix) sel = eq_seen++ < krem;
+      if (sel) {
+        if (pos >= r0 && pos < r1) {
+          const int32_t v = static_cast<int32_t>(cand[s0 + e].y);
+          if (out_g != nullptr) out_g[pos] = v;
+          if (out_l != nullptr) out_l[pos - r0] = v;
+        }
+        ++pos;
+      }
+    }
+}
+
+struct SelectScratch {
+  uint2* cand;     // LDS, cap entries
+  int cap;
+  uint32_t* hist;  // LDS, 2048 words
+  int* offs;       // LDS, nchunks + 1
+};
+
+// The head's exact top-k (k_eff keys, ties to the lower index) from the
+// candidate slots the scan wrote (or, when fewer than k_eff keys passed the
+// threshold, from the whole score row).  Writes the selected indices at
+// output positions [r0, r1) (see block_compact_range) and -1 at positions
+// in [max(r0, k_eff), r1) of out_g.  Returns the selection path taken
+// (0: candidates in LDS, 1: candidates read from HBM, 2: whole score row).
+template <int NT>
+__device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int chunk,
+                            const void* scores_row, bool scores_int, const SelectScratch& ws,
+                            int r0, int r1, int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc,
+                            int* cand_total) {
+  const int nch = (n + chunk - 1) / chunk;
+  const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
+  const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
+  int run = 0;
+  for (int c0 = 0; c0 < nch; c0 += NT) {
+    const int c = c0 + static_cast<int>(threadIdx.x);
+    const int v = c < nch ? static_cast<int>(cnt[c]) : 0;
+    int tot;
+    const int x = block_excl_scan<NT>(v, sc, tot);
+    if (c < nch) ws.offs[c] = run + x;
+    run += tot;
+  }
+  if (threadIdx.x == 0) ws.offs[nch] = run;
+  __syncthreads();
+  const int M = run;
+  *cand_total = M;
+  int path = 0;
+  if (k_eff > 0) {
+    if (M >= k_eff && M <= ws.cap) {
+      for (int i0 = 0; i0 < M; i0 += NT * 8) {  // eight independent loads in flight
+        uint2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
+          if (i < M) {
+            const int c = chunk_of(ws.offs, nch, i);
+            v[u] = slots[static_cast<long long>(c) * chunk + (i - ws.offs[c])];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
+          if (i < M) ws.cand[i] = v[u];
+        }
+      }
+      __syncthreads();
+      select_lds_segments<NT, (8192 + NT - 1) / NT>(ws.cand, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
+    } else if (M >= k_eff) {
+      path = 1;
+      const SlotSrc src{slots, ws.offs, nch, chunk};
+      const SelRule rule = block_select_rule<NT>(src, M, k_eff, ws.hist, sc);
+      block_compact_range<NT>(src, M, rule, r0, r1, out_g, out_l, sc);
+    } else {
+      path = 2;  // the sample overestimated the threshold: use every score
+      if (scores_int) {
+        const I32RowSrc src{static_cast<const int32_t*>(scores_row)};
+        const SelRule rule = block_select_rule<NT>(src, n, k_eff, ws.hist, sc);
+        block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
+      } else {
+        const F32RowSrc src{static_cast<const float*>(scores_row)};
+        const SelRule rule = block_select_rule<NT>(src, n, k_eff, ws.hist, sc);
+        block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
+      }
+    }
+  }
+  if (out_g != nullptr)
+    for (int p = max(r0, k_eff) + static_cast<int>(threadIdx.x); p < r1; p += NT) out_g[p] = -1;
+  __syncthreads();
+  return path;
+}
+
+}  // namespace hst

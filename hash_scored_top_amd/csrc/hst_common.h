@@ -10,6 +10,10 @@ namespace hst {
 
 constexpr int kWave = 64;
 
+// Native 128-bit vector (stays in registers where HIP's struct vector types
+// can end up in scratch memory when held in arrays).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // bf16 element stored as its 16 bit pattern.
 struct bf16 {
   uint16_t bits;

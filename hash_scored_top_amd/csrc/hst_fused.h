@@ -1,0 +1,94 @@
+// Workspace layout and kernel arguments of the fused decode path (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hst.h"
+
+namespace hst {
+
+constexpr int kSample = 2048;      // keys sampled per head for the candidate threshold
+constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
+constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
+
+enum ScanKind { kScanSoftFast = 0, kScanSoftAny = 1, kScanHamming = 2, kScanGivenF32 = 3, kScanGivenI32 = 4 };
+
+// Per (sequence, kv head) state in the workspace header, written by prep.
+struct HeadState {
+  uint32_t theta;       // candidate threshold (order key)
+  int32_t k_eff;        // keys to select
+  int32_t n;            // context length
+  uint32_t cand_total;  // candidates the scan found (diagnostic)
+  uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every score (diagnostic)
+  uint32_t pad[11];
+};
+static_assert(sizeof(HeadState) == 64, "head state stride");
+
+struct FusedLayout {
+  size_t off_heads, off_tables, off_qcodes, off_scores, off_counts, off_slots, off_part_o,
+      off_part_ml, bytes;
+  int chunk, nchunks, sample, rps, nsplit, kind;
+};
+
+struct FusedArgs {
+  int Hq, Hkv, d, Nmax, L, P;
+  double inv_tau;
+  int kcap, sample, nchunks, rps, nsplit, region_bytes;
+  HeadState* heads;
+  float* tables;     // [B*Hkv][2^P][L] bucket-major
+  uint32_t* qcodes;  // [B*Hkv][G][4]
+  uint32_t* counts;  // [B*Hkv][nchunks]
+  uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index)
+  float* part_o;     // [B*Hq][nsplit][d]
+  float* part_ml;    // [B*Hq][nsplit][2]
+};
+__host__ __device__ inline int a_nsplit(const FusedArgs& a) { return a.nsplit; }
+__host__ __device__ inline size_t hst_align16(size_t x) { return (x + 15) / 16 * 16; }
+
+FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap);
+
+// kernel launchers (prep.hip, scan.hip, attend.hip)
+hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* q, const void* W,
+                            const uint8_t* ids, const void* vnorm, int norm_f16,
+                            const int32_t* kps, hipStream_t st);
+hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const void* q, const void* R,
+                               const uint32_t* codes, const int32_t* kps, hipStream_t st);
+hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
+                             const void* scores, const int32_t* kps, hipStream_t st);
+int scan_chunk(int L);
+hipError_t launch_scan(const hst_shape& s, const FusedArgs& a, int kind, const void* src,
+                       const void* vnorm, int norm_f16, void* scores_out, int filter, hipStream_t st);
+hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
+                         const void* V, int32_t* idx, bool select, const void* scores, int scores_int,
+                         int chunk, float scale, float* out, float* lse, hipStream_t st);
+hipError_t launch_select_only(const hst_shape& s, const FusedArgs& a, int32_t* idx, const void* scores,
+                              int scores_int, int chunk, hipStream_t st);
+
+hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
+                                const void* W, int L, int P, double tau, const uint8_t* ids,
+                                const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
+                                float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                hipStream_t st);
+hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
+                                const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
+                                float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                hipStream_t st);
+hipError_t fused_score_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                               double tau, const uint8_t* ids, const void* vnorm, int norm_dtype,
+                               float* scores, void* ws, hipStream_t st);
+hipError_t fused_score_hamming(const hst_shape& s, const void* q, const void* R,
+                               const uint32_t* codes, int32_t* scores, void* ws, hipStream_t st);
+hipError_t fused_tables_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                                double tau, float* tables, hipStream_t st);
+hipError_t fused_scan_softlsh(const hst_shape& s, const float* tables, int L, int P,
+                              const uint8_t* ids, const void* vnorm, int norm_dtype, float* scores,
+                              hipStream_t st);
+hipError_t fused_select(const hst_shape& s, int score_dtype, const void* scores, int kcap,
+                        const int32_t* kps, int32_t* idx, void* ws, hipStream_t st);
+hipError_t fused_attention(const hst_shape& s, const void* q, const void* K, const void* V,
+                           const int32_t* idx, int kcap, float scale, float* out, float* lse,
+                           void* ws, hipStream_t st);
+
+}  // namespace hst

@@ -1,0 +1,173 @@
+// Host-side composition of the decode path: workspace layout and the launch
+// sequence of every C-ABI operation.
+//
+//   decode step (soft-LSH or binary codes):
+//     prep  (one workgroup per kv head: query tables / codes, sample threshold)
+//     scan  (score every key once; candidates >= threshold into chunk slots)
+//     attend (each split derives the exact top-k from the candidates and
+//             attends over its part of the selected rows)
+//     combine (merge the splits through their log-sum-exp)
+#include "hst_fused.h"
+#include "hst_launch.h"
+
+namespace hst {
+
+FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
+  FusedLayout f{};
+  const long long BH = static_cast<long long>(s.B) * s.Hkv;
+  const bool soft = op == HST_OP_SCORE_SOFTLSH || op == HST_OP_DECODE_SOFTLSH;
+  const bool ham = op == HST_OP_SCORE_HAMMING || op == HST_OP_DECODE_HAMMING;
+  const bool decode = op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING;
+  const bool select = op == HST_OP_SELECT_TOPK || decode;
+  const bool attn = op == HST_OP_SPARSE_ATTENTION || decode;
+  f.kind = soft ? ((L == 16 || L == 32 || L == 64 || L == 128) ? kScanSoftFast : kScanSoftAny)
+               : (ham ? kScanHamming : kScanGivenF32);
+  f.chunk = soft ? scan_chunk(L) : scan_chunk(0);
+  f.nchunks = select ? static_cast<int>((s.Nmax + f.chunk - 1) / f.chunk) : 0;
+  f.sample = select ? kSample : 0;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o += (bytes + 255) / 256 * 256;
+    return r;
+  };
+  f.off_heads = take(BH * sizeof(HeadState));
+  if (soft) f.off_tables = take(BH * (static_cast<size_t>(L) << P) * sizeof(float));
+  if (ham) f.off_qcodes = take(static_cast<size_t>(s.B) * s.Hq * 16);
+  if (decode) f.off_scores = take(BH * static_cast<size_t>(s.Nmax) * 4);
+  if (select) {
+    f.off_counts = take(BH * f.nchunks * 4);
+    f.off_slots = take(BH * f.nchunks * static_cast<size_t>(f.chunk) * 8);
+  }
+  if (attn) {
+    const long long rows = static_cast<long long>(kcap) * BH;
+    long long r = (rows + 511) / 512;  // about two splits per CU
+    r = (r + 63) / 64 * 64;
+    if (r < 64) r = 64;
+    if (r > 1024) r = 1024;
+    if ((kcap + r - 1) / r > kMaxSplits) r = (kcap + kMaxSplits - 1) / kMaxSplits;
+    f.rps = static_cast<int>(r);
+    f.nsplit = static_cast<int>((kcap + r - 1) / r);
+    const size_t parts = static_cast<size_t>(s.B) * s.Hq * f.nsplit;
+    f.off_part_o = take(parts * s.d * 4);
+    f.off_part_ml = take(parts * 2 * 4);
+  }
+  f.bytes = o;
+  return f;
+}
+
+static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, int L, int P,
+                           double tau, int kcap) {
+  FusedArgs a{};
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.d = s.d;
+  a.Nmax = s.Nmax;
+  a.L = L;
+  a.P = P;
+  a.inv_tau = tau > 0.0 ? 1.0 / tau : 0.0;
+  a.kcap = kcap;
+  a.sample = f.sample;
+  a.nchunks = f.nchunks;
+  a.rps = f.rps;
+  a.nsplit = f.nsplit;
+  a.region_bytes = 65536;
+  char* p = static_cast<char*>(ws);
+  if (p != nullptr) {
+    a.heads = reinterpret_cast<HeadState*>(p + f.off_heads);
+    a.tables = reinterpret_cast<float*>(p + f.off_tables);
+    a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
+    a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
+    a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
+    a.part_o = reinterpret_cast<float*>(p + f.off_part_o);
+    a.part_ml = reinterpret_cast<float*>(p + f.off_part_ml);
+  }
+  return a;
+}
+
+#define HST_CHECK(x)                   \
+  do {                                 \
+    hipError_t _e = (x);               \
+    if (_e != hipSuccess) return _e;   \
+  } while (0)
+
+hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
+                                const void* W, int L, int P, double tau, const uint8_t* ids,
+                                const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
+                                float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_DECODE_SOFTLSH, L, P, kcap);
+  const FusedArgs a = make_args(s, f, ws, L, P, tau, kcap);
+  const int f16 = norm_dtype == HST_F16;
+  float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + f.off_scores);
+  HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
+  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, st));
+  return launch_attend(s, a, q, K, V, idx, true, scores, 0, f.chunk, scale, out, lse, st);
+}
+
+hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
+                                const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
+                                float scale, int32_t* idx, float* out, float* lse, void* ws,
+                                hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_DECODE_HAMMING, 0, 0, kcap);
+  const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
+  int32_t* scores = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + f.off_scores);
+  HST_CHECK(launch_prep_hamming(s, a, q, R, codes, kps, st));
+  HST_CHECK(launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 1, st));
+  return launch_attend(s, a, q, K, V, idx, true, scores, 1, f.chunk, scale, out, lse, st);
+}
+
+hipError_t fused_score_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                               double tau, const uint8_t* ids, const void* vnorm, int norm_dtype,
+                               float* scores, void* ws, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
+  const FusedArgs a = make_args(s, f, ws, L, P, tau, 1);
+  HST_CHECK(launch_prep_soft(s, a, q, W, nullptr, nullptr, 0, nullptr, st));
+  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, st);
+}
+
+hipError_t fused_score_hamming(const hst_shape& s, const void* q, const void* R,
+                               const uint32_t* codes, int32_t* scores, void* ws, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SCORE_HAMMING, 0, 0, 1);
+  const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, 1);
+  HST_CHECK(launch_prep_hamming(s, a, q, R, codes, nullptr, st));
+  return launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 0, st);
+}
+
+hipError_t fused_tables_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                                double tau, float* tables, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
+  FusedArgs a = make_args(s, f, nullptr, L, P, tau, 1);
+  a.tables = tables;
+  return launch_prep_soft(s, a, q, W, nullptr, nullptr, 0, nullptr, st);
+}
+
+hipError_t fused_scan_softlsh(const hst_shape& s, const float* tables, int L, int P,
+                              const uint8_t* ids, const void* vnorm, int norm_dtype, float* scores,
+                              hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
+  FusedArgs a = make_args(s, f, nullptr, L, P, 0.0, 1);
+  a.tables = const_cast<float*>(tables);
+  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, st);
+}
+
+hipError_t fused_select(const hst_shape& s, int score_dtype, const void* scores, int kcap,
+                        const int32_t* kps, int32_t* idx, void* ws, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SELECT_TOPK, 0, 0, kcap);
+  const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
+  const int is_int = score_dtype == HST_I32;
+  HST_CHECK(launch_prep_given(s, a, score_dtype, scores, kps, st));
+  HST_CHECK(launch_scan(s, a, is_int ? kScanGivenI32 : kScanGivenF32, scores, nullptr, 0, nullptr, 1, st));
+  return launch_select_only(s, a, idx, scores, is_int, f.chunk, st);
+}
+
+hipError_t fused_attention(const hst_shape& s, const void* q, const void* K, const void* V,
+                           const int32_t* idx, int kcap, float scale, float* out, float* lse,
+                           void* ws, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap);
+  const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
+  return launch_attend(s, a, q, K, V, const_cast<int32_t*>(idx), false, nullptr, 0, f.chunk, scale,
+                       out, lse, st);
+}
+
+}  // namespace hst

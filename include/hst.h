@@ -40,6 +40,10 @@
  *     N_b in [0, Nmax]; NULL means every N_b = Nmax.  Rows j >= N_b are
  *     never read or written by any call.
  *   - Pointers must be 16-byte aligned.
+ *   - Workspaces: a caller-owned device buffer of at least
+ *     hst_workspace_size() bytes, 256-byte aligned, with no required initial
+ *     contents.  Calls that share a workspace must not overlap in time (use
+ *     one stream per workspace).
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *     null stream) and never synchronizes.  Arguments are validated on the
  *     host before anything is enqueued; on error nothing is launched.
@@ -141,7 +145,7 @@ hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K,
  * in float32 for j < N_b.  tau > 0.  Workspace holds the tables.
  */
 hst_status hst_score_keys_softlsh(const hst_shape* shape, const void* q,
-                                  const void* W, int L, int P, float tau,
+                                  const void* W, int L, int P, double tau,
                                   const uint8_t* ids, const void* vnorm,
                                   int norm_dtype, float* scores, void* ws,
                                   size_t ws_bytes, void* stream);
@@ -149,14 +153,16 @@ hst_status hst_score_keys_softlsh(const hst_shape* shape, const void* q,
 /*
  * The two steps of hst_score_keys_softlsh as separate calls.
  * hst_query_tables_softlsh writes the per-(sequence, kv head) bucket
- * probability tables T [B][Hkv][L][2^P] float32 (the soft assignment of the
- * query, summed over the G query heads of the kv head).
+ * probability tables, bucket-major: T[b][h][c][l] float32, shape
+ * [B][Hkv][2^P][L] (the soft assignment of the query, summed over the G
+ * query heads of the kv head).
  * hst_score_scan_softlsh streams the bucket ids and value norms of every key
- * once and writes scores[b][h][j] = vnorm * sum_l T[b][h][l][ids[b][h][j][l]]
- * for j < N_b.  No workspace.
+ * once and writes scores[b][h][j] = vnorm * sum_l T[b][h][ids[b][h][j][l]][l]
+ * for j < N_b.  No workspace.  Both require shape->Hq / shape->Hkv query
+ * heads per kv head as for hst_score_keys_softlsh.
  */
 hst_status hst_query_tables_softlsh(const hst_shape* shape, const void* q,
-                                    const void* W, int L, int P, float tau,
+                                    const void* W, int L, int P, double tau,
                                     float* tables, void* stream);
 hst_status hst_score_scan_softlsh(const hst_shape* shape, const float* tables,
                                   int L, int P, const uint8_t* ids,
@@ -213,7 +219,7 @@ hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q,
  */
 hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q,
                                    const void* K, const void* V,
-                                   const void* W, int L, int P, float tau,
+                                   const void* W, int L, int P, double tau,
                                    const uint8_t* ids, const void* vnorm,
                                    int norm_dtype, int k,
                                    const int32_t* k_per_seq, float scale,

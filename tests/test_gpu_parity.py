@@ -349,3 +349,122 @@ def test_decode_is_deterministic():
     i1, o1, l1 = (t.clone() for t in step(d["q"], d["K"], d["V"], d["W"], ids, vn))
     i2, o2, l2 = step(d["q"], d["K"], d["V"], d["W"], ids, vn)
     assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------- fused select paths
+
+def _sample_positions(n, S=2048):
+    """Stratified sample positions of the candidate-threshold estimate."""
+    if S >= n:
+        return list(range(n))
+
+    def mix32(x):
+        x &= 0xFFFFFFFF
+        x ^= x >> 16
+        x = (x * 0x7FEB352D) & 0xFFFFFFFF
+        x ^= x >> 15
+        x = (x * 0x846CA68B) & 0xFFFFFFFF
+        x ^= x >> 16
+        return x
+
+    out = []
+    for i in range(S):
+        lo, hi = i * n // S, (i + 1) * n // S
+        w = hi - lo
+        off = mix32((i * 0x9E3779B9 + 0x632BE5AB) & 0xFFFFFFFF) % w if w > 1 else 0
+        out.append(lo + off)
+    return out
+
+
+def _select_raw(scores_np, k):
+    """Calls hst_select_topk with a workspace we own; returns (idx, path per row)."""
+    import ctypes
+    hst = _hst()
+    from hash_scored_top_amd import _lib as Lb
+    B, H, N = scores_np.shape
+    t = torch.from_numpy(np.ascontiguousarray(scores_np)).to(DEV)
+    shape = Lb.HstShape(B, H, H, 128, N, Lb.HST_BF16, None)
+    nbytes = Lb.workspace_size(Lb.HST_OP_SELECT_TOPK, shape, k=k)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    idx = torch.empty((B, H, k), dtype=torch.int32, device=DEV)
+    sd = Lb.HST_F32 if scores_np.dtype == np.float32 else Lb.HST_I32
+    st = Lb._C.hst_select_topk(ctypes.byref(shape), sd, t.data_ptr(), k, None, idx.data_ptr(),
+                               ws.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    head = ws[:B * H * 64].cpu().numpy().view(np.uint32).reshape(B * H, 16)
+    return idx.cpu().numpy(), head[:, 4].copy()  # selection path of each row
+
+
+def test_select_paths_lds_hbm_fallback():
+    n = 20000
+    rng = np.random.default_rng(11)
+    # path 0: ordinary scores, candidates fit in LDS
+    s0 = rng.random((1, 1, n)).astype(np.float32)
+    # path 1: all scores equal -> every key is a candidate (more than LDS holds)
+    s1 = np.full((1, 1, n), 0.5, np.float32)
+    # path 2: high scores exactly at the sampled positions -> too few candidates
+    s2 = np.zeros((1, 1, n), np.float32)
+    s2[0, 0, _sample_positions(n)] = 10.0 + np.arange(2048, dtype=np.float32) * 1e-3
+    for s, want_path, k in ((s0, 0, 600), (s1, 1, 3000), (s2, 2, 3000)):
+        idx, path = _select_raw(s, k)
+        ref = O.select_topk(s[0, 0].astype(np.float64), k)
+        np.testing.assert_array_equal(idx[0, 0], ref)
+        assert path[0] == want_path, (want_path, path)
+
+
+def test_select_int_fallback_and_reuse():
+    n = 30000
+    s = np.zeros((2, 1, n), np.int32)
+    s[:, 0, _sample_positions(n)] = 7
+    s[1, 0, ::5] = 3
+    for _ in range(2):  # the same workspace type, counters reset between calls
+        idx, path = _select_raw(s, 2500)
+        for b in range(2):
+            np.testing.assert_array_equal(idx[b, 0], O.select_topk(s[b, 0].astype(np.int64), 2500))
+        assert path[0] == 2
+
+
+def test_query_tables_and_score_scan_entry_points():
+    hst = _hst()
+    from tests.gpu_helpers import norms_to_dev
+    w = MED_SOFT
+    x, d = inputs(w)
+    T = hst.hst_query_tables_softlsh(d["q"], d["W"], w.L, w.P, w.tau, d["K"]).cpu().numpy()
+    ids = np.zeros((w.B, w.Hkv, w.N, w.L), dtype=np.uint8)
+    vn = np.zeros((w.B, w.Hkv, w.N))
+    refs = {}
+    for b in range(w.B):
+        n = int(x["seq_lens"][b])
+        for h in range(w.Hkv):
+            q64, K64, V64 = slab64(w, x, b, h)
+            W64 = f64(x["W"][h], w.kv_dtype)
+            Tr = O.query_tables(q64, W64, w.L, w.P, w.tau)
+            np.testing.assert_allclose(T[b, h].T, Tr, rtol=2e-7, atol=0)
+            ids[b, h, :n] = O.hash_keys_softlsh(K64, W64, w.L, w.P)
+            vn[b, h, :n] = O.value_norms(V64, w.norm_dtype)
+            refs[(b, h)] = O.score_softlsh(Tr, ids[b, h, :n], vn[b, h, :n])
+    sc = hst.hst_score_scan_softlsh(torch.from_numpy(T).to(DEV), torch.from_numpy(ids).to(DEV),
+                                    norms_to_dev(vn, w.norm_dtype, DEV), d["K"], w.Hq,
+                                    seq_lens=d["seq_lens"]).cpu().numpy()
+    for (b, h), ref in refs.items():
+        rel = np.abs(sc[b, h, :ref.shape[0]] - ref) / ref
+        assert rel.max() <= 1e-5
+
+
+def test_decode_workspace_reuse_matches_fresh():
+    hst = _hst()
+    from tests.gpu_helpers import norm_torch_dtype
+    w = MED_SOFT
+    x, d = inputs(w)
+    ids, vn = hst.hst_hash_keys_softlsh(d["K"], d["V"], d["W"], w.L, w.P,
+                                        norm_torch_dtype(w.norm_dtype), seq_lens=d["seq_lens"])
+    step = hst.DecodeSoftLSH(d["K"], w.Hq, w.L, w.P, w.tau, w.k_max(), vn.dtype,
+                             seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
+    qs = [d["q"], torch.flip(d["q"], dims=[1]).contiguous(), d["q"] * 0.5]
+    for q in qs + qs:
+        i1, o1, l1 = (t.clone() for t in step(q, d["K"], d["V"], d["W"], ids, vn))
+        fresh = hst.DecodeSoftLSH(d["K"], w.Hq, w.L, w.P, w.tau, w.k_max(), vn.dtype,
+                                  seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
+        i2, o2, l2 = fresh(q, d["K"], d["V"], d["W"], ids, vn)
+        assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
