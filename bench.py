@@ -238,22 +238,23 @@ def main():
     ms_per_step = total_ms / args.steps
     log(f"step {ms_per_step * 1e3:.2f} us (p50 {np.percentile(per, 50):.2f} us)")
 
-    # dominant kernel, timed alone with events on the same stream
+    # dominant kernel (the score scan: every key's metadata once), timed alone
+    # with events on the stream it is launched on
+    tot_keys = sum(int(n) for n in lens) * w.Hkv
     if w.scheme == "softlsh":
-        kname = "score_softlsh_kernel"
-        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "score.hip")
+        kname = "scan_softlsh_kernel"
+        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
         tables = hst.hst_query_tables_softlsh(q, Wp, w.L, w.P, w.tau, K, seq_lens=sl)
         sc = torch.empty((w.B, w.Hkv, w.N), dtype=torch.float32, device=dev)
-        kbytes = meta_b
+        kbytes = meta_b + 4 * tot_keys  # metadata read + one float32 score written per key
         launch = lambda i: hst.hst_score_scan_softlsh(tables, sets[i % R][2], sets[i % R][3], K,
                                                       w.Hq, seq_lens=sl, scores=sc)
     else:
-        kname = "sparse_attn_split_kernel"
-        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "attention.hip")
-        kbytes = gath_b + qo_b
-        idx = step.idx.clone()
-        launch = lambda i: hst.hst_sparse_decode_attention(q, sets[i % R][0], sets[i % R][1], idx,
-                                                           seq_lens=sl)
+        # no entry point launches the binary-code scan alone: time query codes + scan
+        kname = "prep_hamming+scan_lane_kernel"
+        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
+        kbytes = meta_b + 4 * tot_keys
+        launch = lambda i: hst.hst_score_keys_hamming(q, Rp, sets[i % R][2], K, seq_lens=sl)
     for i in range(5):
         launch(i)
     kst = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_iters)]

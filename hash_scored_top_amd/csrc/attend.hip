@@ -17,41 +17,56 @@ namespace hst {
 constexpr int kAttNT = 512;
 constexpr int kSelNT = 1024;
 
+// A lane's EPL elements of a K/V/q row: raw load (issued first, so that all
+// loads of a batch are in flight together) and conversion to float.
 template <typename T, int EPL>
 struct RowLd;
 template <>
 struct RowLd<bf16, 8> {
-  static __device__ __forceinline__ void ld(const bf16* p, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  typedef u32x4 raw;
+  static __device__ __forceinline__ raw load(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+  static __device__ __forceinline__ void cvt(const raw& v, float (&x)[8]) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
     x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
   }
 };
 template <>
 struct RowLd<bf16, 4> {
-  static __device__ __forceinline__ void ld(const bf16* p, float (&x)[4]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+  typedef uint2 raw;
+  static __device__ __forceinline__ raw load(const bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ void cvt(const raw& v, float (&x)[4]) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
   }
 };
+struct U32x8 {
+  u32x4 a, b;
+};
 template <>
 struct RowLd<float, 8> {
-  static __device__ __forceinline__ void ld(const float* p, float (&x)[8]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    const float4 v = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  typedef U32x8 raw;
+  static __device__ __forceinline__ raw load(const float* p) {
+    return U32x8{reinterpret_cast<const u32x4*>(p)[0], reinterpret_cast<const u32x4*>(p)[1]};
+  }
+  static __device__ __forceinline__ void cvt(const raw& v, float (&x)[8]) {
+    x[0] = __uint_as_float(v.a.x); x[1] = __uint_as_float(v.a.y);
+    x[2] = __uint_as_float(v.a.z); x[3] = __uint_as_float(v.a.w);
+    x[4] = __uint_as_float(v.b.x); x[5] = __uint_as_float(v.b.y);
+    x[6] = __uint_as_float(v.b.z); x[7] = __uint_as_float(v.b.w);
   }
 };
 template <>
 struct RowLd<float, 4> {
-  static __device__ __forceinline__ void ld(const float* p, float (&x)[4]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+  typedef u32x4 raw;
+  static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const u32x4*>(p); }
+  static __device__ __forceinline__ void cvt(const raw& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
   }
 };
 
-// LDS of the attend kernel: [64 KB: candidates, later the wave partials]
-// [hist 8 KB][chunk offsets][rows of this split]
+// LDS of the attend kernel: [64 KB: candidate keys and indices, later the
+// wave partials][hist 8 KB][chunk offsets][rows of this split]
+static_assert(8 * kSelCap <= 65536, "candidate region");
 size_t attend_smem(int nchunks, int rps) {
   return 65536 + 8192 + static_cast<size_t>(nchunks + 1) * 4 + static_cast<size_t>(rps) * 4;
 }
@@ -86,7 +101,8 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   int nrows;
   if (SELECT) {
     const int k_eff = a.heads[bh].k_eff;
-    SelectScratch ws{reinterpret_cast<uint2*>(sm), 65536 / 8, reinterpret_cast<uint32_t*>(sm + 65536), offs};
+    SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
+                     reinterpret_cast<uint32_t*>(sm + 65536), offs};
     int M = 0;
     const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
     const int path = select_range<NT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, r0, r1, irow,
@@ -103,15 +119,21 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   __syncthreads();
 
   float qv[GMAX][EPL];
+  {
+    typename RowLd<T, EPL>::raw qr[GMAX];
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    if (g < G) {
-      RowLd<T, EPL>::ld(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL, qv[g]);
+    for (int g = 0; g < GMAX; ++g)
+      if (g < G) qr[g] = RowLd<T, EPL>::load(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
-    } else {
+    for (int g = 0; g < GMAX; ++g) {
+      if (g < G) {
+        RowLd<T, EPL>::cvt(qr[g], qv[g]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
+        for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
+      }
     }
   }
   float m[GMAX], l[GMAX], o[GMAX][EPL];
@@ -124,27 +146,36 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   }
   const long long kvb = static_cast<long long>(bh) * a.Nmax;
   for (int rb = grp; rb < nrows; rb += NG * U) {
-    float kx[U][EPL], vx[U][EPL];
+    // all row loads of the batch issued back to back, without branches: a
+    // row that is absent or out of range reads row 0 of the head (allocated
+    // whenever the head exists) and is skipped below
+    typename RowLd<T, EPL>::raw kr[U], vr[U];
     bool ok[U];
+    long long off[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = rb + u * NG;
       const int j = r < nrows ? rows[r] : -1;
       ok[u] = j >= 0 && j < n;
-      if (ok[u]) {
-        RowLd<T, EPL>::ld(K + (kvb + j) * D + sub * EPL, kx[u]);
-        RowLd<T, EPL>::ld(V + (kvb + j) * D + sub * EPL, vx[u]);
-      }
+      off[u] = (kvb + (ok[u] ? j : 0)) * D + sub * EPL;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kr[u] = RowLd<T, EPL>::load(K + off[u]);
+      vr[u] = RowLd<T, EPL>::load(V + off[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;  // uniform over the 16 lanes of a row group
+      float kx[EPL], vx[EPL];
+      RowLd<T, EPL>::cvt(kr[u], kx);
+      RowLd<T, EPL>::cvt(vr[u], vx);
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
         if (g >= G) break;
         float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[u][e];
+        for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[e];
         s += __shfl_xor(s, 8, 16);
         s += __shfl_xor(s, 4, 16);
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, true));
@@ -154,7 +185,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
         const float p = exp2f(s - mn);
         l[g] = l[g] * c + p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * c + p * vx[u][e];
+        for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * c + p * vx[e];
         m[g] = mn;
       }
     }
@@ -294,8 +325,8 @@ select_kernel(int32_t* __restrict__ idx, const void* __restrict__ scores, int sc
   const int bh = blockIdx.x, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int k_eff = a.heads[bh].k_eff;
-  SelectScratch ws{reinterpret_cast<uint2*>(sm), 65536 / 8, reinterpret_cast<uint32_t*>(sm + 65536),
-                   reinterpret_cast<int*>(sm + 65536 + 8192)};
+  SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
+                   reinterpret_cast<uint32_t*>(sm + 65536), reinterpret_cast<int*>(sm + 65536 + 8192)};
   int M = 0;
   const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
   const int path = select_range<kSelNT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, 0, a.kcap,

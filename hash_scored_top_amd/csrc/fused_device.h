@@ -63,6 +63,8 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+constexpr int kSelCap = 8192;  // candidates a workgroup selects from in LDS
+
 // Candidate slots of one head seen as one array in index order; entry i lives
 // in the chunk c with offs[c] <= i < offs[c+1].
 __device__ __forceinline__ int chunk_of(const int* offs, int nch, int i) {
@@ -117,113 +119,162 @@ __device__ void block_compact_range(const Src& src, int M, const SelRule& rule, 
   }
 }
 
-// Exact selection over M <= NT * PER (key, index) entries in LDS, stored in
-// index order.  Each thread keeps a contiguous segment of PER keys in
-// registers, so the radix passes and the final compaction need only a few
-// block-wide steps; the compaction is one scan of packed (greater, equal)
-// counts.  Writes the selected indices at output positions [r0, r1).
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+}
+
+// Radix search for the k-th largest (1 <= k <= count) of the keys held PER
+// per thread (entry e of thread t is entry t + e * NT; entries >= count are
+// ignored), 11-bit digits below the common prefix of the keys, at most
+// max_pass passes.  On return an entry with masked key m = key & mask is
+// above the k-th iff m > prefix; when all passes ran, exactly krem of the
+// entries with m == prefix are needed to complete the k largest.  After fewer
+// passes (max_pass reached), prefix (with its unresolved low bits zero) is a
+// lower bound of the k-th largest key.  hist: 2048 words of LDS.
 template <int NT, int PER>
-__device__ void select_lds_segments(const uint2* cand, int M, int k, int r0, int r1, int32_t* out_g,
-                                    int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
-  const int s0 = threadIdx.x * PER;
-  uint32_t key[PER];
+__device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, int max_pass,
+                                  uint32_t* hist, BlockScratch<NT>& sc, uint32_t& mask,
+                                  uint32_t& prefix, int& krem, uint32_t* kmin = nullptr) {
+  const int t = threadIdx.x;
+  mask = 0u;
+  prefix = 0u;
+  krem = k;
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) key[e] = s0 + e < M ? cand[s0 + e].x : 0u;
+  for (int e = 0; e < PER; ++e)
+    if (t + e * NT < count) {
+      mn = min(mn, key[e]);
+      mx = max(mx, key[e]);
+    }
+  block_minmax<NT>(mn, mx, sc);
+  if (kmin != nullptr) *kmin = mn;
+  if (mn == mx) return;  // every key equal: mask 0 selects krem of them
+  const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
+  mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
+  prefix = mn & mask;
+  int lo = hb + 1;
+  for (int pass = 0; lo > 0 && pass < max_pass; ++pass) {
+    const int width = lo < 11 ? lo : 11;
+    const int sh = lo - width;
+    const int nb = 1 << width;
+    for (int i = t; i < nb; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (t + e * NT < count && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
+    __syncthreads();
+    const int per = (nb + NT - 1) / NT;  // bins per thread, from the top digit down
+    int mine = 0;
+    for (int i = 0; i < per; ++i) {
+      const int r = t * per + i;
+      if (r < nb) mine += static_cast<int>(hist[nb - 1 - r]);
+    }
+    int tot;
+    const int above = block_excl_scan<NT>(mine, sc, tot);
+    if (above < krem && krem <= above + mine) {
+      int cum = above;
+      for (int i = 0; i < per; ++i) {
+        const int digit = nb - 1 - (t * per + i);
+        const int c = static_cast<int>(hist[digit]);
+        if (cum + c >= krem) {
+          sc.found[0] = digit;
+          sc.found[1] = krem - cum;
+          sc.found[2] = c;
+          break;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
+    const int digit = sc.found[0];
+    krem = sc.found[1];
+    const int cnt = sc.found[2];
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(digit) << sh;
+    mask |= static_cast<uint32_t>(nb - 1) << sh;
+    lo = sh;
+    if (cnt == krem) break;  // the whole bin is taken
+  }
+}
+
+// Exact selection over M <= NT * PER candidates held in LDS in index order
+// (order keys in candk, key indices in candi).  The radix passes work on the
+// keys held in registers (entry t + e * NT in key[e]); the compaction walks
+// one contiguous range per wave twice: counts first, then the output
+// positions from ballots.  Writes the selected indices at output positions
+// [r0, r1).
+template <int NT, int PER>
+__device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, int k, int r0, int r1,
+                           int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t mask = 0u, prefix = 0u;
   int krem = k >= M ? M : k;
   if (k < M) {
-    uint32_t mn = 0xffffffffu, mx = 0u;
+    uint32_t key[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (s0 + e < M) {
-        mn = min(mn, key[e]);
-        mx = max(mx, key[e]);
-      }
-    block_minmax<NT>(mn, mx, sc);
-    if (mn != mx) {
-      const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
-      mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
-      prefix = mn & mask;
-      int lo = hb + 1;
-      while (lo > 0) {
-        const int width = lo < 11 ? lo : 11;
-        const int sh = lo - width;
-        const int nb = 1 << width;
-        for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          if (s0 + e < M && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
-        __syncthreads();
-        const int per = (nb + NT - 1) / NT;  // bins per thread, from the top digit down
-        int mine = 0;
-        for (int i = 0; i < per; ++i) {
-          const int r = threadIdx.x * per + i;
-          if (r < nb) mine += static_cast<int>(hist[nb - 1 - r]);
-        }
-        int tot;
-        const int above = block_excl_scan<NT>(mine, sc, tot);
-        if (above < krem && krem <= above + mine) {
-          int cum = above;
-          for (int i = 0; i < per; ++i) {
-            const int digit = nb - 1 - (threadIdx.x * per + i);
-            const int c = static_cast<int>(hist[digit]);
-            if (cum + c >= krem) {
-              sc.found[0] = digit;
-              sc.found[1] = krem - cum;
-              sc.found[2] = c;
-              break;
-            }
-            cum += c;
-          }
-        }
-        __syncthreads();
-        const int digit = sc.found[0];
-        krem = sc.found[1];
-        const int cnt = sc.found[2];
-        __syncthreads();
-        prefix |= static_cast<uint32_t>(digit) << sh;
-        mask |= static_cast<uint32_t>(nb - 1) << sh;
-        lo = sh;
-        if (cnt == krem) break;  // the whole bin is taken
-      }
-    }
+    for (int e = 0; e < PER; ++e) key[e] = t + e * NT < M ? candk[t + e * NT] : 0u;
+    radix_select_regs<NT, PER>(key, M, k, 32, hist, sc, mask, prefix, krem);
   }
+  // compaction: wave w owns entries [lo, hi) in index order
+  const int span = (M + NW - 1) / NW;
+  const int lo = min(M, wave * span), hi = min(M, lo + span);
   int gtc = 0, eqc = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (s0 + e < M) {
-      const uint32_t m = key[e] & mask;
-      gtc += m > prefix;
-      eqc += m == prefix;
+  for (int i0 = lo; i0 < hi; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t m = i < hi ? (candk[i] & mask) : 0u;
+    gtc += __popcll(__ballot(i < hi && m > prefix));
+    eqc += __popcll(__ballot(i < hi && m == prefix));
+  }
+  if (lane == 0) {
+    sc.red[0][wave] = static_cast<uint32_t>(gtc);
+    sc.red[1][wave] = static_cast<uint32_t>(eqc);
+  }
+  __syncthreads();
+  int gt_before = 0, eq_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += static_cast<int>(sc.red[0][w]);
+    eq_run += static_cast<int>(sc.red[1][w]);
+  }
+  __syncthreads();  // sc.red is reused by the caller
+  int sel_run = gt_before + min(eq_run, krem);
+  for (int i0 = lo; i0 < hi && sel_run < r1; i0 += 64) {  // wave-uniform loop
+    const int i = i0 + lane;
+    const uint32_t m = i < hi ? (candk[i] & mask) : 0u;
+    const bool gt = i < hi && m > prefix;
+    const bool eq = i < hi && m == prefix;
+    const unsigned long long eqb = __ballot(eq);
+    const bool sel = gt || (eq && eq_run + lanes_below(eqb) < krem);
+    const unsigned long long selb = __ballot(sel);
+    const int pos = sel_run + lanes_below(selb);
+    if (sel && pos >= r0 && pos < r1) {
+      const int32_t v = candi[i];
+      if (out_g != nullptr) out_g[pos] = v;
+      if (out_l != nullptr) out_l[pos - r0] = v;
     }
-  int tot;
-  const int ex = block_excl_scan<NT>(gtc | (eqc << 16), sc, tot);
-  const int eq_before = ex >> 16;
-  int pos = (ex & 0xffff) + min(eq_before, krem);
-  int eq_seen = eq_before;
-#pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (s0 + e < M) {
-      const uint32_t m = key[e] & mask;
-      bool sel = m > prefix;
-      if (m == prefix) sel = eq_seen++ < krem;
-      if (sel) {
-        if (pos >= r0 && pos < r1) {
-          const int32_t v = static_cast<int32_t>(cand[s0 + e].y);
-          if (out_g != nullptr) out_g[pos] = v;
-          if (out_l != nullptr) out_l[pos - r0] = v;
-        }
-        ++pos;
-      }
-    }
+    sel_run += __popcll(selb);
+    eq_run += __popcll(eqb);
+  }
+}
+
+// Lower bound of the r-th largest (1 <= r <= count) of the keys held PER per
+// thread: two 11-bit radix passes below the common prefix of the keys, then
+// the low edge of the bin holding rank r (the common key if all are equal).
+template <int NT, int PER>
+__device__ uint32_t rank_lower_bound_regs(const uint32_t (&key)[PER], int count, int r, uint32_t* hist,
+                                          BlockScratch<NT>& sc) {
+  uint32_t mask, prefix, kmin;
+  int krem;
+  radix_select_regs<NT, PER>(key, count, r, 2, hist, sc, mask, prefix, krem, &kmin);
+  return mask == 0u ? kmin : prefix;
 }
 
 struct SelectScratch {
-  uint2* cand;     // LDS, cap entries
-  int cap;
-  uint32_t* hist;  // LDS, 2048 words
-  int* offs;       // LDS, nchunks + 1
+  uint32_t* candk;  // LDS, kSelCap entries
+  int32_t* candi;   // LDS, kSelCap entries
+  uint32_t* hist;   // LDS, 2048 words
+  int* offs;        // LDS, nchunks + 1
 };
 
 // The head's exact top-k (k_eff keys, ties to the lower index) from the
@@ -255,25 +306,41 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
   *cand_total = M;
   int path = 0;
   if (k_eff > 0) {
-    if (M >= k_eff && M <= ws.cap) {
-      for (int i0 = 0; i0 < M; i0 += NT * 8) {  // eight independent loads in flight
-        uint2 v[8];
+    if (M >= k_eff && M <= kSelCap) {
+      // each wave copies whole chunks (coalesced): eight chunks and sixteen
+      // loads per lane in flight
+      constexpr int NW = NT / 64;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      for (int c0 = wave; c0 < nch; c0 += NW * 8) {
+        uint2 v[8][2];
+        int cnt[8], base[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
-          if (i < M) {
-            const int c = chunk_of(ws.offs, nch, i);
-            v[u] = slots[static_cast<long long>(c) * chunk + (i - ws.offs[c])];
-          }
+          const int c = c0 + u * NW;
+          cnt[u] = c < nch ? ws.offs[c + 1] - ws.offs[c] : 0;
+          base[u] = c < nch ? ws.offs[c] : 0;
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            if (lane + 64 * x < cnt[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
-          if (i < M) ws.cand[i] = v[u];
+#pragma unroll
+          for (int x = 0; x < 2; ++x)
+            if (lane + 64 * x < cnt[u]) {
+              ws.candk[base[u] + lane + 64 * x] = v[u][x].x;
+              ws.candi[base[u] + lane + 64 * x] = static_cast<int32_t>(v[u][x].y);
+            }
+          const long long c = c0 + u * NW;
+          for (int i = 128 + lane; i < cnt[u]; i += 64) {  // chunks with many candidates
+            const uint2 w = slots[c * chunk + i];
+            ws.candk[base[u] + i] = w.x;
+            ws.candi[base[u] + i] = static_cast<int32_t>(w.y);
+          }
         }
       }
       __syncthreads();
-      select_lds_segments<NT, (8192 + NT - 1) / NT>(ws.cand, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
+      select_lds<NT, kSelCap / NT>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
     } else if (M >= k_eff) {
       path = 1;
       const SlotSrc src{slots, ws.offs, nch, chunk};

@@ -12,33 +12,39 @@ namespace hst {
 constexpr int kSample = 2048;      // keys sampled per head for the candidate threshold
 constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
 constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
+constexpr int kPrepBlocks = 8;     // prep workgroups per head (at least): each gathers 1/8 of the sample
 
 enum ScanKind { kScanSoftFast = 0, kScanSoftAny = 1, kScanHamming = 2, kScanGivenF32 = 3, kScanGivenI32 = 4 };
 
-// Per (sequence, kv head) state in the workspace header, written by prep.
+// Per (sequence, kv head) state in the workspace header.
 struct HeadState {
   uint32_t theta;       // candidate threshold (order key)
   int32_t k_eff;        // keys to select
   int32_t n;            // context length
   uint32_t cand_total;  // candidates the scan found (diagnostic)
   uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every score (diagnostic)
-  uint32_t pad[11];
+  uint32_t pad0;
+  uint64_t thr_word;    // (1 << 32) | theta once published within the scan, else 0
+  uint32_t pad[8];
 };
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_heads, off_tables, off_qcodes, off_scores, off_counts, off_slots, off_part_o,
-      off_part_ml, bytes;
-  int chunk, nchunks, sample, rps, nsplit, kind;
+  size_t off_ctrl, off_heads, off_tables, off_qcodes, off_samp, off_samp_vn, off_scores, off_counts,
+      off_slots, off_part_o, off_part_ml, bytes;
+  int chunk, nchunks, sample, srow, rps, nsplit, kind;
 };
 
 struct FusedArgs {
   int Hq, Hkv, d, Nmax, L, P;
   double inv_tau;
-  int kcap, sample, nchunks, rps, nsplit, region_bytes;
+  int kcap, sample, srow, nchunks, rps, nsplit, region_bytes;
+  uint32_t* ticket;  // workgroup ticket counter of a filtering scan (zeroed by prep)
   HeadState* heads;
   float* tables;     // [B*Hkv][2^P][L] bucket-major
   uint32_t* qcodes;  // [B*Hkv][G][4]
+  uint8_t* samp;     // [B*Hkv][kSample][srow]: sampled key metadata (ids / code / score key)
+  float* samp_vn;    // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
   uint32_t* counts;  // [B*Hkv][nchunks]
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index)
   float* part_o;     // [B*Hq][nsplit][d]
@@ -58,8 +64,12 @@ hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const voi
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
                              const void* scores, const int32_t* kps, hipStream_t st);
 int scan_chunk(int L);
+// filter != 0: the scan also derives each head's candidate threshold from the
+// gathered sample (prep with sampling must precede it) and fills the
+// candidate slots
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a, int kind, const void* src,
-                       const void* vnorm, int norm_f16, void* scores_out, int filter, hipStream_t st);
+                       const void* vnorm, int norm_f16, void* scores_out, int filter,
+                       const int32_t* kps, hipStream_t st);
 hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
                          const void* V, int32_t* idx, bool select, const void* scores, int scores_int,
                          int chunk, float scale, float* out, float* lse, hipStream_t st);

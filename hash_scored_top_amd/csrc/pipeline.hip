@@ -2,8 +2,11 @@
 // sequence of every C-ABI operation.
 //
 //   decode step (soft-LSH or binary codes):
-//     prep  (one workgroup per kv head: query tables / codes, sample threshold)
-//     scan  (score every key once; candidates >= threshold into chunk slots)
+//     prep  (several workgroups per kv head: query tables / codes, and the
+//            key sample copied to a compact buffer)
+//     scan  (score every key once; one extra workgroup per kv head derives
+//            the candidate threshold from the sample meanwhile; keys scoring
+//            >= threshold go to the chunk candidate slots)
 //     attend (each split derives the exact top-k from the candidates and
 //             attends over its part of the selected rows)
 //     combine (merge the splits through their log-sum-exp)
@@ -31,9 +34,15 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
     o += (bytes + 255) / 256 * 256;
     return r;
   };
-  f.off_heads = take(BH * sizeof(HeadState));
+  f.off_heads = take(BH * sizeof(HeadState));  // first: the head states start the workspace
+  f.off_ctrl = take(256);
   if (soft) f.off_tables = take(BH * (static_cast<size_t>(L) << P) * sizeof(float));
   if (ham) f.off_qcodes = take(static_cast<size_t>(s.B) * s.Hq * 16);
+  if (select) {
+    f.srow = soft ? L : (ham ? 16 : 4);
+    f.off_samp = take(BH * static_cast<size_t>(kSample) * f.srow);
+    if (soft) f.off_samp_vn = take(BH * static_cast<size_t>(kSample) * 4);
+  }
   if (decode) f.off_scores = take(BH * static_cast<size_t>(s.Nmax) * 4);
   if (select) {
     f.off_counts = take(BH * f.nchunks * 4);
@@ -41,7 +50,7 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
   }
   if (attn) {
     const long long rows = static_cast<long long>(kcap) * BH;
-    long long r = (rows + 511) / 512;  // about two splits per CU
+    long long r = (rows + 255) / 256;  // about one split per CU
     r = (r + 63) / 64 * 64;
     if (r < 64) r = 64;
     if (r > 1024) r = 1024;
@@ -71,12 +80,16 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   a.nchunks = f.nchunks;
   a.rps = f.rps;
   a.nsplit = f.nsplit;
+  a.srow = f.srow;
   a.region_bytes = 65536;
   char* p = static_cast<char*>(ws);
   if (p != nullptr) {
+    a.ticket = reinterpret_cast<uint32_t*>(p + f.off_ctrl);
     a.heads = reinterpret_cast<HeadState*>(p + f.off_heads);
     a.tables = reinterpret_cast<float*>(p + f.off_tables);
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
+    a.samp = reinterpret_cast<uint8_t*>(p + f.off_samp);
+    a.samp_vn = reinterpret_cast<float*>(p + f.off_samp_vn);
     a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
     a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
     a.part_o = reinterpret_cast<float*>(p + f.off_part_o);
@@ -101,7 +114,7 @@ hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K
   const int f16 = norm_dtype == HST_F16;
   float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + f.off_scores);
   HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
-  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, st));
+  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, kps, st));
   return launch_attend(s, a, q, K, V, idx, true, scores, 0, f.chunk, scale, out, lse, st);
 }
 
@@ -113,7 +126,7 @@ hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K
   const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
   int32_t* scores = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + f.off_scores);
   HST_CHECK(launch_prep_hamming(s, a, q, R, codes, kps, st));
-  HST_CHECK(launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 1, st));
+  HST_CHECK(launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 1, kps, st));
   return launch_attend(s, a, q, K, V, idx, true, scores, 1, f.chunk, scale, out, lse, st);
 }
 
@@ -123,7 +136,7 @@ hipError_t fused_score_softlsh(const hst_shape& s, const void* q, const void* W,
   const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   const FusedArgs a = make_args(s, f, ws, L, P, tau, 1);
   HST_CHECK(launch_prep_soft(s, a, q, W, nullptr, nullptr, 0, nullptr, st));
-  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, st);
+  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, nullptr, st);
 }
 
 hipError_t fused_score_hamming(const hst_shape& s, const void* q, const void* R,
@@ -131,7 +144,7 @@ hipError_t fused_score_hamming(const hst_shape& s, const void* q, const void* R,
   const FusedLayout f = fused_layout(s, HST_OP_SCORE_HAMMING, 0, 0, 1);
   const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, 1);
   HST_CHECK(launch_prep_hamming(s, a, q, R, codes, nullptr, st));
-  return launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 0, st);
+  return launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 0, nullptr, st);
 }
 
 hipError_t fused_tables_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
@@ -148,7 +161,7 @@ hipError_t fused_scan_softlsh(const hst_shape& s, const float* tables, int L, in
   const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   FusedArgs a = make_args(s, f, nullptr, L, P, 0.0, 1);
   a.tables = const_cast<float*>(tables);
-  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, st);
+  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, nullptr, st);
 }
 
 hipError_t fused_select(const hst_shape& s, int score_dtype, const void* scores, int kcap,
@@ -157,7 +170,7 @@ hipError_t fused_select(const hst_shape& s, int score_dtype, const void* scores,
   const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
   const int is_int = score_dtype == HST_I32;
   HST_CHECK(launch_prep_given(s, a, score_dtype, scores, kps, st));
-  HST_CHECK(launch_scan(s, a, is_int ? kScanGivenI32 : kScanGivenF32, scores, nullptr, 0, nullptr, 1, st));
+  HST_CHECK(launch_scan(s, a, is_int ? kScanGivenI32 : kScanGivenF32, scores, nullptr, 0, nullptr, 1, kps, st));
   return launch_select_only(s, a, idx, scores, is_int, f.chunk, st);
 }
 

@@ -9,6 +9,17 @@
 //  * Code similarity (HATA explainer page, section 3): XOR + popcount of
 //    128-bit codes against the G query codes.
 //  * Given scores (the stand-alone top-k): the scores are only filtered.
+//
+// When filtering, B*Hkv extra workgroups derive the heads' candidate
+// thresholds from the key sample prep gathered, while the others stream their
+// chunks; a chunk workgroup waits for its head's threshold only before its
+// epilogue.  Roles come from a ticket taken when a workgroup starts, and the
+// first B*Hkv tickets are the threshold workgroups: every workgroup that
+// waits therefore waits for one that is already running and never waits
+// itself.  The threshold is handed over in one 64-bit atomic word (flag and
+// value), so no other memory needs ordering; a wait that exceeds its bound
+// falls back to threshold 0 (every key a candidate), which leaves the
+// selection exact.
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -17,7 +28,10 @@ namespace hst {
 constexpr int kScanNT = 1024;
 constexpr int kSoftChunk = 2048;
 constexpr int kLaneChunk = 4096;
-static_assert(kSoftChunk >= 2048 && kLaneChunk >= 2048, "chunk tile doubles as the select histogram");
+static_assert(kSoftChunk >= kSample && kLaneChunk >= kSample && kSample >= 2048,
+              "chunk tile holds the sample scores and doubles as the select histogram");
+constexpr int kThetaSpin = 1 << 16;
+constexpr int kScanSoftU = 2;  // key batches per lane group in flight (two workgroups fit a CU)  // polls of the threshold word before falling back
 
 template <int LANES, int NT, int U>
 struct SoftScorer {
@@ -29,14 +43,11 @@ struct SoftScorer {
   int norm_f16;
   const float* tbl;  // LDS
   uint32_t idmask;   // 2^P - 1: ids outside the table cannot leave it
-  int sub, grp, lofs[16];
+  int sub, grp;
 
   __device__ __forceinline__ void setup() {
     sub = threadIdx.x % LANES;
     grp = threadIdx.x / LANES;
-    const int k = grp & 15;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lofs[i] = (sub * 16 + ((i + k) & 15)) * 4;
   }
   __device__ __forceinline__ void load(uint4 (&w)[U], float (&nr)[U], long long base, int jb,
                                        int jend) const {
@@ -75,8 +86,9 @@ struct SoftScorer {
         for (int i = 0; i < 16; i += 2) {
           const uint32_t id0 = (c[i >> 2] >> ((i & 3) * 8)) & idmask;
           const uint32_t id1 = (c[(i + 1) >> 2] >> (((i + 1) & 3) * 8)) & idmask;
-          acc0 += *reinterpret_cast<const float*>(tb + id0 * (L * 4) + lofs[i]);
-          acc1 += *reinterpret_cast<const float*>(tb + id1 * (L * 4) + lofs[i + 1]);
+          const int l0 = sub * 16 + ((i + k) & 15), l1 = sub * 16 + ((i + 1 + k) & 15);
+          acc0 += *reinterpret_cast<const float*>(tb + (id0 * L + l0) * 4);
+          acc1 += *reinterpret_cast<const float*>(tb + (id1 * L + l1) * 4);
         }
         const float sv = group_sum<LANES>(acc0 + acc1) * nr[u];
         if (sub == 0) out[j - j0] = sv;
@@ -84,6 +96,29 @@ struct SoftScorer {
     }
   }
 };
+
+// Scores of keys [j0, jend) (rows base + j) into out[j - j0]; (w, nr) hold the
+// first batch, already loaded.  The next batch is in flight during each
+// batch's table lookups.
+template <class S, int U>
+__device__ __forceinline__ void soft_score_range(const S& sco, long long base, int j0, int jend,
+                                                 uint4 (&w)[U], float (&nr)[U], float* out) {
+  uint4 wn[U];
+  float nn[U];
+  for (int t0 = j0; t0 < jend; t0 += S::TILE) {
+    const int jb = t0 + sco.grp;
+    const bool more = t0 + S::TILE < jend;
+    if (more) sco.load(wn, nn, base, jb + S::TILE, jend);
+    sco.compute(w, nr, jb, jend, j0, out);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        w[u] = wn[u];
+        nr[u] = nn[u];
+      }
+    }
+  }
+}
 
 // The chunk's scores sit in LDS (tile[0..cnt)): write them out (coalesced)
 // and append the keys scoring >= theta, in index order, to the chunk's
@@ -123,23 +158,154 @@ __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt
   return tot;
 }
 
-// Soft-LSH scan, L a multiple of 16.  grid (nchunks, B*Hkv).
+
+// Work of a scan workgroup: a chunk of one head, or (filtering) the
+// threshold of one head.
+struct ScanWork {
+  int bh, chunk;
+  bool theta;
+};
+__device__ __forceinline__ ScanWork scan_work(const FusedArgs& a, bool filt, int BH, int nch, int* s_lid) {
+  int lid = blockIdx.x;
+  if (filt) {
+    if (threadIdx.x == 0) *s_lid = static_cast<int>(atomicAdd(a.ticket, 1u));
+    __syncthreads();
+    lid = *s_lid;
+  }
+  ScanWork w;
+  w.theta = filt && lid < BH;
+  const int x = w.theta ? 0 : (filt ? lid - BH : lid);
+  w.bh = w.theta ? lid : x / nch;
+  w.chunk = w.theta ? 0 : x % nch;
+  return w;
+}
+
+// Candidate threshold of head bh from the sample prep gathered; every thread
+// of the workgroup calls.  LDS: the head's table (soft-LSH, as the scan holds
+// it), the query codes (binary codes), kSample words of scratch in tile.
+template <int KIND, int LANES>
+__device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, const float* tbl,
+                                 const uint32_t* qc, uint32_t* tile, BlockScratch<kScanNT>& sc) {
+  constexpr int NT = kScanNT;
+  constexpr int PER = kSample / NT;
+  const int S = a.sample > n ? n : a.sample;
+  const int r = sample_rank(k_eff, n, S);
+  if (!(S > 0 && k_eff > 0 && r < S)) return 0u;
+  const int t = threadIdx.x;
+  const long long sb = static_cast<long long>(bh) * kSample;
+  uint32_t key[PER];
+  if (KIND == kScanSoftFast) {
+    constexpr int U = kScanSoftU;
+    SoftScorer<LANES, NT, U> ss;
+    ss.idv = reinterpret_cast<const uint4*>(a.samp);
+    ss.vnorm = a.samp_vn;
+    ss.norm_f16 = 0;
+    ss.tbl = tbl;
+    ss.idmask = (1u << a.P) - 1u;
+    ss.setup();
+    uint4 w[U];
+    float nr[U];
+    ss.load(w, nr, sb, ss.grp, S);
+    soft_score_range(ss, sb, 0, S, w, nr, reinterpret_cast<float*>(tile));
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = t + e * NT;
+      key[e] = i < S ? order_key_f32(__uint_as_float(tile[i])) : 0u;
+    }
+  } else if (KIND == kScanSoftAny) {
+    const uint32_t idm = (1u << a.P) - 1u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = t + e * NT;
+      float sv = 0.f;
+      if (i < S) {
+        const uint8_t* row = a.samp + (sb + i) * a.L;
+        for (int l = 0; l < a.L; ++l) sv += tbl[(row[l] & idm) * a.L + l];
+        sv *= a.samp_vn[sb + i];
+      }
+      key[e] = order_key_f32(sv);
+    }
+  } else if (KIND == kScanHamming) {
+    const int G = a.Hq / a.Hkv;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = t + e * NT;
+      int ham = 0;
+      if (i < S) {
+        const u32x4 cv = reinterpret_cast<const u32x4*>(a.samp)[sb + i];
+        for (int g = 0; g < G; ++g)
+          ham += __popc(cv.x ^ qc[4 * g]) + __popc(cv.y ^ qc[4 * g + 1]) +
+                 __popc(cv.z ^ qc[4 * g + 2]) + __popc(cv.w ^ qc[4 * g + 3]);
+      }
+      key[e] = order_key_i32(128 * G - ham);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = t + e * NT;
+      key[e] = i < S ? reinterpret_cast<const uint32_t*>(a.samp)[sb + i] : 0u;
+    }
+  }
+  __syncthreads();  // tile becomes the histogram
+  return rank_lower_bound_regs<NT, PER>(key, S, r, tile, sc);
+}
+
+// Threshold workgroup: derive and publish head bh's threshold and state.
+template <int KIND, int LANES>
+__device__ void theta_publish(const FusedArgs& a, int bh, const int32_t* seq_lens, const int32_t* k_per_seq,
+                              const float* tbl, const uint32_t* qc, uint32_t* tile,
+                              BlockScratch<kScanNT>& sc) {
+  const int b = bh / a.Hkv;
+  const int n = seq_len(seq_lens, b, a.Nmax);
+  const int k_eff = keff_of(a.kcap, k_per_seq, b, n);
+  const uint32_t theta = sample_theta<KIND, LANES>(a, bh, n, k_eff, tbl, qc, tile, sc);
+  if (threadIdx.x == 0) {
+    HeadState* hs = a.heads + bh;
+    hs->theta = theta;
+    hs->k_eff = k_eff;
+    hs->n = n;
+    __hip_atomic_store(&hs->thr_word, (1ull << 32) | theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Chunk workgroup: the head's threshold, once published (see above).
+__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, uint32_t* s_theta) {
+  if (threadIdx.x == 0) {
+    uint64_t v = 0;
+    for (int i = 0; i < kThetaSpin; ++i) {
+      v = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v >> 32) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    *s_theta = (v >> 32) ? static_cast<uint32_t>(v) : 0u;
+  }
+  __syncthreads();
+  return *s_theta;
+}
+
+// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]).
 template <int LANES, int U>
-__global__ void __launch_bounds__(kScanNT)
+__global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
 scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm, int norm_f16,
-                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores_out,
-                    int filter, FusedArgs a) {
+                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
+                    float* __restrict__ scores_out, int filter, int nch, FusedArgs a) {
   constexpr int NT = kScanNT;
   using S = SoftScorer<LANES, NT, U>;
   constexpr int CH = kSoftChunk;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
+  __shared__ int s_lid;
+  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
-  const int bh = blockIdx.y, b = bh / a.Hkv;
+  const bool filt = filter != 0;
+  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
+  const ScanWork wk = scan_work(a, filt, BH, nch, &s_lid);
+  const int bh = wk.bh, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = blockIdx.x * CH;
-  if (j0 >= n) return;
+  const int j0 = wk.chunk * CH;
+  if (!wk.theta && j0 >= n) return;
   const int jend = min(j0 + CH, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   S sco;
@@ -149,57 +315,54 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   sco.tbl = tbl;
   sco.idmask = (1u << a.P) - 1u;
   sco.setup();
-  uint4 w[U], wn[U];
-  float nr[U], nn[U];
-  sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
+  uint4 w[U];
+  float nr[U];
+  if (!wk.theta) sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
   {
     const int nflt = S::L << a.P;
     const float4* src = reinterpret_cast<const float4*>(a.tables + static_cast<long long>(bh) * nflt);
     for (int i = threadIdx.x; i < nflt / 4; i += NT) reinterpret_cast<float4*>(tbl)[i] = src[i];
   }
-  const bool filt = filter != 0;
-  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
-  for (int t0 = j0; t0 < jend; t0 += S::TILE) {
-    const int jb = t0 + sco.grp;
-    const bool more = t0 + S::TILE < jend;
-    if (more) sco.load(wn, nn, base, jb + S::TILE, jend);
-    sco.compute(w, nr, jb, jend, j0, tile);
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        w[u] = wn[u];
-        nr[u] = nn[u];
-      }
-    }
+  if (wk.theta) {
+    theta_publish<kScanSoftFast, LANES>(a, bh, seq_lens, k_per_seq, tbl, nullptr,
+                                        reinterpret_cast<uint32_t*>(tile), sc);
+    return;
   }
+  soft_score_range(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(blockIdx.x) * CH;
+  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
+  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(wk.chunk) * CH;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
                                                    slot, sc);
-  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + blockIdx.x] = count;
+  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + wk.chunk] = count;
 }
 
 // One-lane-per-key scans: soft-LSH with any L, binary codes, given scores.
 template <int KIND>
 __global__ void __launch_bounds__(kScanNT)
 scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, int norm_f16,
-                 const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ scores_out,
-                 int filter, FusedArgs a) {
+                 const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
+                 uint32_t* __restrict__ scores_out, int filter, int nch, FusedArgs a) {
   constexpr int NT = kScanNT;
   constexpr bool KINT = KIND == kScanHamming || KIND == kScanGivenI32;
   constexpr int CH = kLaneChunk;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
   __shared__ uint32_t qc[64 * 4];
+  __shared__ int s_lid;
+  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);
   uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);
-  const int bh = blockIdx.y, b = bh / a.Hkv;
+  const bool filt = filter != 0;
+  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
+  const ScanWork wk = scan_work(a, filt, BH, nch, &s_lid);
+  const int bh = wk.bh, b = bh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = blockIdx.x * CH;
-  if (j0 >= n) return;
+  const int j0 = wk.chunk * CH;
+  if (!wk.theta && j0 >= n) return;
   const int jend = min(j0 + CH, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   if (KIND == kScanSoftAny) {
@@ -209,9 +372,11 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   }
   if (KIND == kScanHamming)
     for (int i = threadIdx.x; i < G * 4; i += NT) qc[i] = a.qcodes[static_cast<long long>(bh) * G * 4 + i];
-  const bool filt = filter != 0;
-  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
+  if (wk.theta) {
+    theta_publish<KIND == kScanGivenI32 ? kScanGivenF32 : KIND, 1>(a, bh, seq_lens, k_per_seq, tbl, qc, tile, sc);
+    return;
+  }
   if (KIND == kScanSoftAny) {
     const uint32_t idmask = (1u << a.P) - 1u;
     for (int j = j0 + static_cast<int>(threadIdx.x); j < jend; j += NT) {
@@ -252,10 +417,11 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
     }
   }
   __syncthreads();
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(blockIdx.x) * CH;
+  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
+  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(wk.chunk) * CH;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
                                                   slot, sc);
-  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + blockIdx.x] = count;
+  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + wk.chunk] = count;
 }
 
 int scan_chunk(int L) {
@@ -266,58 +432,65 @@ size_t scan_smem(int region, int chunk) { return static_cast<size_t>(region) + s
 
 template <int LANES>
 static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_t* ids,
-                                     const void* vnorm, int f16, const int32_t* sl, float* sout,
-                                     int filter, hipStream_t st) {
-  constexpr int U = 2;
+                                     const void* vnorm, int f16, const int32_t* sl, const int32_t* kps,
+                                     float* sout, int filter, int nch, hipStream_t st) {
+  constexpr int U = kScanSoftU;
   const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
   auto kern = scan_softlsh_kernel<LANES, U>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, sout, filter, a);
+  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, kps, sout, filter, nch, a);
   return hipGetLastError();
 }
 
 template <int KIND>
 static hipError_t launch_scan_lane_t(dim3 grid, const FusedArgs& a, const void* src, const void* vnorm,
-                                     int f16, const int32_t* sl, void* sout, int filter, hipStream_t st) {
+                                     int f16, const int32_t* sl, const int32_t* kps, void* sout,
+                                     int filter, int nch, hipStream_t st) {
   const size_t smem = scan_smem(a.region_bytes, kLaneChunk);
   auto kern = scan_lane_kernel<KIND>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, src, vnorm, f16, sl,
-                     static_cast<uint32_t*>(sout), filter, a);
+  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, src, vnorm, f16, sl, kps,
+                     static_cast<uint32_t*>(sout), filter, nch, a);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, const void* src,
-                       const void* vnorm, int norm_f16, void* scores_out, int filter, hipStream_t st) {
+                       const void* vnorm, int norm_f16, void* scores_out, int filter,
+                       const int32_t* kps, hipStream_t st) {
   const int chunk = kind == kScanSoftFast ? kSoftChunk : kLaneChunk;
   // LDS ahead of the chunk tile: the kv head's table (soft-LSH) or nothing
   FusedArgs a = a_in;
   a.region_bytes = (kind == kScanSoftFast || kind == kScanSoftAny)
                        ? static_cast<int>(hst_align16(static_cast<size_t>(a.L << a.P) * 4))
                        : 0;
-  dim3 grid((s.Nmax + chunk - 1) / chunk, s.B * s.Hkv);
+  const int nch = static_cast<int>((s.Nmax + chunk - 1) / chunk);
+  const long long BH = static_cast<long long>(s.B) * s.Hkv;
+  const long long nblk = BH * nch + (filter ? BH : 0);
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(nblk));
   const uint8_t* ids = static_cast<const uint8_t*>(src);
   float* sout = static_cast<float*>(scores_out);
+  const int32_t* sl = s.seq_lens;
   switch (kind) {
     case kScanSoftFast:
       switch (a.L) {
-        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, s.seq_lens, sout, filter, st);
-        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, s.seq_lens, sout, filter, st);
-        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, s.seq_lens, sout, filter, st);
-        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, s.seq_lens, sout, filter, st);
+        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
       }
     case kScanSoftAny:
-      return launch_scan_lane_t<kScanSoftAny>(grid, a, src, vnorm, norm_f16, s.seq_lens, scores_out, filter, st);
+      return launch_scan_lane_t<kScanSoftAny>(grid, a, src, vnorm, norm_f16, sl, kps, scores_out, filter, nch, st);
     case kScanHamming:
-      return launch_scan_lane_t<kScanHamming>(grid, a, src, nullptr, 0, s.seq_lens, scores_out, filter, st);
+      return launch_scan_lane_t<kScanHamming>(grid, a, src, nullptr, 0, sl, kps, scores_out, filter, nch, st);
     case kScanGivenF32:
-      return launch_scan_lane_t<kScanGivenF32>(grid, a, src, nullptr, 0, s.seq_lens, nullptr, filter, st);
+      return launch_scan_lane_t<kScanGivenF32>(grid, a, src, nullptr, 0, sl, kps, nullptr, filter, nch, st);
     default:
-      return launch_scan_lane_t<kScanGivenI32>(grid, a, src, nullptr, 0, s.seq_lens, nullptr, filter, st);
+      return launch_scan_lane_t<kScanGivenI32>(grid, a, src, nullptr, 0, sl, kps, nullptr, filter, nch, st);
   }
 }
 
