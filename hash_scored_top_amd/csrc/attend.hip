@@ -337,6 +337,21 @@ select_kernel(int32_t* __restrict__ idx, const void* __restrict__ scores, int sc
   }
 }
 
+// Raises a kernel's dynamic LDS limit once per device (the largest size
+// requested so far).
+template <typename K>
+static hipError_t lds_limit(K kern, size_t bytes) {
+  static size_t done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(bytes));
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
+  return e;
+}
+
 template <typename T, int D, bool SELECT>
 static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
                                   const void* V, int32_t* idx, const void* scores, int scores_int,
@@ -347,9 +362,7 @@ static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const 
 #define HST_ATT(GM)                                                                             \
   do {                                                                                          \
     auto kern = attend_kernel<T, D, GM, SELECT>;                                                \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),                     \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,              \
-                                       static_cast<int>(smem));                                 \
+    hipError_t e = lds_limit(kern, smem);                                                       \
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL(kern, grid, dim3(kAttNT), smem, st, static_cast<const T*>(q),            \
                        static_cast<const T*>(K), static_cast<const T*>(V), idx, scores,         \
@@ -403,8 +416,7 @@ hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, 
 hipError_t launch_select_only(const hst_shape& s, const FusedArgs& a, int32_t* idx, const void* scores,
                               int scores_int, int chunk, hipStream_t st) {
   const size_t smem = 65536 + 8192 + static_cast<size_t>(a.nchunks + 1) * 4;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  hipError_t e = lds_limit(select_kernel, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3(s.B * s.Hkv), dim3(kSelNT), smem, st, idx, scores, scores_int,
                      chunk, s.seq_lens, a);

@@ -164,33 +164,50 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
     for (int e = 0; e < PER; ++e)
       if (t + e * NT < count && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & (nb - 1)], 1u);
     __syncthreads();
-    const int per = (nb + NT - 1) / NT;  // bins per thread, from the top digit down
+    // thread t owns bins [t*per, t*per + per) counted from the top digit down;
+    // wave-level inclusive scan, then every thread adds the totals of the
+    // waves before its own
+    constexpr int NW = NT / 64;
+    constexpr int MAXPER = (2048 + NT - 1) / NT;
+    const int per = (nb + NT - 1) / NT;
+    int c[MAXPER];
     int mine = 0;
-    for (int i = 0; i < per; ++i) {
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
       const int r = t * per + i;
-      if (r < nb) mine += static_cast<int>(hist[nb - 1 - r]);
+      c[i] = (i < per && r < nb) ? static_cast<int>(hist[nb - 1 - r]) : 0;
+      mine += c[i];
     }
-    int tot;
-    const int above = block_excl_scan<NT>(mine, sc, tot);
+    const int lane = t & 63, w = t >> 6;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) sc.wsum[w] = incl;
+    __syncthreads();
+    int above = incl - mine;
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (i < w) above += sc.wsum[i];
     if (above < krem && krem <= above + mine) {
       int cum = above;
-      for (int i = 0; i < per; ++i) {
-        const int digit = nb - 1 - (t * per + i);
-        const int c = static_cast<int>(hist[digit]);
-        if (cum + c >= krem) {
-          sc.found[0] = digit;
+#pragma unroll
+      for (int i = 0; i < MAXPER; ++i) {
+        if (i < per && cum + c[i] >= krem) {
+          sc.found[0] = nb - 1 - (t * per + i);
           sc.found[1] = krem - cum;
-          sc.found[2] = c;
+          sc.found[2] = c[i];
           break;
         }
-        cum += c;
+        cum += c[i];
       }
     }
     __syncthreads();
     const int digit = sc.found[0];
     krem = sc.found[1];
     const int cnt = sc.found[2];
-    __syncthreads();
     prefix |= static_cast<uint32_t>(digit) << sh;
     mask |= static_cast<uint32_t>(nb - 1) << sh;
     lo = sh;
@@ -221,11 +238,19 @@ __device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, i
   const int span = (M + NW - 1) / NW;
   const int lo = min(M, wave * span), hi = min(M, lo + span);
   int gtc = 0, eqc = 0;
-  for (int i0 = lo; i0 < hi; i0 += 64) {
-    const int i = i0 + lane;
-    const uint32_t m = i < hi ? (candk[i] & mask) : 0u;
-    gtc += __popcll(__ballot(i < hi && m > prefix));
-    eqc += __popcll(__ballot(i < hi && m == prefix));
+  for (int i0 = lo; i0 < hi; i0 += 256) {  // four reads per lane in flight
+    uint32_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      m[u] = i < hi ? (candk[i] & mask) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      gtc += __popcll(__ballot(i < hi && m[u] > prefix));
+      eqc += __popcll(__ballot(i < hi && m[u] == prefix));
+    }
   }
   if (lane == 0) {
     sc.red[0][wave] = static_cast<uint32_t>(gtc);
@@ -239,22 +264,30 @@ __device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, i
   }
   __syncthreads();  // sc.red is reused by the caller
   int sel_run = gt_before + min(eq_run, krem);
-  for (int i0 = lo; i0 < hi && sel_run < r1; i0 += 64) {  // wave-uniform loop
-    const int i = i0 + lane;
-    const uint32_t m = i < hi ? (candk[i] & mask) : 0u;
-    const bool gt = i < hi && m > prefix;
-    const bool eq = i < hi && m == prefix;
-    const unsigned long long eqb = __ballot(eq);
-    const bool sel = gt || (eq && eq_run + lanes_below(eqb) < krem);
-    const unsigned long long selb = __ballot(sel);
-    const int pos = sel_run + lanes_below(selb);
-    if (sel && pos >= r0 && pos < r1) {
-      const int32_t v = candi[i];
-      if (out_g != nullptr) out_g[pos] = v;
-      if (out_l != nullptr) out_l[pos - r0] = v;
+  for (int i0 = lo; i0 < hi && sel_run < r1; i0 += 256) {  // wave-uniform loop
+    uint32_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      m[u] = i < hi ? (candk[i] & mask) : 0u;
     }
-    sel_run += __popcll(selb);
-    eq_run += __popcll(eqb);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      const bool gt = i < hi && m[u] > prefix;
+      const bool eq = i < hi && m[u] == prefix;
+      const unsigned long long eqb = __ballot(eq);
+      const bool sel = gt || (eq && eq_run + lanes_below(eqb) < krem);
+      const unsigned long long selb = __ballot(sel);
+      const int pos = sel_run + lanes_below(selb);
+      if (sel && pos >= r0 && pos < r1) {
+        const int32_t v = candi[i];
+        if (out_g != nullptr) out_g[pos] = v;
+        if (out_l != nullptr) out_l[pos - r0] = v;
+      }
+      sel_run += __popcll(selb);
+      eq_run += __popcll(eqb);
+    }
   }
 }
 

@@ -23,14 +23,12 @@ struct HeadState {
   int32_t n;            // context length
   uint32_t cand_total;  // candidates the scan found (diagnostic)
   uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every score (diagnostic)
-  uint32_t pad0;
-  uint64_t thr_word;    // (1 << 32) | theta once published within the scan, else 0
-  uint32_t pad[8];
+  uint32_t pad[11];
 };
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_ctrl, off_heads, off_tables, off_qcodes, off_samp, off_samp_vn, off_scores, off_counts,
+  size_t off_heads, off_tables, off_qcodes, off_samp, off_samp_vn, off_scores, off_counts,
       off_slots, off_part_o, off_part_ml, bytes;
   int chunk, nchunks, sample, srow, rps, nsplit, kind;
 };
@@ -39,7 +37,6 @@ struct FusedArgs {
   int Hq, Hkv, d, Nmax, L, P;
   double inv_tau;
   int kcap, sample, srow, nchunks, rps, nsplit, region_bytes;
-  uint32_t* ticket;  // workgroup ticket counter of a filtering scan (zeroed by prep)
   HeadState* heads;
   float* tables;     // [B*Hkv][2^P][L] bucket-major
   uint32_t* qcodes;  // [B*Hkv][G][4]
@@ -64,8 +61,8 @@ hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const voi
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
                              const void* scores, const int32_t* kps, hipStream_t st);
 int scan_chunk(int L);
-// filter != 0: the scan also derives each head's candidate threshold from the
-// gathered sample (prep with sampling must precede it) and fills the
+// filter != 0: each head's candidate threshold is first derived from the
+// gathered sample (prep with sampling must precede), then the scan fills the
 // candidate slots
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a, int kind, const void* src,
                        const void* vnorm, int norm_f16, void* scores_out, int filter,

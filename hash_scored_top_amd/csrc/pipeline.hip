@@ -4,9 +4,9 @@
 //   decode step (soft-LSH or binary codes):
 //     prep  (several workgroups per kv head: query tables / codes, and the
 //            key sample copied to a compact buffer)
-//     scan  (score every key once; one extra workgroup per kv head derives
-//            the candidate threshold from the sample meanwhile; keys scoring
-//            >= threshold go to the chunk candidate slots)
+//     threshold (one workgroup per kv head: sample scores -> threshold)
+//     scan  (score every key once; keys scoring >= threshold go to the
+//            chunk candidate slots)
 //     attend (each split derives the exact top-k from the candidates and
 //             attends over its part of the selected rows)
 //     combine (merge the splits through their log-sum-exp)
@@ -35,7 +35,6 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
     return r;
   };
   f.off_heads = take(BH * sizeof(HeadState));  // first: the head states start the workspace
-  f.off_ctrl = take(256);
   if (soft) f.off_tables = take(BH * (static_cast<size_t>(L) << P) * sizeof(float));
   if (ham) f.off_qcodes = take(static_cast<size_t>(s.B) * s.Hq * 16);
   if (select) {
@@ -84,7 +83,6 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   a.region_bytes = 65536;
   char* p = static_cast<char*>(ws);
   if (p != nullptr) {
-    a.ticket = reinterpret_cast<uint32_t*>(p + f.off_ctrl);
     a.heads = reinterpret_cast<HeadState*>(p + f.off_heads);
     a.tables = reinterpret_cast<float*>(p + f.off_tables);
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);

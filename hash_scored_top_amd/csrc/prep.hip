@@ -18,8 +18,8 @@
 //    stratified key sample (kSample keys per head) into a compact buffer, so
 //    the scattered reads are spread over many compute units.
 //
-// The scan derives the candidate threshold from that sample (scan.hip) and
-// keeps the keys scoring >= theta.  theta only bounds the work of the
+// A small kernel ahead of the scan derives the candidate threshold from that
+// sample (scan.hip); the scan keeps the keys scoring >= theta.  theta only bounds the work of the
 // selection: the selected set never depends on it.
 #include "fused_device.h"
 #include "hst_launch.h"
@@ -115,10 +115,6 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const int bh = blockIdx.y, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
-  if (a.sample != 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // state of the filtering scan
-    a.heads[bh].thr_word = 0ull;
-    if (bh == 0) *a.ticket = 0u;
-  }
   // sample share: loads issued now, stored after the table work
   const SampleShare ss = sample_share(a, seq_lens, k_per_seq, b);
   const int si = ss.i0 + t;
@@ -275,10 +271,6 @@ prep_qcodes_kernel(const T* __restrict__ q, const T* __restrict__ R, const uint3
   float* rl = reinterpret_cast<float*>(sm);
   float* ql = rl + 16 * ds;
 
-  if (a.sample != 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // state of the filtering scan
-    a.heads[bh].thr_word = 0ull;
-    if (bh == 0) *a.ticket = 0u;
-  }
   const SampleShare ss = sample_share(a, seq_lens, k_per_seq, b);
   const int si = ss.i0 + t;
   const bool son = si < ss.i1;
@@ -314,10 +306,6 @@ __global__ void __launch_bounds__(kPrepNT)
 prep_given_kernel(const KT* __restrict__ scores, const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ k_per_seq, FusedArgs a) {
   const int bh = blockIdx.y, b = bh / a.Hkv;
-  if (a.sample != 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // state of the filtering scan
-    a.heads[bh].thr_word = 0ull;
-    if (bh == 0) *a.ticket = 0u;
-  }
   const SampleShare ss = sample_share(a, seq_lens, k_per_seq, b);
   const int si = ss.i0 + static_cast<int>(threadIdx.x);
   if (si < ss.i1) {
@@ -329,10 +317,19 @@ prep_given_kernel(const KT* __restrict__ scores, const int32_t* __restrict__ seq
 // ---------------------------------------------------------------------------
 // launchers
 
+// Raises a kernel's dynamic LDS limit once per device (the largest size
+// requested so far).
 template <typename K>
 static hipError_t set_smem(K kern, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  static size_t done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(bytes));
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
+  return e;
 }
 
 hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* q, const void* W,

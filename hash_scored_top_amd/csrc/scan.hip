@@ -10,16 +10,8 @@
 //    128-bit codes against the G query codes.
 //  * Given scores (the stand-alone top-k): the scores are only filtered.
 //
-// When filtering, B*Hkv extra workgroups derive the heads' candidate
-// thresholds from the key sample prep gathered, while the others stream their
-// chunks; a chunk workgroup waits for its head's threshold only before its
-// epilogue.  Roles come from a ticket taken when a workgroup starts, and the
-// first B*Hkv tickets are the threshold workgroups: every workgroup that
-// waits therefore waits for one that is already running and never waits
-// itself.  The threshold is handed over in one 64-bit atomic word (flag and
-// value), so no other memory needs ordering; a wait that exceeds its bound
-// falls back to threshold 0 (every key a candidate), which leaves the
-// selection exact.
+// The candidate threshold of each head is derived from the key sample prep
+// gathered by a small kernel that runs before the scan (threshold_kernel).
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -159,33 +151,13 @@ __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt
 }
 
 
-// Work of a scan workgroup: a chunk of one head, or (filtering) the
-// threshold of one head.
-struct ScanWork {
-  int bh, chunk;
-  bool theta;
-};
-__device__ __forceinline__ ScanWork scan_work(const FusedArgs& a, bool filt, int BH, int nch, int* s_lid) {
-  int lid = blockIdx.x;
-  if (filt) {
-    if (threadIdx.x == 0) *s_lid = static_cast<int>(atomicAdd(a.ticket, 1u));
-    __syncthreads();
-    lid = *s_lid;
-  }
-  ScanWork w;
-  w.theta = filt && lid < BH;
-  const int x = w.theta ? 0 : (filt ? lid - BH : lid);
-  w.bh = w.theta ? lid : x / nch;
-  w.chunk = w.theta ? 0 : x % nch;
-  return w;
-}
-
 // Candidate threshold of head bh from the sample prep gathered; every thread
 // of the workgroup calls.  LDS: the head's table (soft-LSH, as the scan holds
 // it), the query codes (binary codes), kSample words of scratch in tile.
 template <int KIND, int LANES>
 __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, const float* tbl,
                                  const uint32_t* qc, uint32_t* tile, BlockScratch<kScanNT>& sc) {
+  // (the whole sample in one batch: every lane's loads in flight together)
   constexpr int NT = kScanNT;
   constexpr int PER = kSample / NT;
   const int S = a.sample > n ? n : a.sample;
@@ -195,7 +167,7 @@ __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, c
   const long long sb = static_cast<long long>(bh) * kSample;
   uint32_t key[PER];
   if (KIND == kScanSoftFast) {
-    constexpr int U = kScanSoftU;
+    constexpr int U = kSample * LANES / NT;
     SoftScorer<LANES, NT, U> ss;
     ss.idv = reinterpret_cast<const uint4*>(a.samp);
     ss.vnorm = a.samp_vn;
@@ -206,7 +178,7 @@ __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, c
     uint4 w[U];
     float nr[U];
     ss.load(w, nr, sb, ss.grp, S);
-    soft_score_range(ss, sb, 0, S, w, nr, reinterpret_cast<float*>(tile));
+    ss.compute(w, nr, ss.grp, S, 0, reinterpret_cast<float*>(tile));
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -251,40 +223,53 @@ __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, c
   return rank_lower_bound_regs<NT, PER>(key, S, r, tile, sc);
 }
 
-// Threshold workgroup: derive and publish head bh's threshold and state.
+// grid (B*Hkv): each head's candidate threshold and state.
 template <int KIND, int LANES>
-__device__ void theta_publish(const FusedArgs& a, int bh, const int32_t* seq_lens, const int32_t* k_per_seq,
-                              const float* tbl, const uint32_t* qc, uint32_t* tile,
-                              BlockScratch<kScanNT>& sc) {
-  const int b = bh / a.Hkv;
+__global__ void __launch_bounds__(kScanNT)
+threshold_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq, FusedArgs a) {
+  constexpr int NT = kScanNT;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ BlockScratch<NT> sc;
+  __shared__ uint32_t qc[64 * 4];
+  float* tbl = reinterpret_cast<float*>(smem_raw);
+  uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);  // kSample words
+  const int bh = blockIdx.x, b = bh / a.Hkv;
+  const int t = threadIdx.x;
+  if (KIND == kScanSoftFast || KIND == kScanSoftAny) {
+    const int nflt = a.L << a.P;
+    const float* src = a.tables + static_cast<long long>(bh) * nflt;
+    if ((nflt & 3) == 0) {  // 16-byte loads, four in flight per thread
+      const int nv = nflt / 4;
+      for (int i0 = 0; i0 < nv; i0 += NT * 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (i0 + u * NT + t < nv) v[u] = reinterpret_cast<const u32x4*>(src)[i0 + u * NT + t];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (i0 + u * NT + t < nv) reinterpret_cast<u32x4*>(tbl)[i0 + u * NT + t] = v[u];
+      }
+    } else {
+      for (int i = t; i < nflt; i += NT) tbl[i] = src[i];
+    }
+  }
+  if (KIND == kScanHamming) {
+    const int G = a.Hq / a.Hkv;
+    for (int i = t; i < G * 4; i += NT) qc[i] = a.qcodes[static_cast<long long>(bh) * G * 4 + i];
+  }
+  __syncthreads();
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int k_eff = keff_of(a.kcap, k_per_seq, b, n);
   const uint32_t theta = sample_theta<KIND, LANES>(a, bh, n, k_eff, tbl, qc, tile, sc);
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     HeadState* hs = a.heads + bh;
     hs->theta = theta;
     hs->k_eff = k_eff;
     hs->n = n;
-    __hip_atomic_store(&hs->thr_word, (1ull << 32) | theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Chunk workgroup: the head's threshold, once published (see above).
-__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, uint32_t* s_theta) {
-  if (threadIdx.x == 0) {
-    uint64_t v = 0;
-    for (int i = 0; i < kThetaSpin; ++i) {
-      v = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (v >> 32) break;
-      __builtin_amdgcn_s_sleep(4);
-    }
-    *s_theta = (v >> 32) ? static_cast<uint32_t>(v) : 0u;
-  }
-  __syncthreads();
-  return *s_theta;
-}
-
-// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]).
+// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch), chunk-major per head.
 template <int LANES, int U>
 __global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
 scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm, int norm_f16,
@@ -295,17 +280,13 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   constexpr int CH = kSoftChunk;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
-  __shared__ int s_lid;
-  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
   const bool filt = filter != 0;
-  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
-  const ScanWork wk = scan_work(a, filt, BH, nch, &s_lid);
-  const int bh = wk.bh, b = bh / a.Hkv;
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = wk.chunk * CH;
-  if (!wk.theta && j0 >= n) return;
+  const int j0 = chunk * CH;
+  if (j0 >= n) return;
   const int jend = min(j0 + CH, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   S sco;
@@ -317,26 +298,21 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   sco.setup();
   uint4 w[U];
   float nr[U];
-  if (!wk.theta) sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
+  sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
   {
     const int nflt = S::L << a.P;
     const float4* src = reinterpret_cast<const float4*>(a.tables + static_cast<long long>(bh) * nflt);
     for (int i = threadIdx.x; i < nflt / 4; i += NT) reinterpret_cast<float4*>(tbl)[i] = src[i];
   }
+  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
-  if (wk.theta) {
-    theta_publish<kScanSoftFast, LANES>(a, bh, seq_lens, k_per_seq, tbl, nullptr,
-                                        reinterpret_cast<uint32_t*>(tile), sc);
-    return;
-  }
   soft_score_range(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
-  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(wk.chunk) * CH;
+  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
                                                    slot, sc);
-  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + wk.chunk] = count;
+  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 
 // One-lane-per-key scans: soft-LSH with any L, binary codes, given scores.
@@ -351,18 +327,14 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
   __shared__ uint32_t qc[64 * 4];
-  __shared__ int s_lid;
-  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);
   uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);
   const bool filt = filter != 0;
-  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
-  const ScanWork wk = scan_work(a, filt, BH, nch, &s_lid);
-  const int bh = wk.bh, b = bh / a.Hkv;
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch, b = bh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = wk.chunk * CH;
-  if (!wk.theta && j0 >= n) return;
+  const int j0 = chunk * CH;
+  if (j0 >= n) return;
   const int jend = min(j0 + CH, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   if (KIND == kScanSoftAny) {
@@ -372,11 +344,8 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   }
   if (KIND == kScanHamming)
     for (int i = threadIdx.x; i < G * 4; i += NT) qc[i] = a.qcodes[static_cast<long long>(bh) * G * 4 + i];
+  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
-  if (wk.theta) {
-    theta_publish<KIND == kScanGivenI32 ? kScanGivenF32 : KIND, 1>(a, bh, seq_lens, k_per_seq, tbl, qc, tile, sc);
-    return;
-  }
   if (KIND == kScanSoftAny) {
     const uint32_t idmask = (1u << a.P) - 1u;
     for (int j = j0 + static_cast<int>(threadIdx.x); j < jend; j += NT) {
@@ -417,11 +386,10 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
     }
   }
   __syncthreads();
-  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(wk.chunk) * CH;
+  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
                                                   slot, sc);
-  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + wk.chunk] = count;
+  if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 
 int scan_chunk(int L) {
@@ -430,6 +398,21 @@ int scan_chunk(int L) {
 
 size_t scan_smem(int region, int chunk) { return static_cast<size_t>(region) + static_cast<size_t>(chunk) * 4; }
 
+// Raises a kernel's dynamic LDS limit once per device (the largest size
+// requested so far).
+template <typename K>
+static hipError_t lds_limit(K kern, size_t bytes) {
+  static size_t done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(bytes));
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
+  return e;
+}
+
 template <int LANES>
 static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_t* ids,
                                      const void* vnorm, int f16, const int32_t* sl, const int32_t* kps,
@@ -437,8 +420,7 @@ static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_
   constexpr int U = kScanSoftU;
   const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
   auto kern = scan_softlsh_kernel<LANES, U>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, kps, sout, filter, nch, a);
   return hipGetLastError();
@@ -450,12 +432,38 @@ static hipError_t launch_scan_lane_t(dim3 grid, const FusedArgs& a, const void* 
                                      int filter, int nch, hipStream_t st) {
   const size_t smem = scan_smem(a.region_bytes, kLaneChunk);
   auto kern = scan_lane_kernel<KIND>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, src, vnorm, f16, sl, kps,
                      static_cast<uint32_t*>(sout), filter, nch, a);
   return hipGetLastError();
+}
+
+template <int KIND, int LANES>
+static hipError_t launch_threshold_t(const hst_shape& s, const FusedArgs& a, const int32_t* kps,
+                                     hipStream_t st) {
+  const size_t smem = static_cast<size_t>(a.region_bytes) + kSample * 4;
+  auto kern = threshold_kernel<KIND, LANES>;
+  hipError_t e = lds_limit(kern, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(s.B * s.Hkv), dim3(kScanNT), smem, st, s.seq_lens, kps, a);
+  return hipGetLastError();
+}
+
+static hipError_t launch_threshold(const hst_shape& s, const FusedArgs& a, int kind, const int32_t* kps,
+                                   hipStream_t st) {
+  switch (kind) {
+    case kScanSoftFast:
+      switch (a.L) {
+        case 16: return launch_threshold_t<kScanSoftFast, 1>(s, a, kps, st);
+        case 32: return launch_threshold_t<kScanSoftFast, 2>(s, a, kps, st);
+        case 64: return launch_threshold_t<kScanSoftFast, 4>(s, a, kps, st);
+        default: return launch_threshold_t<kScanSoftFast, 8>(s, a, kps, st);
+      }
+    case kScanSoftAny: return launch_threshold_t<kScanSoftAny, 1>(s, a, kps, st);
+    case kScanHamming: return launch_threshold_t<kScanHamming, 1>(s, a, kps, st);
+    default: return launch_threshold_t<kScanGivenF32, 1>(s, a, kps, st);
+  }
 }
 
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, const void* src,
@@ -469,12 +477,16 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
                        : 0;
   const int nch = static_cast<int>((s.Nmax + chunk - 1) / chunk);
   const long long BH = static_cast<long long>(s.B) * s.Hkv;
-  const long long nblk = BH * nch + (filter ? BH : 0);
+  const long long nblk = BH * nch;
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(nblk));
   const uint8_t* ids = static_cast<const uint8_t*>(src);
   float* sout = static_cast<float*>(scores_out);
   const int32_t* sl = s.seq_lens;
+  if (filter) {
+    hipError_t e = launch_threshold(s, a, kind, kps, st);
+    if (e != hipSuccess) return e;
+  }
   switch (kind) {
     case kScanSoftFast:
       switch (a.L) {
