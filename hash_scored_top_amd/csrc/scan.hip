@@ -270,11 +270,11 @@ threshold_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict
 }
 
 // Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch), chunk-major per head.
-template <int LANES, int U>
+template <int LANES, int U, bool FILTER>
 __global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
 scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm, int norm_f16,
-                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
-                    float* __restrict__ scores_out, int filter, int nch, FusedArgs a) {
+                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores_out, int nch,
+                    FusedArgs a) {
   constexpr int NT = kScanNT;
   using S = SoftScorer<LANES, NT, U>;
   constexpr int CH = kSoftChunk;
@@ -282,7 +282,7 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   __shared__ BlockScratch<NT> sc;
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
-  const bool filt = filter != 0;
+  constexpr bool filt = FILTER;
   const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int j0 = chunk * CH;
@@ -413,17 +413,24 @@ static hipError_t lds_limit(K kern, size_t bytes) {
   return e;
 }
 
-template <int LANES>
-static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_t* ids,
-                                     const void* vnorm, int f16, const int32_t* sl, const int32_t* kps,
-                                     float* sout, int filter, int nch, hipStream_t st) {
-  constexpr int U = kScanSoftU;
+template <int LANES, bool FILTER>
+static hipError_t launch_scan_soft_f(dim3 grid, const FusedArgs& a, const uint8_t* ids,
+                                     const void* vnorm, int f16, const int32_t* sl, float* sout, int nch,
+                                     hipStream_t st) {
   const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
-  auto kern = scan_softlsh_kernel<LANES, U>;
+  auto kern = scan_softlsh_kernel<LANES, kScanSoftU, FILTER>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, kps, sout, filter, nch, a);
+  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, sout, nch, a);
   return hipGetLastError();
+}
+
+template <int LANES>
+static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_t* ids,
+                                     const void* vnorm, int f16, const int32_t* sl, float* sout,
+                                     int filter, int nch, hipStream_t st) {
+  return filter ? launch_scan_soft_f<LANES, true>(grid, a, ids, vnorm, f16, sl, sout, nch, st)
+                : launch_scan_soft_f<LANES, false>(grid, a, ids, vnorm, f16, sl, sout, nch, st);
 }
 
 template <int KIND>
@@ -490,10 +497,10 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
   switch (kind) {
     case kScanSoftFast:
       switch (a.L) {
-        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
-        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
-        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
-        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
+        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
+        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
+        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
       }
     case kScanSoftAny:
       return launch_scan_lane_t<kScanSoftAny>(grid, a, src, vnorm, norm_f16, sl, kps, scores_out, filter, nch, st);

@@ -468,3 +468,37 @@ def test_decode_workspace_reuse_matches_fresh():
                                   seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
         i2, o2, l2 = fresh(q, d["K"], d["V"], d["W"], ids, vn)
         assert torch.equal(i1, i2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The decode step captured in a graph (as bench.py times it) reproduces the
+    eager result on every replay, with other eager steps on the same buffers
+    and synchronizations between the replays."""
+    hst = _hst()
+    from tests.gpu_helpers import norm_torch_dtype
+    w = MED_SOFT
+    x, d = inputs(w)
+    ids, vn = hst.hst_hash_keys_softlsh(d["K"], d["V"], d["W"], w.L, w.P,
+                                        norm_torch_dtype(w.norm_dtype), seq_lens=d["seq_lens"])
+    step = hst.DecodeSoftLSH(d["K"], w.Hq, w.L, w.P, w.tau, w.k_max(), vn.dtype,
+                             seq_lens=d["seq_lens"], k_per_seq=d["k_per_seq"])
+    q_other = torch.flip(d["q"], dims=[1]).contiguous()
+    ref = [t.clone() for t in step(d["q"], d["K"], d["V"], d["W"], ids, vn)]
+    other = [t.clone() for t in step(q_other, d["K"], d["V"], d["W"], ids, vn)]
+    assert not torch.equal(ref[1], other[1])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(d["q"], d["K"], d["V"], d["W"], ids, vn)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(d["q"], d["K"], d["V"], d["W"], ids, vn)
+    for _ in range(4):
+        got = step(q_other, d["K"], d["V"], d["W"], ids, vn)  # eager work on the same buffers
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(got, other))
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip((step.idx, step.out, step.lse), ref))
