@@ -21,17 +21,22 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
   return x;
 }
 
-// Position of sample i among n keys: one key per stratum [i*n/S, (i+1)*n/S).
-// S is kSample (a power of two) whenever n > kSample, else every key is taken.
-static_assert((kSample & (kSample - 1)) == 0, "sample size must be a power of two");
+// Position of sample i among n keys.  When n > kSample the sample is
+// kSample / kRunLen runs of kRunLen consecutive keys, run r at a fixed
+// pseudo-random offset inside stratum r = [r*n/R, (r+1)*n/R) (every stratum
+// is at least kRunLen keys wide), so a workgroup can read the sampled keys'
+// metadata in short contiguous pieces; otherwise every key is taken.
+static_assert((kSample & (kSample - 1)) == 0 && kSample % kRunLen == 0, "sample shape");
 __device__ __forceinline__ int sample_pos(int i, int S, int n) {
   if (S >= n) return i;
-  constexpr int kShift = __builtin_ctz(kSample);
+  constexpr int kRuns = kSample / kRunLen;
+  constexpr int kShift = __builtin_ctz(kRuns);
+  const int r = i / kRunLen, o = i % kRunLen;
   const unsigned long long nn = static_cast<unsigned long long>(n);
-  const uint32_t lo = static_cast<uint32_t>((static_cast<unsigned long long>(i) * nn) >> kShift);
-  const uint32_t hi = static_cast<uint32_t>((static_cast<unsigned long long>(i + 1) * nn) >> kShift);
-  const uint32_t w = hi - lo;
-  return static_cast<int>(lo + (w > 1 ? mix32(static_cast<uint32_t>(i) * 0x9e3779b9u + 0x632be5abu) % w : 0u));
+  const uint32_t lo = static_cast<uint32_t>((static_cast<unsigned long long>(r) * nn) >> kShift);
+  const uint32_t hi = static_cast<uint32_t>((static_cast<unsigned long long>(r + 1) * nn) >> kShift);
+  const uint32_t span = hi - lo - kRunLen + 1;  // >= 1
+  return static_cast<int>(lo + mix32(static_cast<uint32_t>(r) * 0x9e3779b9u + 0x632be5abu) % span) + o;
 }
 
 __device__ __forceinline__ int keff_of(int kcap, const int32_t* k_per_seq, int b, int n) {
@@ -61,6 +66,25 @@ __device__ __forceinline__ float group_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
   if (LANES >= 8) v += __shfl_xor(v, 4, 8);
   return v;
+}
+
+// Copies n >= 1 16-byte vectors from global memory to LDS with NT threads.
+// Each thread moves runs of B consecutive vectors (one address, immediate
+// offsets), so its B loads are issued back to back; a run past the end is
+// clamped to the last vector and only the stores are predicated.
+template <int NT, int B>
+__device__ __forceinline__ void copy_to_lds(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int n) {
+  for (int r0 = 0; r0 < n; r0 += NT * B) {
+    const int i = r0 + static_cast<int>(threadIdx.x) * B;
+    const u32x4* p = src + (i + B <= n ? i : n - B >= 0 ? n - B : 0);
+    u32x4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) v[u] = p[u < n ? u : 0];
+    const int base = i + B <= n ? i : (n - B >= 0 ? n - B : 0);
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (base + u < n && base + u >= i) dst[base + u] = v[u];
+  }
 }
 
 constexpr int kSelCap = 8192;  // candidates a workgroup selects from in LDS

@@ -10,6 +10,7 @@
 namespace hst {
 
 constexpr int kSample = 2048;      // keys sampled per head for the candidate threshold
+constexpr int kRunLen = 8;         // the sample is kSample / kRunLen runs of consecutive keys
 constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
 constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
 constexpr int kPrepBlocks = 8;     // prep workgroups per head (at least): each gathers 1/8 of the sample
@@ -23,25 +24,29 @@ struct HeadState {
   int32_t n;            // context length
   uint32_t cand_total;  // candidates the scan found (diagnostic)
   uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every score (diagnostic)
-  uint32_t pad[11];
+  uint32_t pad0;
+  uint64_t thr_word;    // (1 << 32) | theta once the scan has published it, else 0
+  uint32_t pad[8];
 };
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_heads, off_tables, off_qcodes, off_samp, off_samp_vn, off_scores, off_counts,
+  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_scores, off_counts,
       off_slots, off_part_o, off_part_ml, bytes;
-  int chunk, nchunks, sample, srow, rps, nsplit, kind;
+  int chunk, nchunks, sample, xparts, rps, nsplit, kind;
 };
 
 struct FusedArgs {
   int Hq, Hkv, d, Nmax, L, P;
   double inv_tau;
-  int kcap, sample, srow, nchunks, rps, nsplit, region_bytes;
+  int kcap, sample, xparts, nchunks, rps, nsplit, region_bytes;
   HeadState* heads;
   float* tables;     // [B*Hkv][2^P][L] bucket-major
   uint32_t* qcodes;  // [B*Hkv][G][4]
-  uint8_t* samp;     // [B*Hkv][kSample][srow]: sampled key metadata (ids / code / score key)
-  float* samp_vn;    // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
+  float* spart;      // [B*Hkv][xparts][kSample]: partial sample scores, one part per prep workgroup
+                     //   (soft-LSH: tables of the workgroup; binary codes: its 16 code bits;
+                     //   given scores: part 0 holds the order keys' bits)
+  float* svn;        // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
   uint32_t* counts;  // [B*Hkv][nchunks]
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index)
   float* part_o;     // [B*Hq][nsplit][d]
@@ -60,9 +65,10 @@ hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const voi
                                const uint32_t* codes, const int32_t* kps, hipStream_t st);
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
                              const void* scores, const int32_t* kps, hipStream_t st);
+int prep_parts(int kind, int L);  // partial sample scores per head (prep workgroups)
 int scan_chunk(int L);
-// filter != 0: each head's candidate threshold is first derived from the
-// gathered sample (prep with sampling must precede), then the scan fills the
+// filter != 0: the scan also derives each head's candidate threshold from the
+// partial sample scores (prep with sampling must precede it) and fills the
 // candidate slots
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a, int kind, const void* src,
                        const void* vnorm, int norm_f16, void* scores_out, int filter,

@@ -3,10 +3,10 @@
 //
 //   decode step (soft-LSH or binary codes):
 //     prep  (several workgroups per kv head: query tables / codes, and the
-//            key sample copied to a compact buffer)
-//     threshold (one workgroup per kv head: sample scores -> threshold)
-//     scan  (score every key once; keys scoring >= threshold go to the
-//            chunk candidate slots)
+//            key sample scored on each workgroup's part of the hash)
+//     scan  (score every key once; one extra workgroup per kv head derives
+//            the candidate threshold from the sample meanwhile; keys scoring
+//            >= threshold go to the chunk candidate slots)
 //     attend (each split derives the exact top-k from the candidates and
 //             attends over its part of the selected rows)
 //     combine (merge the splits through their log-sum-exp)
@@ -38,9 +38,9 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
   if (soft) f.off_tables = take(BH * (static_cast<size_t>(L) << P) * sizeof(float));
   if (ham) f.off_qcodes = take(static_cast<size_t>(s.B) * s.Hq * 16);
   if (select) {
-    f.srow = soft ? L : (ham ? 16 : 4);
-    f.off_samp = take(BH * static_cast<size_t>(kSample) * f.srow);
-    if (soft) f.off_samp_vn = take(BH * static_cast<size_t>(kSample) * 4);
+    f.xparts = prep_parts(f.kind, L);
+    f.off_spart = take(BH * static_cast<size_t>(f.xparts) * kSample * 4);
+    if (soft) f.off_svn = take(BH * static_cast<size_t>(kSample) * 4);
   }
   if (decode) f.off_scores = take(BH * static_cast<size_t>(s.Nmax) * 4);
   if (select) {
@@ -79,15 +79,15 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   a.nchunks = f.nchunks;
   a.rps = f.rps;
   a.nsplit = f.nsplit;
-  a.srow = f.srow;
+  a.xparts = f.xparts;
   a.region_bytes = 65536;
   char* p = static_cast<char*>(ws);
   if (p != nullptr) {
     a.heads = reinterpret_cast<HeadState*>(p + f.off_heads);
     a.tables = reinterpret_cast<float*>(p + f.off_tables);
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
-    a.samp = reinterpret_cast<uint8_t*>(p + f.off_samp);
-    a.samp_vn = reinterpret_cast<float*>(p + f.off_samp_vn);
+    a.spart = reinterpret_cast<float*>(p + f.off_spart);
+    a.svn = reinterpret_cast<float*>(p + f.off_svn);
     a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
     a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
     a.part_o = reinterpret_cast<float*>(p + f.off_part_o);

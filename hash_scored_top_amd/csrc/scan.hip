@@ -10,8 +10,14 @@
 //    128-bit codes against the G query codes.
 //  * Given scores (the stand-alone top-k): the scores are only filtered.
 //
-// The candidate threshold of each head is derived from the key sample prep
-// gathered by a small kernel that runs before the scan (threshold_kernel).
+// When filtering, B*Hkv extra workgroups (the first ones of the grid, which
+// the dispatcher starts first) derive the heads' candidate thresholds from the
+// partial sample scores prep wrote, while the others stream their chunks; a
+// chunk workgroup waits for its head's threshold only before its epilogue.
+// The threshold is handed over in one 64-bit atomic word (flag and value), so
+// no other memory needs ordering.  Every wait is bounded: past the bound it
+// falls back to threshold 0 (every key a candidate), which leaves the
+// selection exact, so no dispatch order can stall the kernel.
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -22,17 +28,19 @@ constexpr int kSoftChunk = 2048;
 constexpr int kLaneChunk = 4096;
 static_assert(kSoftChunk >= kSample && kLaneChunk >= kSample && kSample >= 2048,
               "chunk tile holds the sample scores and doubles as the select histogram");
-constexpr int kThetaSpin = 1 << 16;
-constexpr int kScanSoftU = 2;  // key batches per lane group in flight (two workgroups fit a CU)  // polls of the threshold word before falling back
+constexpr int kScanSoftU = 2;        // key batches per lane group in flight (two workgroups fit a CU)
+constexpr int kThetaSpin = 1 << 16;  // polls of the threshold word before falling back
+constexpr int kMaxParts = 16;        // partial sample scores per head (prep workgroups)
 
-template <int LANES, int NT, int U>
+// F16: value norms stored as binary16 (else float32); the raw bits are loaded
+// and converted only when used, so a load never waits for its own result.
+template <int LANES, int NT, int U, bool F16>
 struct SoftScorer {
   static constexpr int L = 16 * LANES;
   static constexpr int KPI = NT / LANES;  // keys per batch
   static constexpr int TILE = KPI * U;
   const uint4* idv;
   const void* vnorm;
-  int norm_f16;
   const float* tbl;  // LDS
   uint32_t idmask;   // 2^P - 1: ids outside the table cannot leave it
   int sub, grp;
@@ -41,20 +49,21 @@ struct SoftScorer {
     sub = threadIdx.x % LANES;
     grp = threadIdx.x / LANES;
   }
-  __device__ __forceinline__ void load(uint4 (&w)[U], float (&nr)[U], long long base, int jb,
+  // Loads of a batch; keys past jend (>= 1) read key jend - 1 instead, so the
+  // loads carry no branch and all are in flight together.
+  __device__ __forceinline__ void load(uint4 (&w)[U], uint32_t (&nr)[U], long long base, int jb,
                                        int jend) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + u * KPI;
-      if (j < jend) {
-        w[u] = idv[(base + j) * LANES + sub];
-        nr[u] = norm_f16 ? f16_bits_to_f32(static_cast<const uint16_t*>(vnorm)[base + j])
-                         : static_cast<const float*>(vnorm)[base + j];
-      }
+      const int j0 = jb + u * KPI;
+      const long long j = base + (j0 < jend ? j0 : jend - 1);
+      w[u] = idv[j * LANES + sub];
+      nr[u] = F16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(vnorm)[j])
+                  : static_cast<const uint32_t*>(vnorm)[j];
     }
   }
   // scores of the batch held in (w, nr) into out[j - j0]
-  __device__ __forceinline__ void compute(const uint4 (&w)[U], const float (&nr)[U], int jb, int jend,
+  __device__ __forceinline__ void compute(const uint4 (&w)[U], const uint32_t (&nr)[U], int jb, int jend,
                                           int j0, float* out) const {
     const int k = grp & 15;
     const int qw = k >> 2, sh = k & 3;
@@ -82,33 +91,32 @@ struct SoftScorer {
           acc0 += *reinterpret_cast<const float*>(tb + (id0 * L + l0) * 4);
           acc1 += *reinterpret_cast<const float*>(tb + (id1 * L + l1) * 4);
         }
-        const float sv = group_sum<LANES>(acc0 + acc1) * nr[u];
+        const float vn = F16 ? f16_bits_to_f32(static_cast<uint16_t>(nr[u])) : __uint_as_float(nr[u]);
+        const float sv = group_sum<LANES>(acc0 + acc1) * vn;
         if (sub == 0) out[j - j0] = sv;
       }
     }
   }
 };
 
-// Scores of keys [j0, jend) (rows base + j) into out[j - j0]; (w, nr) hold the
-// first batch, already loaded.  The next batch is in flight during each
-// batch's table lookups.
-template <class S, int U>
-__device__ __forceinline__ void soft_score_range(const S& sco, long long base, int j0, int jend,
-                                                 uint4 (&w)[U], float (&nr)[U], float* out) {
-  uint4 wn[U];
-  float nn[U];
-  for (int t0 = j0; t0 < jend; t0 += S::TILE) {
-    const int jb = t0 + sco.grp;
-    const bool more = t0 + S::TILE < jend;
-    if (more) sco.load(wn, nn, base, jb + S::TILE, jend);
-    sco.compute(w, nr, jb, jend, j0, out);
-    if (more) {
+// Scores of keys [j0, min(jend, j0 + NTILES * TILE)) into out[j - j0];
+// (wa, na) hold the first batch, already loaded.  Two register sets
+// alternate, so the next batch is in flight during each batch's table
+// lookups without register copies (a copy, or a loop back edge, would make
+// the compiler wait for the loads first): the tile loop is unrolled and every
+// load is unconditional, only the lookups are skipped past jend.
+template <int NTILES, class S, int U>
+__device__ __forceinline__ void soft_score_tiles(const S& sco, long long base, int j0, int jend,
+                                                 uint4 (&wa)[U], uint32_t (&na)[U], float* out) {
+  uint4 wb[U];
+  uint32_t nb[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        w[u] = wn[u];
-        nr[u] = nn[u];
-      }
-    }
+  for (int it = 0; it < NTILES; it += 2) {
+    const int t0 = j0 + it * S::TILE, t1 = t0 + S::TILE;
+    if (it + 1 < NTILES) sco.load(wb, nb, base, t1 + sco.grp, jend);
+    if (t0 < jend) sco.compute(wa, na, t0 + sco.grp, jend, j0, out);
+    if (it + 2 < NTILES) sco.load(wa, na, base, t1 + S::TILE + sco.grp, jend);
+    if (it + 1 < NTILES && t1 < jend) sco.compute(wb, nb, t1 + sco.grp, jend, j0, out);
   }
 }
 
@@ -151,139 +159,122 @@ __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt
 }
 
 
-// Candidate threshold of head bh from the sample prep gathered; every thread
-// of the workgroup calls.  LDS: the head's table (soft-LSH, as the scan holds
-// it), the query codes (binary codes), kSample words of scratch in tile.
-template <int KIND, int LANES>
-__device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, const float* tbl,
-                                 const uint32_t* qc, uint32_t* tile, BlockScratch<kScanNT>& sc) {
-  // (the whole sample in one batch: every lane's loads in flight together)
+// Work of a scan workgroup: a chunk of one head, or (filtering) the
+// threshold of one head.
+struct ScanWork {
+  int bh, chunk;
+  bool theta;
+};
+__device__ __forceinline__ ScanWork scan_work(bool filt, int BH, int nch) {
+  const int lid = blockIdx.x;
+  ScanWork w;
+  w.theta = filt && lid < BH;
+  const int x = w.theta ? 0 : (filt ? lid - BH : lid);
+  w.bh = w.theta ? lid : x / nch;
+  w.chunk = w.theta ? 0 : x % nch;
+  return w;
+}
+
+// Candidate threshold of head bh: the sample scores are the sums of the
+// parts prep wrote (times the sampled value norm for soft-LSH), and theta is
+// a lower bound of the sample score at a high-margin rank.  Every thread of
+// the workgroup calls; tile: kSample words of LDS scratch.
+template <int KIND>
+__device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, uint32_t* tile,
+                                 BlockScratch<kScanNT>& sc) {
   constexpr int NT = kScanNT;
   constexpr int PER = kSample / NT;
   const int S = a.sample > n ? n : a.sample;
   const int r = sample_rank(k_eff, n, S);
   if (!(S > 0 && k_eff > 0 && r < S)) return 0u;
   const int t = threadIdx.x;
-  const long long sb = static_cast<long long>(bh) * kSample;
+  const float* part = a.spart + static_cast<long long>(bh) * a.xparts * kSample;
+  const int X = a.xparts;
   uint32_t key[PER];
-  if (KIND == kScanSoftFast) {
-    constexpr int U = kSample * LANES / NT;
-    SoftScorer<LANES, NT, U> ss;
-    ss.idv = reinterpret_cast<const uint4*>(a.samp);
-    ss.vnorm = a.samp_vn;
-    ss.norm_f16 = 0;
-    ss.tbl = tbl;
-    ss.idmask = (1u << a.P) - 1u;
-    ss.setup();
-    uint4 w[U];
-    float nr[U];
-    ss.load(w, nr, sb, ss.grp, S);
-    ss.compute(w, nr, ss.grp, S, 0, reinterpret_cast<float*>(tile));
-    __syncthreads();
+  if (KIND == kScanGivenF32 || KIND == kScanGivenI32) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int i = t + e * NT;
-      key[e] = i < S ? order_key_f32(__uint_as_float(tile[i])) : 0u;
-    }
-  } else if (KIND == kScanSoftAny) {
-    const uint32_t idm = (1u << a.P) - 1u;
+    for (int e = 0; e < PER; ++e) key[e] = __float_as_uint(part[t + e * NT]);  // order keys' bits
+  } else {
+    // every part of both keys in flight together (indices clamped to the parts
+    // that exist; entries past S are ignored by the rank)
+    float pv[PER][kMaxParts];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int i = t + e * NT;
-      float sv = 0.f;
-      if (i < S) {
-        const uint8_t* row = a.samp + (sb + i) * a.L;
-        for (int l = 0; l < a.L; ++l) sv += tbl[(row[l] & idm) * a.L + l];
-        sv *= a.samp_vn[sb + i];
-      }
-      key[e] = order_key_f32(sv);
-    }
-  } else if (KIND == kScanHamming) {
+    for (int e = 0; e < PER; ++e)
+#pragma unroll
+      for (int x = 0; x < kMaxParts; ++x) pv[e][x] = part[(x < X ? x : X - 1) * kSample + t + e * NT];
+    float vn[PER];
+    if (KIND != kScanHamming)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) vn[e] = a.svn[static_cast<long long>(bh) * kSample + t + e * NT];
     const int G = a.Hq / a.Hkv;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int i = t + e * NT;
-      int ham = 0;
-      if (i < S) {
-        const u32x4 cv = reinterpret_cast<const u32x4*>(a.samp)[sb + i];
-        for (int g = 0; g < G; ++g)
-          ham += __popc(cv.x ^ qc[4 * g]) + __popc(cv.y ^ qc[4 * g + 1]) +
-                 __popc(cv.z ^ qc[4 * g + 2]) + __popc(cv.w ^ qc[4 * g + 3]);
-      }
-      key[e] = order_key_i32(128 * G - ham);
-    }
-  } else {
+      float acc = 0.f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int i = t + e * NT;
-      key[e] = i < S ? reinterpret_cast<const uint32_t*>(a.samp)[sb + i] : 0u;
+      for (int x = 0; x < kMaxParts; ++x)
+        if (x < X) acc += pv[e][x];
+      key[e] = KIND == kScanHamming ? order_key_i32(128 * G - static_cast<int>(acc))
+                                    : order_key_f32(acc * vn[e]);
     }
   }
-  __syncthreads();  // tile becomes the histogram
   return rank_lower_bound_regs<NT, PER>(key, S, r, tile, sc);
 }
 
-// grid (B*Hkv): each head's candidate threshold and state.
-template <int KIND, int LANES>
-__global__ void __launch_bounds__(kScanNT)
-threshold_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq, FusedArgs a) {
-  constexpr int NT = kScanNT;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ BlockScratch<NT> sc;
-  __shared__ uint32_t qc[64 * 4];
-  float* tbl = reinterpret_cast<float*>(smem_raw);
-  uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);  // kSample words
-  const int bh = blockIdx.x, b = bh / a.Hkv;
-  const int t = threadIdx.x;
-  if (KIND == kScanSoftFast || KIND == kScanSoftAny) {
-    const int nflt = a.L << a.P;
-    const float* src = a.tables + static_cast<long long>(bh) * nflt;
-    if ((nflt & 3) == 0) {  // 16-byte loads, four in flight per thread
-      const int nv = nflt / 4;
-      for (int i0 = 0; i0 < nv; i0 += NT * 4) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i0 + u * NT + t < nv) v[u] = reinterpret_cast<const u32x4*>(src)[i0 + u * NT + t];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i0 + u * NT + t < nv) reinterpret_cast<u32x4*>(tbl)[i0 + u * NT + t] = v[u];
-      }
-    } else {
-      for (int i = t; i < nflt; i += NT) tbl[i] = src[i];
-    }
-  }
-  if (KIND == kScanHamming) {
-    const int G = a.Hq / a.Hkv;
-    for (int i = t; i < G * 4; i += NT) qc[i] = a.qcodes[static_cast<long long>(bh) * G * 4 + i];
-  }
-  __syncthreads();
+// Threshold workgroup: derive and publish head bh's threshold and state.
+template <int KIND>
+__device__ void theta_publish(const FusedArgs& a, int bh, const int32_t* seq_lens, const int32_t* k_per_seq,
+                              uint32_t* tile, BlockScratch<kScanNT>& sc) {
+  const int b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int k_eff = keff_of(a.kcap, k_per_seq, b, n);
-  const uint32_t theta = sample_theta<KIND, LANES>(a, bh, n, k_eff, tbl, qc, tile, sc);
-  if (t == 0) {
+  const uint32_t theta = sample_theta<KIND>(a, bh, n, k_eff, tile, sc);
+  if (threadIdx.x == 0) {
     HeadState* hs = a.heads + bh;
     hs->theta = theta;
     hs->k_eff = k_eff;
     hs->n = n;
+    __hip_atomic_store(&hs->thr_word, (1ull << 32) | theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch), chunk-major per head.
-template <int LANES, int U, bool FILTER>
+// Chunk workgroup: the head's threshold, once published (see above).
+__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, uint32_t* s_theta) {
+  if (threadIdx.x == 0) {
+    uint64_t v = 0;
+    for (int i = 0; i < kThetaSpin; ++i) {
+      v = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v >> 32) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    *s_theta = (v >> 32) ? static_cast<uint32_t>(v) : 0u;
+  }
+  __syncthreads();
+  return *s_theta;
+}
+
+// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]).
+template <int LANES, int U, bool FILTER, bool F16>
 __global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
-scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm, int norm_f16,
-                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores_out, int nch,
-                    FusedArgs a) {
+scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm,
+                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
+                    float* __restrict__ scores_out, int nch, FusedArgs a) {
   constexpr int NT = kScanNT;
-  using S = SoftScorer<LANES, NT, U>;
+  using S = SoftScorer<LANES, NT, U, F16>;
   constexpr int CH = kSoftChunk;
+  static_assert(CH % S::TILE == 0, "whole tiles per chunk");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
+  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
   constexpr bool filt = FILTER;
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch, b = bh / a.Hkv;
+  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
+  const ScanWork wk = scan_work(filt, BH, nch);
+  if (filt && wk.theta) {
+    theta_publish<kScanSoftFast>(a, wk.bh, seq_lens, k_per_seq, reinterpret_cast<uint32_t*>(tile), sc);
+    return;
+  }
+  const int bh = wk.bh, chunk = wk.chunk, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int j0 = chunk * CH;
   if (j0 >= n) return;
@@ -292,22 +283,21 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   S sco;
   sco.idv = reinterpret_cast<const uint4*>(ids);
   sco.vnorm = vnorm;
-  sco.norm_f16 = norm_f16;
   sco.tbl = tbl;
   sco.idmask = (1u << a.P) - 1u;
   sco.setup();
   uint4 w[U];
-  float nr[U];
+  uint32_t nr[U];
   sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
   {
-    const int nflt = S::L << a.P;
-    const float4* src = reinterpret_cast<const float4*>(a.tables + static_cast<long long>(bh) * nflt);
-    for (int i = threadIdx.x; i < nflt / 4; i += NT) reinterpret_cast<float4*>(tbl)[i] = src[i];
+    const int nflt = S::L << a.P;  // a multiple of 16: L is
+    copy_to_lds<NT, 4>(reinterpret_cast<u32x4*>(tbl),
+                       reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt), nflt / 4);
   }
-  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
-  soft_score_range(sco, base, j0, jend, w, nr, tile);
+  soft_score_tiles<CH / S::TILE>(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
+  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
   uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
@@ -327,10 +317,17 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
   __shared__ uint32_t qc[64 * 4];
+  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);
   uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);
   const bool filt = filter != 0;
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch, b = bh / a.Hkv;
+  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
+  const ScanWork wk = scan_work(filt, BH, nch);
+  if (filt && wk.theta) {
+    theta_publish<KIND>(a, wk.bh, seq_lens, k_per_seq, tile, sc);
+    return;
+  }
+  const int bh = wk.bh, chunk = wk.chunk, b = bh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
   const int j0 = chunk * CH;
@@ -344,7 +341,6 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   }
   if (KIND == kScanHamming)
     for (int i = threadIdx.x; i < G * 4; i += NT) qc[i] = a.qcodes[static_cast<long long>(bh) * G * 4 + i];
-  const uint32_t theta = filt ? a.heads[bh].theta : 0u;
   __syncthreads();
   if (KIND == kScanSoftAny) {
     const uint32_t idmask = (1u << a.P) - 1u;
@@ -386,6 +382,7 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
     }
   }
   __syncthreads();
+  const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
   uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
                                                   slot, sc);
@@ -413,24 +410,27 @@ static hipError_t lds_limit(K kern, size_t bytes) {
   return e;
 }
 
-template <int LANES, bool FILTER>
+template <int LANES, bool FILTER, bool F16>
 static hipError_t launch_scan_soft_f(dim3 grid, const FusedArgs& a, const uint8_t* ids,
-                                     const void* vnorm, int f16, const int32_t* sl, float* sout, int nch,
-                                     hipStream_t st) {
+                                     const void* vnorm, const int32_t* sl, const int32_t* kps,
+                                     float* sout, int nch, hipStream_t st) {
   const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
-  auto kern = scan_softlsh_kernel<LANES, kScanSoftU, FILTER>;
+  auto kern = scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, f16, sl, sout, nch, a);
+  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, sl, kps, sout, nch, a);
   return hipGetLastError();
 }
 
 template <int LANES>
 static hipError_t launch_scan_soft_t(dim3 grid, const FusedArgs& a, const uint8_t* ids,
-                                     const void* vnorm, int f16, const int32_t* sl, float* sout,
-                                     int filter, int nch, hipStream_t st) {
-  return filter ? launch_scan_soft_f<LANES, true>(grid, a, ids, vnorm, f16, sl, sout, nch, st)
-                : launch_scan_soft_f<LANES, false>(grid, a, ids, vnorm, f16, sl, sout, nch, st);
+                                     const void* vnorm, int f16, const int32_t* sl, const int32_t* kps,
+                                     float* sout, int filter, int nch, hipStream_t st) {
+  if (filter)
+    return f16 ? launch_scan_soft_f<LANES, true, true>(grid, a, ids, vnorm, sl, kps, sout, nch, st)
+               : launch_scan_soft_f<LANES, true, false>(grid, a, ids, vnorm, sl, kps, sout, nch, st);
+  return f16 ? launch_scan_soft_f<LANES, false, true>(grid, a, ids, vnorm, sl, kps, sout, nch, st)
+             : launch_scan_soft_f<LANES, false, false>(grid, a, ids, vnorm, sl, kps, sout, nch, st);
 }
 
 template <int KIND>
@@ -446,33 +446,6 @@ static hipError_t launch_scan_lane_t(dim3 grid, const FusedArgs& a, const void* 
   return hipGetLastError();
 }
 
-template <int KIND, int LANES>
-static hipError_t launch_threshold_t(const hst_shape& s, const FusedArgs& a, const int32_t* kps,
-                                     hipStream_t st) {
-  const size_t smem = static_cast<size_t>(a.region_bytes) + kSample * 4;
-  auto kern = threshold_kernel<KIND, LANES>;
-  hipError_t e = lds_limit(kern, smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(s.B * s.Hkv), dim3(kScanNT), smem, st, s.seq_lens, kps, a);
-  return hipGetLastError();
-}
-
-static hipError_t launch_threshold(const hst_shape& s, const FusedArgs& a, int kind, const int32_t* kps,
-                                   hipStream_t st) {
-  switch (kind) {
-    case kScanSoftFast:
-      switch (a.L) {
-        case 16: return launch_threshold_t<kScanSoftFast, 1>(s, a, kps, st);
-        case 32: return launch_threshold_t<kScanSoftFast, 2>(s, a, kps, st);
-        case 64: return launch_threshold_t<kScanSoftFast, 4>(s, a, kps, st);
-        default: return launch_threshold_t<kScanSoftFast, 8>(s, a, kps, st);
-      }
-    case kScanSoftAny: return launch_threshold_t<kScanSoftAny, 1>(s, a, kps, st);
-    case kScanHamming: return launch_threshold_t<kScanHamming, 1>(s, a, kps, st);
-    default: return launch_threshold_t<kScanGivenF32, 1>(s, a, kps, st);
-  }
-}
-
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, const void* src,
                        const void* vnorm, int norm_f16, void* scores_out, int filter,
                        const int32_t* kps, hipStream_t st) {
@@ -484,23 +457,19 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
                        : 0;
   const int nch = static_cast<int>((s.Nmax + chunk - 1) / chunk);
   const long long BH = static_cast<long long>(s.B) * s.Hkv;
-  const long long nblk = BH * nch;
+  const long long nblk = BH * nch + (filter ? BH : 0);
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(nblk));
   const uint8_t* ids = static_cast<const uint8_t*>(src);
   float* sout = static_cast<float*>(scores_out);
   const int32_t* sl = s.seq_lens;
-  if (filter) {
-    hipError_t e = launch_threshold(s, a, kind, kps, st);
-    if (e != hipSuccess) return e;
-  }
   switch (kind) {
     case kScanSoftFast:
       switch (a.L) {
-        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
-        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
-        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
-        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, sl, sout, filter, nch, st);
+        case 16: return launch_scan_soft_t<1>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        case 32: return launch_scan_soft_t<2>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        case 64: return launch_scan_soft_t<4>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
+        default: return launch_scan_soft_t<8>(grid, a, ids, vnorm, norm_f16, sl, kps, sout, filter, nch, st);
       }
     case kScanSoftAny:
       return launch_scan_lane_t<kScanSoftAny>(grid, a, src, vnorm, norm_f16, sl, kps, scores_out, filter, nch, st);

@@ -353,8 +353,10 @@ def test_decode_is_deterministic():
 
 # ---------------------------------------------------------------- fused select paths
 
-def _sample_positions(n, S=2048):
-    """Stratified sample positions of the candidate-threshold estimate."""
+def _sample_positions(n, S=2048, run=8):
+    """Positions of the key sample behind the candidate threshold: S/run runs
+    of `run` consecutive keys, run r at a fixed pseudo-random offset inside
+    stratum r of [0, n) (every key when n <= S)."""
     if S >= n:
         return list(range(n))
 
@@ -367,12 +369,13 @@ def _sample_positions(n, S=2048):
         x ^= x >> 16
         return x
 
+    runs = S // run
     out = []
-    for i in range(S):
-        lo, hi = i * n // S, (i + 1) * n // S
-        w = hi - lo
-        off = mix32((i * 0x9E3779B9 + 0x632BE5AB) & 0xFFFFFFFF) % w if w > 1 else 0
-        out.append(lo + off)
+    for r in range(runs):
+        lo, hi = r * n // runs, (r + 1) * n // runs
+        span = hi - lo - run + 1
+        start = lo + mix32((r * 0x9E3779B9 + 0x632BE5AB) & 0xFFFFFFFF) % span
+        out.extend(range(start, start + run))
     return out
 
 
