@@ -95,6 +95,37 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const int l0 = j * kTabGroup, lg = min(kTabGroup, L - l0), R = lg * P;
   const bool full8 = lg == kTabGroup && (L & 7) == 0;
 
+  const int plo = P < 4 ? P : 4, phi = P - plo, nlo = 1 << plo, hw = nlo + (1 << phi);
+  const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P);
+  const int rowb = d * static_cast<int>(sizeof(T)) + 16;
+  double* qn = reinterpret_cast<double*>(sm + mp.qn);
+  double* zl = reinterpret_cast<double*>(sm + mp.z);
+  double* sg = reinterpret_cast<double*>(sm + mp.sg);
+  double* half = reinterpret_cast<double*>(sm + mp.half);
+  float* tl = reinterpret_cast<float*>(sm + mp.tl);
+
+  // W rows of the group (contiguous in HBM) and the G query rows:
+  // unconditional (clamped) loads, all in flight together.  They are issued
+  // before the scattered sample loads below, so waiting for them does not
+  // wait for those (loads complete in issue order for the wait counter).
+  const T* wsrc = W + (static_cast<long long>(h) * L * P + static_cast<long long>(l0) * P) * d;
+  // >= 1 and <= 4 * NT: at most 8 tables x 8 planes x 128 dims x 4 bytes / 16
+  const int nblk = R * (d / E);
+  u32x4 wv4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = u * NT + t;
+    wv4[u] = reinterpret_cast<const u32x4*>(wsrc)[e < nblk ? e : nblk - 1];
+  }
+  const T* qsrc = q + (static_cast<long long>(b) * a.Hq + h * G) * d;
+  constexpr int kQPer = 2;  // G * d <= 1024 = kQPer * NT
+  float qv[kQPer];
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = u * NT + t;
+    qv[u] = to_f32(qsrc[e < G * d ? e : G * d - 1]);
+  }
+
   // sampled keys' ids of this table group (8 bytes per key), loads issued now
   int n;
   const int S = sample_size(a, seq_lens, k_per_seq, b, n);
@@ -113,44 +144,24 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     }
   }
 
-  const int plo = P < 4 ? P : 4, phi = P - plo, nlo = 1 << plo, hw = nlo + (1 << phi);
-  const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P);
-  const int rowb = d * static_cast<int>(sizeof(T)) + 16;
-  double* qn = reinterpret_cast<double*>(sm + mp.qn);
-  double* zl = reinterpret_cast<double*>(sm + mp.z);
-  double* sg = reinterpret_cast<double*>(sm + mp.sg);
-  double* half = reinterpret_cast<double*>(sm + mp.half);
-  float* tl = reinterpret_cast<float*>(sm + mp.tl);
-
-  // W rows of the group (contiguous in HBM): unconditional (clamped) 16-byte
-  // loads, all in flight together
-  const T* wsrc = W + (static_cast<long long>(h) * L * P + static_cast<long long>(l0) * P) * d;
-  const int nblk = R * (d / E);  // >= 1
-  for (int i0 = 0; i0 < nblk; i0 += NT * 4) {
-    u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = i0 + u * NT + t;
-      v[u] = reinterpret_cast<const u32x4*>(wsrc)[e < nblk ? e : nblk - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = i0 + u * NT + t;
-      if (e < nblk) {
-        const int r = e / (d / E), cb = e % (d / E);
-        *reinterpret_cast<u32x4*>(sm + mp.wrows + r * rowb + cb * 16) = v[u];
-      }
+  for (int u = 0; u < 4; ++u) {
+    const int e = u * NT + t;
+    if (e < nblk) {
+      const int r = e / (d / E), cb = e % (d / E);
+      *reinterpret_cast<u32x4*>(sm + mp.wrows + r * rowb + cb * 16) = wv4[u];
     }
   }
+#pragma unroll
+  for (int u = 0; u < kQPer; ++u) {
+    const int e = u * NT + t;
+    if (e < G * d) qn[e] = static_cast<double>(qv[u]);
+  }
+  __syncthreads();
   // normalised queries
   for (int g = wave; g < G; g += NT / 64) {
-    const T* qr = q + (static_cast<long long>(b) * a.Hq + h * G + g) * d;
     double s2 = 0.0;
-    for (int c = lane; c < d; c += 64) {
-      const double v = to_f64(qr[c]);
-      qn[g * d + c] = v;
-      s2 += v * v;
-    }
+    for (int c = lane; c < d; c += 64) s2 += qn[g * d + c] * qn[g * d + c];
     for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
     const double nrm = sqrt(s2);
     for (int c = lane; c < d; c += 64) qn[g * d + c] = nrm > 0.0 ? qn[g * d + c] / nrm : 0.0;
