@@ -245,75 +245,89 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   }
 }
 
-// Merge the split states of one kv head's G query heads.  grid (B*Hkv).
-template <int D, int GMAX>
+// Merge the split states of one query head.  grid (B*Hq), 256 threads.
+// Thread t owns column block c = t % (D/4) (four output elements) of the
+// splits so, so + SP, ... (so = t / (D/4)); the (m, l) pairs and the partial
+// outputs are loaded together (one round trip), then weighted by
+// 2^(m_s - max m) and summed; the sum of weights times l is the denominator.
+template <int D>
 __global__ void __launch_bounds__(256)
-combine_kernel(int Hq, int Hkv, int nsplit, const float* __restrict__ part_o,
-               const float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NT = 256;
-  constexpr int C4 = D / 4;
-  __shared__ float wgt[GMAX][kMaxSplits];
-  __shared__ float accq[4][GMAX * D];
-  __shared__ float gM[GMAX], gL[GMAX];
-  const int G = Hq / Hkv;
-  const int bh = blockIdx.x, b = bh / Hkv, h = bh % Hkv;
+combine_kernel(int nsplit, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+               float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NT = 256, CW = D / 4, SP = NT / CW, NW = NT / 64;
+  constexpr int B8 = 8;  // partial-output loads per thread per batch
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[2][NW];
+  __shared__ u32x4 accs[SP][CW];
+  const long long qh = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const long long qb = static_cast<long long>(b) * Hq + h * G;
-  for (int g = wave; g < G; g += NT / 64) {
-    float M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_ml[((qb + g) * nsplit + s) * 2]);
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float Ls = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float ms = part_ml[((qb + g) * nsplit + s) * 2];
-      const float wv = (ms == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ms - M);
-      Ls += part_ml[((qb + g) * nsplit + s) * 2 + 1] * wv;
-      wgt[g][s] = wv;
-    }
-    for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
-    if (lane == 0) {
-      gM[g] = M;
-      gL[g] = Ls;
-    }
+  const int c = t % CW, so = t / CW;
+  const float* po = part_o + qh * nsplit * D;
+  // first batch of partial outputs and this thread's (m, l) pair, together
+  u32x4 ov[B8];
+#pragma unroll
+  for (int i = 0; i < B8; ++i) {
+    const int sp = so + i * SP;
+    ov[i] = reinterpret_cast<const u32x4*>(po)[(sp < nsplit ? sp : nsplit - 1) * CW + c];
   }
+  const float2 ml = t < nsplit ? reinterpret_cast<const float2*>(part_ml)[qh * nsplit + t]
+                               : make_float2(-INFINITY, 0.f);
+  // M = max m; weights; L = sum w * l
+  float M = ml.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if (lane == 0) red[0][wave] = M;
   __syncthreads();
-  // each thread: 4 output elements of one query head over a quarter of the splits
-  for (int i = t; i < 4 * GMAX * C4; i += NT) {
-    const int quarter = i / (GMAX * C4), gc = i % (GMAX * C4);
-    const int g = gc / C4, c4 = gc % C4;
-    if (g >= G) continue;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int sq = (nsplit + 3) / 4;
-    const int s_lo = quarter * sq, s_hi = min(nsplit, s_lo + sq);
-    for (int sb = s_lo; sb < s_hi; sb += 8) {  // eight independent loads in flight
-      float4 v[8];
+  M = red[0][0];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (sb + u < s_hi) v[u] = reinterpret_cast<const float4*>(part_o + ((qb + g) * nsplit + sb + u) * D)[c4];
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[0][w]);
+  const float wv = (ml.x == -INFINITY || M == -INFINITY) ? 0.f : exp2f(ml.x - M);
+  if (t < nsplit) wgt[t] = wv;
+  float Ls = wv * ml.y;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (sb + u >= s_hi) continue;
-        const float wv = wgt[g][sb + u];
-        acc.x += v[u].x * wv;
-        acc.y += v[u].y * wv;
-        acc.z += v[u].z * wv;
-        acc.w += v[u].w * wv;
+  for (int o = 32; o >= 1; o >>= 1) Ls += __shfl_xor(Ls, o, 64);
+  if (lane == 0) red[1][wave] = Ls;
+  __syncthreads();
+  Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) Ls += red[1][w];
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int i0 = 0; i0 < nsplit; i0 += B8 * SP) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int i = 0; i < B8; ++i) {
+        const int sp = so + i0 + i * SP;
+        ov[i] = reinterpret_cast<const u32x4*>(po)[(sp < nsplit ? sp : nsplit - 1) * CW + c];
       }
     }
-    float* dst = &accq[quarter][g * D + c4 * 4];
-    dst[0] = acc.x;
-    dst[1] = acc.y;
-    dst[2] = acc.z;
-    dst[3] = acc.w;
+#pragma unroll
+    for (int i = 0; i < B8; ++i) {
+      const int sp = so + i0 + i * SP;
+      if (sp < nsplit) {
+        const float w = wgt[sp];
+        a0 += w * __uint_as_float(ov[i].x);
+        a1 += w * __uint_as_float(ov[i].y);
+        a2 += w * __uint_as_float(ov[i].z);
+        a3 += w * __uint_as_float(ov[i].w);
+      }
+    }
   }
+  accs[so][c] = u32x4{__float_as_uint(a0), __float_as_uint(a1), __float_as_uint(a2), __float_as_uint(a3)};
   __syncthreads();
-  for (int i = t; i < G * D; i += NT) {
-    const int g = i / D, c = i % D;
-    const float Ls = gL[g];
-    const float o = accq[0][i] + accq[1][i] + accq[2][i] + accq[3][i];
-    out[(qb + g) * D + c] = Ls > 0.f ? o / Ls : 0.f;
-    if (c == 0 && lse != nullptr) lse[qb + g] = Ls > 0.f ? (gM[g] + log2f(Ls)) * kLn2F : -INFINITY;
+  if (t < CW) {
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+#pragma unroll
+    for (int k = 0; k < SP; ++k) {
+      const u32x4 v = accs[k][t];
+      r0 += __uint_as_float(v.x);
+      r1 += __uint_as_float(v.y);
+      r2 += __uint_as_float(v.z);
+      r3 += __uint_as_float(v.w);
+    }
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    reinterpret_cast<float4*>(out + qh * D)[t] = make_float4(r0 * inv, r1 * inv, r2 * inv, r3 * inv);
   }
+  if (t == 0 && lse != nullptr) lse[qh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2F : -INFINITY;
 }
 
 // Stand-alone top-k: one workgroup per (sequence, kv head) writes the row.
@@ -379,13 +393,8 @@ static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const 
 template <int D>
 static hipError_t launch_combine_t(const hst_shape& s, const FusedArgs& a, float* out, float* lse,
                                    hipStream_t st) {
-  const int G = s.Hq / s.Hkv;
-  dim3 grid(s.B * s.Hkv);
-  const int ns = a_nsplit(a);
-  if (G <= 1) hipLaunchKernelGGL((combine_kernel<D, 1>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
-  else if (G <= 2) hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
-  else if (G <= 4) hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
-  else hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(256), 0, st, s.Hq, s.Hkv, ns, a.part_o, a.part_ml, out, lse);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(s.B * s.Hq), dim3(256), 0, st, a_nsplit(a), a.part_o,
+                     a.part_ml, out, lse);
   return hipGetLastError();
 }
 

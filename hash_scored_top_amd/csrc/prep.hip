@@ -63,18 +63,18 @@ struct TabSmem {
   int wrows, qn, z, sg, half, tl, bytes;
 };
 
-// LDS map of one table group: W rows (padded by 16 bytes), q_hat [G][d],
-// z [G][8P], logistic pairs [G][2][P][8], half products [G][hw][8] (float64),
-// the group's float32 table [2^P][8].
+// LDS map of one table group: W rows (padded by 16 bytes), q [G][d] and the
+// query norms [G] (float64), z [G][8P] (float64, unnormalised), half
+// products [G][hw][8] (float64), the group's float32 table [2^P][8].
 __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P) {
   const int plo = P < 4 ? P : 4;
   const int hw = (1 << plo) + (1 << (P - plo));
   TabSmem m{};
   m.wrows = 0;
   m.qn = m.wrows + kTabGroup * P * (d * esize + 16);
-  m.z = m.qn + G * d * 8;
-  m.sg = m.z + G * kTabGroup * P * 8;
-  m.half = m.sg + G * 2 * P * kTabGroup * 8;
+  m.sg = m.qn + G * d * 8;  // the G query norms
+  m.z = m.sg + G * 8;
+  m.half = m.z + G * kTabGroup * P * 8;
   m.tl = m.half + G * hw * kTabGroup * 8;
   m.bytes = m.tl + (kTabGroup << P) * 4;
   return m;
@@ -100,7 +100,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const int rowb = d * static_cast<int>(sizeof(T)) + 16;
   double* qn = reinterpret_cast<double*>(sm + mp.qn);
   double* zl = reinterpret_cast<double*>(sm + mp.z);
-  double* sg = reinterpret_cast<double*>(sm + mp.sg);
+  double* nrm = reinterpret_cast<double*>(sm + mp.sg);
   double* half = reinterpret_cast<double*>(sm + mp.half);
   float* tl = reinterpret_cast<float*>(sm + mp.tl);
 
@@ -158,18 +158,11 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     if (e < G * d) qn[e] = static_cast<double>(qv[u]);
   }
   __syncthreads();
-  // normalised queries
-  for (int g = wave; g < G; g += NT / 64) {
-    double s2 = 0.0;
-    for (int c = lane; c < d; c += 64) s2 += qn[g * d + c] * qn[g * d + c];
-    for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
-    const double nrm = sqrt(s2);
-    for (int c = lane; c < d; c += 64) qn[g * d + c] = nrm > 0.0 ? qn[g * d + c] / nrm : 0.0;
-  }
-  __syncthreads();
 
-  // projections z[g][r], r = ll * P + p: four lanes per dot (interleaved
-  // 16-byte blocks of the row), each with its own partial sum
+  // projections of the raw queries z[g][r] = W_r . q_g, r = ll * P + p: four
+  // lanes per dot (interleaved 16-byte blocks of the row), each with its own
+  // partial sum; meanwhile waves g < G take the query norms (z / ||q|| is the
+  // projection of the normalised query)
   for (int pr0 = 0; pr0 < G * R * 4; pr0 += NT) {  // uniform trip count (shuffles below)
     const int pq = pr0 + t, pr = pq >> 2, part = pq & 3;
     double acc = 0.0;
@@ -193,26 +186,40 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     const double a2 = a1 + __shfl_xor(a1, 2, 64);
     if (pr < G * R && part == 0) zl[pr] = a2;  // zl[g * R + r]
   }
-  __syncthreads();
-  // logistic pairs: sg[((g*2 + bit)*P + p)*8 + ll]
-  for (int e = t; e < G * P * lg; e += NT) {
-    const int g = e / (P * lg), rem = e % (P * lg), p = rem / lg, ll = rem % lg;
-    const double x = 2.0 * zl[g * R + ll * P + p] * a.inv_tau;
-    sg[((g * 2 + 0) * P + p) * kTabGroup + ll] = 1.0 / (1.0 + exp(x));   // bit clear
-    sg[((g * 2 + 1) * P + p) * kTabGroup + ll] = 1.0 / (1.0 + exp(-x));  // bit set
+  for (int g = wave; g < G; g += NT / 64) {
+    double s2 = 0.0;
+    for (int c = lane; c < d; c += 64) s2 += qn[g * d + c] * qn[g * d + c];
+    for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
+    if (lane == 0) nrm[g] = sqrt(s2);
   }
   __syncthreads();
-  // half products: half[(g*hw + c)*8 + ll], c < nlo: low bits, else high bits
-  for (int e = t; e < G * hw * lg; e += NT) {
-    const int g = e / (hw * lg), rem = e % (hw * lg), c = rem / lg, ll = rem % lg;
-    double pr = 1.0;
-    if (c < nlo) {
-      for (int p = 0; p < plo; ++p) pr *= sg[((g * 2 + ((c >> p) & 1)) * P + p) * kTabGroup + ll];
-    } else {
-      const int ch = c - nlo;
-      for (int p = 0; p < phi; ++p) pr *= sg[((g * 2 + ((ch >> p) & 1)) * P + plo + p) * kTabGroup + ll];
+
+  // one thread per (query head g, table ll, half of the planes): the logistic
+  // pairs of its planes (one exp each: with e = exp(-|x|), sigma(|x|) =
+  // 1 / (1 + e) and sigma(-|x|) = e / (1 + e)), then the products over those
+  // planes for every bit pattern of the half: half[(g*hw + c)*8 + ll]
+  if (t < G * lg * 2) {
+    const int g = t / (lg * 2), rem = t % (lg * 2), ll = rem >> 1, hi = rem & 1;
+    const int p0 = hi ? plo : 0, m = hi ? phi : plo, c0 = hi ? nlo : 0;
+    const double nq = nrm[g];
+    double vals[16];
+    vals[0] = 1.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < m) {
+        const double x = nq > 0.0 ? 2.0 * (zl[g * R + ll * P + p0 + k] / nq) * a.inv_tau : 0.0;
+        const double e = exp(-fabs(x));
+        const double big = 1.0 / (1.0 + e), small = e * big;
+        const double set = x >= 0.0 ? big : small;    // sigma(x): bit set
+        const double clear = x >= 0.0 ? small : big;  // sigma(-x): bit clear
+#pragma unroll
+        for (int b = 0; b < (1 << k); ++b) {
+          vals[b | (1 << k)] = vals[b] * set;
+          vals[b] = vals[b] * clear;
+        }
+      }
     }
-    half[(g * hw + c) * kTabGroup + ll] = pr;
+    for (int b = 0; b < (1 << m); ++b) half[(g * hw + c0 + b) * kTabGroup + ll] = vals[b];
   }
   __syncthreads();
   // entries (bucket c, table l0 + ll), summed over the query heads in order;
