@@ -33,8 +33,10 @@ as is, bf16 by round-to-nearest-even from the float32 value.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -228,7 +230,8 @@ def storage_np_dtype(dtype: str):
     return np.float32 if dtype == "f32" else np.uint16
 
 
-def make_full(w: Workload, slabs: Optional[List[Tuple[int, int]]] = None) -> dict:
+def make_full(w: Workload, slabs: Optional[List[Tuple[int, int]]] = None,
+              workers: Optional[int] = None) -> dict:
     """Whole-batch arrays in the library layout.
 
     K, V: [B, Hkv, Nmax, d]; q: [B, Hq, d]; W: [Hkv, L*P, d] (soft-LSH) or
@@ -244,13 +247,27 @@ def make_full(w: Workload, slabs: Optional[List[Tuple[int, int]]] = None) -> dic
     needles = {}
     todo = slabs if slabs is not None else [(b, h) for b in range(w.B)
                                             for h in range(w.Hkv)]
-    for (b, h) in todo:
+
+    def fill(bh):
+        b, h = bh
         s = make_slab(w, b, h, int(lens[b]))
         n = int(lens[b])
         K[b, h, :n] = s["K"]
         V[b, h, :n] = s["V"]
         q[b, h * w.G:(h + 1) * w.G] = s["q"]
-        needles[(b, h)] = s["needle_pos"]
+        return bh, s["needle_pos"]
+
+    # every slab has its own seed and its own rows, so slabs can be drawn on
+    # worker threads (numpy's samplers release the GIL) with the same result
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1)
+    if workers > 1 and len(todo) > 1:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            for bh, pos in ex.map(fill, todo):
+                needles[bh] = pos
+    else:
+        for bh in todo:
+            needles[bh] = fill(bh)[1]
     out = {"K": K, "V": V, "q": q, "seq_lens": lens,
            "k_per_seq": w.k_per_seq(), "needles": needles}
     if w.scheme == "softlsh":
