@@ -124,7 +124,9 @@ hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K, const vo
                                  const void* W, int L, int P, int norm_dtype, uint8_t* ids,
                                  void* vnorm, void* stream) {
   HST_TRY(check_shape(shape));
-  HST_TRY(check_lp(L, P));
+  // hashing alone has no table-size limit: ids are bytes (P <= 8), at most 1024 tables
+  if (L < 1 || P < 1) return HST_ERR_INVALID_ARG;
+  if (P > 8 || L > 1024) return HST_ERR_UNSUPPORTED;
   HST_TRY(check_norm_dtype(norm_dtype));
   if (!ptr_ok(K) || !ptr_ok(V) || !ptr_ok(W) || !ptr_ok(ids) || !ptr_ok(vnorm))
     return HST_ERR_INVALID_ARG;

@@ -53,7 +53,7 @@ __device__ __forceinline__ int sample_size(const FusedArgs& a, const int32_t* se
 
 // Zeroes the head's threshold word, which the filtering scan publishes.
 __device__ __forceinline__ void reset_scan_state(const FusedArgs& a, int bh) {
-  if (a.sample != 0 && blockIdx.x == 0 && threadIdx.x == 0) a.heads[bh].thr_word = 0ull;
+  if (a.sample != 0 && blockIdx.y == 0 && threadIdx.x == 0) a.heads[bh].thr_word = 0ull;
 }
 
 // ---------------------------------------------------------------------------
@@ -89,7 +89,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   constexpr int E = 16 / static_cast<int>(sizeof(T));
   extern __shared__ __align__(16) unsigned char sm[];
   const int G = a.Hq / a.Hkv, d = a.d, L = a.L, P = a.P, nb = 1 << P;
-  const int bh = blockIdx.y, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.x;
+  const int bh = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   reset_scan_state(a, bh);
   const int l0 = j * kTabGroup, lg = min(kTabGroup, L - l0), R = lg * P;
@@ -296,7 +296,7 @@ prep_qcodes_kernel(const T* __restrict__ q, const T* __restrict__ R, const uint3
   constexpr int NT = kPrepNT;
   extern __shared__ __align__(16) unsigned char sm[];
   const int G = a.Hq / a.Hkv, d = a.d, ds = d + 1;
-  const int bh = blockIdx.y, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.x;
+  const int bh = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63;
   float* rl = reinterpret_cast<float*>(sm);
   float* ql = rl + 16 * ds;
@@ -356,7 +356,7 @@ template <typename KT>
 __global__ void __launch_bounds__(kPrepNT)
 prep_given_kernel(const KT* __restrict__ scores, const int32_t* __restrict__ seq_lens,
                   const int32_t* __restrict__ k_per_seq, FusedArgs a) {
-  const int bh = blockIdx.y, b = bh / a.Hkv;
+  const int bh = blockIdx.x, b = bh / a.Hkv;
   reset_scan_state(a, bh);
   int n;
   const int S = sample_size(a, seq_lens, k_per_seq, b, n);
@@ -378,7 +378,11 @@ hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* 
                             const uint8_t* ids, const void* vnorm, int norm_f16,
                             const int32_t* kps, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
-  dim3 grid((a.L + kTabGroup - 1) / kTabGroup, s.B * s.Hkv);
+  // x = (sequence, kv head): workgroups are handed to the XCDs round robin in
+  // linear order, so the parts of one head (B*Hkv apart) share an XCD and its
+  // L2 whenever B*Hkv is a multiple of 8, and the sampled id rows are fetched
+  // from HBM once per head
+  dim3 grid(s.B * s.Hkv, (a.L + kTabGroup - 1) / kTabGroup);
   if (s.kv_dtype == HST_F32) {
     auto kern = prep_tables_kernel<float>;
     const size_t smem = tab_smem(G, s.d, 4, a.P).bytes;
@@ -399,7 +403,7 @@ hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* 
 
 hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const void* q, const void* R,
                                const uint32_t* codes, const int32_t* kps, hipStream_t st) {
-  dim3 grid(8, s.B * s.Hkv);
+  dim3 grid(s.B * s.Hkv, 8);
   const size_t smem = qcodes_smem(s.Hq / s.Hkv, s.d);
   if (s.kv_dtype == HST_F32) {
     auto kern = prep_qcodes_kernel<float>;
@@ -419,7 +423,7 @@ hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const voi
 
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
                              const void* scores, const int32_t* kps, hipStream_t st) {
-  dim3 grid(1, s.B * s.Hkv);
+  dim3 grid(s.B * s.Hkv, 1);
   if (score_dtype == HST_F32)
     hipLaunchKernelGGL(prep_given_kernel<float>, grid, dim3(kPrepNT), 0, st,
                        static_cast<const float*>(scores), s.seq_lens, kps, a);

@@ -116,7 +116,8 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P,
  * The sign is that of the exact real dot product of the stored values (a
  * zero projection sets the bit).  vnorm[b][h][j] = ||V[b][h][j]||_2 rounded
  * to nearest-even in norm_dtype (F16 or F32).
- * Requires 1 <= P <= 8, 1 <= L <= 128, L * 2^P <= 16384.  No workspace.
+ * Requires 1 <= P <= 8, 1 <= L <= 1024.  No workspace.  Rows j >= N_b are
+ * not written.  Inputs must be finite.
  */
 hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K,
                                  const void* V, const void* W, int L, int P,

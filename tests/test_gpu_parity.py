@@ -96,6 +96,69 @@ def test_hash_binary_bit_exact():
                                           O.binary_codes(K64, f64(x["R"][h], w.kv_dtype)))
 
 
+def _cancel_case(rng, d, nplanes, n):
+    """bf16-exact planes and keys whose projections are often exactly zero or
+    a tiny residue of large cancelling terms (the float32 sum of such a
+    projection can have either sign)."""
+    h = d // 2
+
+    def bf(x):  # round to bf16 (values are chosen representable or close)
+        return WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+    W = bf(rng.standard_normal((nplanes, d)) * 2.0 ** rng.integers(-2, 3, (nplanes, 1)))
+    dup = rng.random(nplanes) < 0.5          # planes with w[c + d/2] = w[c]
+    W[dup, h:] = W[dup, :h]
+    big = dup & (rng.random(nplanes) < 0.5)  # large entries, one tiny one
+    W[big, :] = bf(np.sign(W[big, :]) * 2.0 ** 10)
+    W[big, h - 1] = W[big, d - 1] = 2.0 ** -6
+    K = bf(rng.standard_normal((n, d)))
+    kind = rng.integers(0, 5, n)
+    anti = kind >= 2                         # k[c + d/2] = -k[c]: zero on duplicated planes
+    K[anti, h:] = -K[anti, :h]
+    K[kind == 1] = 0.0
+    huge = kind == 3                         # large cancelling products
+    K[huge] = bf(np.sign(K[huge]) * 2.0 ** 10)
+    K[huge, h:] = -K[huge, :h]
+    pert = kind == 4                         # antisymmetric but one channel nudged by an ulp
+    K[pert, d - 1] = bf(K[pert, d - 1] * (1.0 + 2.0 ** -7))
+    return W.astype(np.float32), K.astype(np.float32)
+
+
+@pytest.mark.parametrize("d,L", [(128, 64), (128, 16), (128, 128), (64, 64), (64, 16)])
+def test_hash_mfma_signs_exact_under_cancellation(d, L):
+    hst = _hst()
+    rng = np.random.default_rng(1000 + d + L)
+    B, Hkv, N = 2, 2, 1500
+    lens = np.array([N, 977], dtype=np.int32)
+    Ws, Ks = [], np.zeros((B, Hkv, N, d), np.float32)
+    for h in range(Hkv):
+        Wh, _ = _cancel_case(rng, d, L * 8, 1)
+        Ws.append(Wh)
+    for b in range(B):
+        for h in range(Hkv):
+            Ks[b, h] = _cancel_case(np.random.default_rng(7 * b + h), d, L * 8, N)[1]
+            Ks[b, h, lens[b]:] = 0.0
+    W = np.stack(Ws)
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(DEV)
+    ids, _ = hst.hst_hash_keys_softlsh(to(Ks), to(Ks), to(W), L, 8, torch.float32,
+                                       seq_lens=torch.from_numpy(lens).to(DEV))
+    ids = ids.cpu().numpy()
+    codes = None
+    if L == 16 and d == 128:  # 128 planes: the same signs as a 128-bit code
+        codes = hst.hst_hash_keys_binary(to(Ks), to(W), seq_lens=torch.from_numpy(lens).to(DEV))
+        codes = codes.cpu().numpy().view(np.uint32)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hkv):
+            K64 = Ks[b, h, :n].astype(np.float64)
+            ref = O.hash_keys_softlsh(K64, W[h].astype(np.float64), L, 8)
+            np.testing.assert_array_equal(ids[b, h, :n], ref, err_msg=f"{(b, h)}")
+            assert not ids[b, h, n:].any()
+            if codes is not None:
+                np.testing.assert_array_equal(codes[b, h, :n],
+                                              O.binary_codes(K64, W[h].astype(np.float64)))
+
+
 def test_hash_sign_exact_under_cancellation():
     # fp32 keys whose projection is -1 exactly while a plain float sum gives 0
     hst = _hst()
