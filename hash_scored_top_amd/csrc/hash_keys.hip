@@ -34,6 +34,7 @@ namespace hst {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename Kern>
 static hipError_t set_lds_limit(Kern kern, size_t bytes) {
@@ -100,63 +101,76 @@ binary_codes_generic_kernel(const T* __restrict__ X, const T* __restrict__ R,
 
 // ---------------------------------------------------------------- matrix-core path
 
-constexpr int kSgnWaves = 8;    // waves per workgroup (2 per SIMD)
-constexpr int kSgnQueue = 64;   // projections awaiting the exact decision, per wave
+constexpr int kSgnTile = 64;   // keys per tile
+constexpr int kSgnExp = 16;    // float64 partials of an exact expansion (LDS, per lane)
 
 template <int D, int NBG>
-struct SignLds {
-  static constexpr int kRowU32 = D / 2 + 4;  // plane row: D bf16 + 16 B pad (conflict-free b128 reads)
-  static constexpr size_t kW = static_cast<size_t>(NBG) * kRowU32 * 4;
-  static constexpr size_t kBound = (NBG / 32) * 4;
-  static constexpr size_t kQueue = static_cast<size_t>(kSgnWaves) * kSgnQueue * 8;
-  static constexpr size_t kBytes = kW + kBound + kQueue;
+struct SignCfg {
+  static constexpr int kWaves = 8;
+  static constexpr int kNT = kWaves * 64;
+  static constexpr int kPS = NBG / 64;                     // 64-plane slices
+  static constexpr int kKG = kWaves / kPS;                 // key groups
+  static constexpr int kChunk = 256;                       // keys staged per step
+  static constexpr int kSub = kChunk / kSgnTile / kKG;     // 64-key tiles per wave per step
+  static constexpr int kS = D / 16;                        // MFMA steps along the channels
+  static constexpr int kPPR = D / 8;                       // 16-byte pieces per key row
+  static constexpr int kPieces = kChunk * kPPR / kNT;      // pieces per thread per step
+  static constexpr int kRowB = 2 * D + 16;                 // padded LDS row: conflict-free b128 reads
+  static constexpr size_t kBuf = static_cast<size_t>(kChunk) * kRowB + kChunk * 4;  // rows + norms
+  // plus, per wave, a list of the tiles holding uncertain signs (kpw / 64 + 1 words)
+  static size_t bytes(int kpw) {
+    return 2 * kBuf + static_cast<size_t>(kWaves) * (kpw / kSgnTile + 1) * 4;
+  }
 };
 
-// Exact decisions for the queued (key, plane) pairs, one per lane, and the
-// fix-up of the already stored words.
-template <int D, int NBG>
-__device__ __noinline__ void sign_queue_flush(const uint2* __restrict__ q, int count, int lane,
-                                              const uint32_t* wl, const bf16* __restrict__ Kh,
-                                              uint32_t* __restrict__ outw, int out_words,
-                                              int word0) {
-  // the words were written with plain stores by this wave: let them land first
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  if (lane < count) {
-    const uint2 it = q[lane];
-    const long long j = it.x;
-    const int plane = static_cast<int>(it.y);
-    const bf16* wrow = reinterpret_cast<const bf16*>(wl + plane * SignLds<D, NBG>::kRowU32);
-    const bool bit = dot_nonneg_exact(wrow, Kh + j * D, D);
-    uint32_t* word = outw + j * out_words + word0 + (plane >> 5);
-    const uint32_t m = 1u << (plane & 31);
-    if (bit)
-      atomicOr(word, m);
-    else
-      atomicAnd(word, ~m);
+// Exact sign of W[plane] . K[j] (bf16 rows of D values, 16-byte aligned):
+// both rows are loaded at once, the float64 sum decides unless it lies
+// within its rounding band, where the exact expansion takes over.
+template <int D>
+__device__ __forceinline__ bool exact_sign_rows(const bf16* __restrict__ wrow,
+                                                const bf16* __restrict__ krow, double* h) {
+  u32x4 wv[D / 8], kv[D / 8];
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    wv[i] = reinterpret_cast<const u32x4*>(wrow)[i];
+    kv[i] = reinterpret_cast<const u32x4*>(krow)[i];
   }
+  double s = 0.0, sa = 0.0;
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double p0 = static_cast<double>(bf16_lo(wv[i][e])) * bf16_lo(kv[i][e]);
+      const double p1 = static_cast<double>(bf16_hi(wv[i][e])) * bf16_hi(kv[i][e]);
+      s += p0;
+      s += p1;
+      sa += fabs(p0) + fabs(p1);
+    }
+  if (fabs(s) > 2.0 * D * 0x1p-53 * sa) return s >= 0.0;
+  return expansion_dot_nonneg_in(wrow, krow, D, h, kSgnExp);
 }
 
 // Workgroup = 8 waves over keys [j0, j0 + kpw) of one (sequence, kv head) and
-// planes [pg * NBG, (pg + 1) * NBG).  The planes live in LDS (MFMA A operand,
-// 32 planes x 16 channels per step); each wave takes 64-key tiles whose
-// channels sit in registers (B operand, loaded straight from HBM; the other
-// waves of the SIMD compute while one waits for its tile).  Result of a 32x32 block: lane
-// (j = lane % 32, half = lane / 32) holds key j, planes 8(r/4) + 4 half + r%4
-// for r < 16; their sign bits are packed with alignbit and merged across the
-// two halves into the 32-bit output word of that key and plane block.
+// the planes [pg * NBG, (pg + 1) * NBG).  Wave w takes the 64-plane slice
+// w % (NBG / 64), kept in registers as the MFMA A operand (plane 32 rb +
+// lane % 32, channels 16 s + 8 (lane / 32) at step s), and key group
+// w / (NBG / 64).  The workgroup streams 256-key steps: coalesced 16-byte
+// loads of the next step run in registers during the current step's compute,
+// then go to one of two padded LDS buffers (with the key norms), from which
+// every wave reads the B operands of its 64-key tiles.  Result of a 32x32
+// block: lane (j = lane % 32, half = lane / 32) holds key j, planes
+// 8(r/4) + 4 half + r%4 for r < 16; their sign bits are packed with alignbit
+// and merged across the two halves into the 32-bit output word of that key
+// and plane block.
 template <int D, int NBG>
-__global__ void __launch_bounds__(kSgnWaves * 64)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 hash_signs_mfma_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Wall,
                        const int32_t* __restrict__ seq_lens, int Hkv, int Nmax, int nplanes,
                        int kpw, uint32_t* __restrict__ out) {
-  using LD = SignLds<D, NBG>;
-  constexpr int S = D / 16;       // MFMA steps along the channels
-  constexpr int RB = NBG / 32;    // 32-plane blocks
-  constexpr int ROW = LD::kRowU32;
-  extern __shared__ __align__(16) uint32_t sgn_lds[];
-  uint32_t* wl = sgn_lds;
-  float* bound = reinterpret_cast<float*>(sgn_lds + LD::kW / 4);
-  uint2* queue = reinterpret_cast<uint2*>(sgn_lds + (LD::kW + LD::kBound) / 4);
+  using C = SignCfg<D, NBG>;
+  constexpr int S = C::kS, NP = C::kPieces, PPR = C::kPPR, ROWB = C::kRowB;
+  constexpr int NT = C::kNT, CH = C::kChunk;
+  extern __shared__ __align__(16) unsigned char sgn_lds[];
 
   const int bh = blockIdx.x, b = bh / Hkv, h = bh % Hkv;
   const int pg = blockIdx.z;
@@ -165,159 +179,299 @@ hash_signs_mfma_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Wall
   if (j0 >= n) return;
   const long long jend = (j0 + kpw < n) ? j0 + kpw : n;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, jl = lane & 31, hf = lane >> 5;
+  const int ps = wave % C::kPS, kg = wave / C::kPS;  // plane slice, key group
+  const int ntile = static_cast<int>((jend - j0 + kSgnTile - 1) / kSgnTile);
+  const int nchunk = static_cast<int>((jend - j0 + CH - 1) / CH);
 
-  // planes of this group -> LDS
-  {
-    const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(
-        Wall + (static_cast<long long>(h) * nplanes + static_cast<long long>(pg) * NBG) * D);
-    constexpr int CPR = D / 8;  // 16-byte pieces per plane row
-    for (int p = tid; p < NBG * CPR; p += kSgnWaves * 64) {
-      const int row = p / CPR, c = p % CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(wsrc + row * (D / 2) + c * 4);
-      *reinterpret_cast<u32x4*>(wl + row * ROW + c * 4) = v;
-    }
+  // this wave's planes (A operands) and the error-bound factor per 32-plane block
+  const bf16* Wg = Wall + (static_cast<long long>(h) * nplanes + static_cast<long long>(pg) * NBG) * D;
+  u32x4 wa[2][S];
+  float bnd[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(Wg + static_cast<long long>(ps * 64 + rb * 32 + jl) * D) +
+        hf * 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) wa[rb][s] = *reinterpret_cast<const u32x4*>(src + s * 8);
   }
-  __syncthreads();
-  // bound factor per 32-plane block: d 2^-26 (1 + 2^-8) max ||w||
-  for (int rb = wave; rb < RB; rb += kSgnWaves) {
-    const uint32_t* row = wl + (rb * 32 + jl) * ROW + hf * (D / 4);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
     float s2 = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
-      const float lo = bf16_lo(row[c]), hi = bf16_hi(row[c]);
-      s2 = fmaf(lo, lo, s2);
-      s2 = fmaf(hi, hi, s2);
-    }
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(wa[rb][s][e]), hi = bf16_hi(wa[rb][s][e]);
+        s2 = fmaf(lo, lo, s2);
+        s2 = fmaf(hi, hi, s2);
+      }
     s2 += __shfl_xor(s2, 32);
     for (int m = 16; m >= 1; m >>= 1) s2 = fmaxf(s2, __shfl_xor(s2, m));
-    if (lane == 0) bound[rb] = sqrtf(s2) * (static_cast<float>(D) * 0x1p-26f * (1.f + 0x1p-8f));
+    // (d/16) MFMA steps x 2 ulps each, norms inflated by 2^-8
+    bnd[rb] = sqrtf(s2) * (static_cast<float>(D) * 0x1p-26f * (1.f + 0x1p-8f));
   }
-  __syncthreads();
 
   const bf16* Kh = K + static_cast<long long>(bh) * Nmax * D;
   const uint32_t* Kw = reinterpret_cast<const uint32_t*>(Kh);
   const int out_words = nplanes / 32;
   uint32_t* outw = out + static_cast<long long>(bh) * Nmax * out_words;
-  const int word0 = pg * RB;
-  uint2* q = queue + wave * kSgnQueue;
-  int qn = 0;  // wave-uniform
+  const int word0 = pg * (NBG / 32);
+  // output rows of this workgroup behind a buffer resource: a store whose
+  // offset is out of range is dropped, so rows past the sequence end need no
+  // branch around the store
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      outw + j0 * out_words, 0, static_cast<int>((jend - j0) * out_words * 4), 0x00020000);
+  // tiles of this wave with uncertain signs: entry = tile | block mask << 24
+  uint32_t* flist = reinterpret_cast<uint32_t*>(sgn_lds + 2 * C::kBuf) + wave * (kpw / kSgnTile + 1);
+  int nfl = 0;  // wave-uniform
 
-  const int ntile = static_cast<int>((jend - j0 + 63) / 64);
-  u32x4 bop[2][S];
-  auto load_tile = [&](int t, u32x4(&dst)[2][S]) {
+  auto gload = [&](int ch, u32x4(&r)[NP]) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      long long j = j0 + t * 64 + cb * 32 + jl;
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * NT, row = p / PPR, c = p % PPR;
+      long long j = j0 + static_cast<long long>(ch) * CH + row;
       j = j < jend ? j : jend - 1;
-      const uint32_t* src = Kw + j * (D / 2) + hf * 4;
-#pragma unroll
-      for (int s = 0; s < S; ++s) dst[cb][s] = *reinterpret_cast<const u32x4*>(src + s * 8);
+      r[i] = *reinterpret_cast<const u32x4*>(Kw + j * (D / 2) + c * 4);
     }
   };
-  for (int t = wave; t < ntile; t += kSgnWaves) {
-    load_tile(t, bop);
-    // the plane rows are re-read from LDS per tile: an opaque offset keeps the
-    // compiler from hoisting them into registers across the tile loop
-    int aoff = (jl * ROW) + hf * 4;
-    asm volatile("" : "+v"(aoff));
-    // upper estimates of the key norms (both halves of the channels)
-    float nk[2];
+  // tile -> LDS buffer, with the key norms (float32 upper estimates before
+  // the 2^-8 inflation folded into the bound factor)
+  auto stage = [&](int buf, const u32x4(&r)[NP]) {
+    unsigned char* tb = sgn_lds + buf * C::kBuf;
+    float* nrm = reinterpret_cast<float*>(tb + CH * ROWB);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * NT, row = p / PPR, c = p % PPR;
+      *reinterpret_cast<u32x4*>(tb + row * ROWB + c * 16) = r[i];
       float s2 = 0.f;
 #pragma unroll
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2_t v = __builtin_bit_cast(bf16x2_t, bop[cb][s][e]);
-          s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
-        }
-      s2 += __shfl_xor(s2, 32);
-      nk[cb] = sqrtf(s2);
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t v = __builtin_bit_cast(bf16x2_t, r[i][e]);
+        s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
+      }
+      s2 = dpp_group_sum<PPR>(s2);
+      if (c == 0) nrm[row] = sqrtf(s2);
     }
-    long long jk[2];
-    jk[0] = j0 + t * 64 + jl;
-    jk[1] = jk[0] + 32;
-#pragma unroll 2
-    for (int rb = 0; rb < RB; ++rb) {
-      f32x16 acc0 = {}, acc1 = {};
-      const uint32_t* arow = wl + rb * 32 * ROW + aoff;
+  };
+  auto mfma_block = [&](const u32x4(&a)[S], const u32x4(&bb)[S]) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[s]),
+                                                    __builtin_bit_cast(bf16x8_t, bb[s]), acc, 0,
+                                                    0, 0);
+    return acc;
+  };
+  // signs of one 32x32 block -> the 32-bit word of (key, plane block), and
+  // whether some sign lies inside the error band
+  auto pack = [&](const f32x16& acc, float thr, uint32_t& word) {
+    float mn = fabsf(acc[0]);
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      v = __builtin_amdgcn_alignbit(v, __float_as_uint(acc[r]), 31);  // bit r = sign of acc[r]
+      if (r > 0) mn = fminf(mn, fabsf(acc[r]));
+    }
+    v = ~v & 0xffffu;  // 1 = non-negative
+    v = (v | (v << 8)) & 0x00ff00ffu;
+    v = (v | (v << 4)) & 0x0f0f0f0fu;
+    v <<= 4 * hf;
+    const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    word = sw[0] | sw[1];  // both halves' planes
+    return !(mn > thr);
+  };
+  // One step = this wave's kSub tiles of the buffer, 4 blocks (column block
+  // cb, plane block rb) each, software-pipelined: the MFMAs of block k+1 are
+  // issued before block k is packed, so the matrix cores and the vector units
+  // work side by side.  Tiles past the end are computed and masked out.
+  auto compute_step = [&](int c, int buf) {
+    constexpr int NBLK = C::kSub * 4;
+    const unsigned char* base = sgn_lds + buf * C::kBuf;
+    const float* nrm = reinterpret_cast<const float*>(base + CH * ROWB);
+    u32x4 bb[C::kSub * 2][S];
+    f32x16 acc[NBLK];
+    uint32_t word[2][2] = {{0u, 0u}, {0u, 0u}};
+    uint32_t flags = 0;  // bit 2 rb + cb of the current tile
+    auto ld = [&](int i, int cb) {
+      const int row = (kg * C::kSub + i) * kSgnTile + cb * 32 + jl;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        bb[i * 2 + cb][s] = *reinterpret_cast<const u32x4*>(base + row * ROWB + s * 32 + hf * 16);
+    };
+    ld(0, 0);
+    acc[0] = mfma_block(wa[0], bb[0]);
+#pragma unroll
+    for (int k = 0; k < NBLK; ++k) {
+      const int i = k >> 2, cb = (k >> 1) & 1, rb = k & 1;
+      if (k + 1 < NBLK) {
+        if (((k + 1) & 1) == 0) ld((k + 1) >> 2, ((k + 1) >> 1) & 1);
+        acc[k + 1] = mfma_block(wa[(k + 1) & 1], bb[(k + 1) >> 1]);
+      }
+      const int t = c * (CH / kSgnTile) + kg * C::kSub + i;  // tile of the workgroup
+      const long long j = j0 + static_cast<long long>(t) * kSgnTile + cb * 32 + jl;
+      const float nk = nrm[(kg * C::kSub + i) * kSgnTile + cb * 32 + jl];
+      const bool unsure = pack(acc[k], fmaf(nk, bnd[rb], 0x1p-100f), word[rb][cb]);
+      flags |= (unsure && j < jend) ? (1u << (2 * rb + cb)) : 0u;
+      if (rb == 1 && cb == 1) {
+        // lane (jl, hf) stores the two words of key hf * 32 + jl
+        const long long jb = j0 + static_cast<long long>(t) * kSgnTile;
+        const bool mine = jb + hf * 32 + jl < jend;
+        const int orow = t * kSgnTile + hf * 32 + jl;
+        u32x2 w2;
+        w2[0] = hf ? word[0][1] : word[0][0];
+        w2[1] = hf ? word[1][1] : word[1][0];
+        __builtin_amdgcn_raw_buffer_store_b64(
+            w2, orsrc,
+            mine ? static_cast<uint32_t>((orow * out_words + word0 + ps * 2) * 4) : 0x80000000u, 0,
+            0);
+        // note the tile if a block holds an uncertain sign (the slot is
+        // written every time and kept only then: no branch)
+        const uint32_t fl = (__ballot(flags & 1u) ? 1u : 0u) | (__ballot(flags & 2u) ? 2u : 0u) |
+                            (__ballot(flags & 4u) ? 4u : 0u) | (__ballot(flags & 8u) ? 8u : 0u);
+        flist[nfl] = static_cast<uint32_t>(t) | (fl << 24);
+        nfl += fl != 0u ? 1 : 0;
+        flags = 0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // step c: copy step c+1 (loaded during step c-1) to the other buffer, load
+  // step c+2, then compute step c; one barrier per step
+  u32x4 rg[NP];
+  gload(0, rg);
+  stage(0, rg);
+  if (1 < nchunk) gload(1, rg);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    if (c + 1 < nchunk) {
+      stage((c + 1) & 1, rg);
+      if (c + 2 < nchunk) gload(c + 2, rg);
+    }
+    compute_step(c, c & 1);
+    __syncthreads();
+  }
+
+  // Exact decisions for the noted tiles.  A: recompute their flagged blocks
+  // from HBM and list the uncertain (key, plane) pairs in the step buffers
+  // (free once every wave has left the loop); B: settle the listed pairs one
+  // per lane and fix their bits.
+  if (nfl == 0) return;
+  // per wave: the lanes' expansion partials, then the listed pairs
+  constexpr int kRegion = static_cast<int>(2 * C::kBuf / C::kWaves) / 8 * 8;
+  constexpr int kCap = (kRegion - 64 * kSgnExp * 8) / 8;
+  static_assert(kCap >= 64, "room for a wave of pairs");
+  double* hx = reinterpret_cast<double*>(sgn_lds + wave * kRegion) + lane * kSgnExp;
+  uint2* items = reinterpret_cast<uint2*>(sgn_lds + wave * kRegion + 64 * kSgnExp * 8);
+  int nit = 0;  // wave-uniform
+  // the planes again (L2-resident): the main loop's copy is dead by now,
+  // which keeps this cold path clear of register spills
+  u32x4 wc[2][S];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(Wg + static_cast<long long>(ps * 64 + rb * 32 + jl) * D) +
+        hf * 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) wc[rb][s] = *reinterpret_cast<const u32x4*>(src + s * 8);
+  }
+  auto settle = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the words have landed
+    for (int i = lane; i < nit; i += 64) {
+      const uint2 it = items[i];
+      const long long j = it.x;
+      const int plane = static_cast<int>(it.y);
+      const bool bit = exact_sign_rows<D>(Wg + static_cast<long long>(plane) * D, Kh + j * D, hx);
+      uint32_t* word = outw + j * out_words + word0 + (plane >> 5);
+      const uint32_t m = 1u << (plane & 31);
+      if (bit)
+        atomicOr(word, m);
+      else
+        atomicAnd(word, ~m);
+    }
+    nit = 0;
+  };
+  for (int e = 0; e < nfl; ++e) {
+    const uint32_t ent = flist[e];
+    const int t = static_cast<int>(ent & 0xffffffu);
+    const uint32_t fl = ent >> 24;
+    const long long jb = j0 + static_cast<long long>(t) * kSgnTile;
+#pragma unroll 1
+    for (int cb = 0; cb < 2; ++cb) {
+      if ((fl & (5u << cb)) == 0u) continue;
+      const long long j = jb + cb * 32 + jl;
+      const long long jc = j < jend ? j : jend - 1;
+      u32x4 bk[S];
+      float s2 = 0.f;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + s * 8);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bop[0][s]),
-                                                       acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bop[1][s]),
-                                                       acc1, 0, 0, 0);
+        bk[s] = *reinterpret_cast<const u32x4*>(Kw + jc * (D / 2) + s * 8 + hf * 4);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const bf16x2_t v = __builtin_bit_cast(bf16x2_t, bk[s][e2]);
+          s2 = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2, false);
+        }
       }
-      const float bnd = bound[rb];
+      s2 += __shfl_xor(s2, 32);
+      const float nk = sqrtf(s2);
+      uint32_t fm = 0;  // bit 16 rb + r: uncertain (shifted in from the top bit down)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const f32x16& acc = cb == 0 ? acc0 : acc1;
-        const float thr = fmaf(nk[cb], bnd, 0x1p-100f);
-        float mn = fabsf(acc[0]);
-        uint32_t v = 0;
+      for (int rb = 1; rb >= 0; --rb) {
+        const f32x16 acc = mfma_block(wc[rb], bk);
+        const float thr = fmaf(nk, bnd[rb], 0x1p-100f);
 #pragma unroll
-        for (int r = 15; r >= 0; --r) {
-          v = __builtin_amdgcn_alignbit(v, __float_as_uint(acc[r]), 31);  // bit r = sign of acc[r]
-          if (r > 0) mn = fminf(mn, fabsf(acc[r]));
+        for (int r = 15; r >= 0; --r) fm = (fm << 1) | (!(fabsf(acc[r]) > thr) ? 1u : 0u);
+      }
+      if (!(j < jend)) fm = 0u;
+      // append this lane's pairs, one per lane and round (wave-uniform count)
+      while (true) {
+        const bool f = fm != 0u;
+        const unsigned long long m = __ballot(f);
+        if (m == 0ull) break;
+        if (nit + __popcll(m) > kCap) settle();
+        if (f) {
+          const int i = __builtin_ctz(fm);
+          fm &= fm - 1u;
+          const int pos = nit + __builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(m >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+          const int rb = i >> 4, r = i & 15;
+          items[pos] = make_uint2(static_cast<uint32_t>(j),
+                                  static_cast<uint32_t>(ps * 64 + rb * 32 + 8 * (r >> 2) +
+                                                        4 * hf + (r & 3)));
         }
-        v = ~v & 0xffffu;  // 1 = non-negative
-        v = (v | (v << 8)) & 0x00ff00ffu;
-        v = (v | (v << 4)) & 0x0f0f0f0fu;
-        v <<= 4 * hf;
-        v |= __shfl_xor(v, 32);
-        const long long j = jk[cb];
-        if (hf == 0 && j < jend) outw[j * out_words + word0 + rb] = v;
-        // rare: some sign inside the error band
-        if (__ballot(!(mn > thr) && j < jend) != 0ull) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool f = !(fabsf(acc[r]) > thr) && j < jend;
-            const unsigned long long m = __ballot(f);
-            if (m == 0ull) continue;
-            const int cnt = __popcll(m);
-            if (qn + cnt > kSgnQueue) {
-              sign_queue_flush<D, NBG>(q, qn, lane, wl, Kh, outw, out_words, word0);
-              qn = 0;
-            }
-            if (f) {
-              const int pos = qn + __builtin_amdgcn_mbcnt_hi(
-                                       static_cast<uint32_t>(m >> 32),
-                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-              q[pos] = make_uint2(static_cast<uint32_t>(j),
-                                  static_cast<uint32_t>(rb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)));
-            }
-            qn += cnt;
-          }
-        }
+        nit += __popcll(m);
       }
     }
   }
-  if (qn > 0) sign_queue_flush<D, NBG>(q, qn, lane, wl, Kh, outw, out_words, word0);
+  settle();
 }
 
 template <int D, int NBG>
 static hipError_t launch_signs_mfma(const hst_shape& s, const void* K, const void* W, int nplanes,
                                     void* out, hipStream_t st) {
+  using C = SignCfg<D, NBG>;
   auto kern = hash_signs_mfma_kernel<D, NBG>;
-  constexpr size_t smem = SignLds<D, NBG>::kBytes;
-  hipError_t e = set_lds_limit(kern, smem);
-  if (e != hipSuccess) return e;
   const long long BH = static_cast<long long>(s.B) * s.Hkv;
-  // about 256 workgroups (one per CU), 512..16384 keys each
-  long long kpw = (BH * s.Nmax + 255) / 256;
-  kpw = (kpw + 511) / 512 * 512;
-  kpw = kpw < 512 ? 512 : (kpw > 16384 ? 16384 : kpw);
+  // one workgroup per CU at a time (the two step buffers fill most of the LDS):
+  // about 256 workgroups over all keys and plane groups, whole 256-key steps
+  const long long wgs = 256;
+  long long kpw = (BH * s.Nmax * (nplanes / NBG) + wgs - 1) / wgs;
+  kpw = (kpw + 255) / 256 * 256;
+  kpw = kpw < 256 ? 256 : (kpw > 16384 ? 16384 : kpw);
   while ((s.Nmax + kpw - 1) / kpw > 65535) kpw *= 2;
   const long long gy = (s.Nmax + kpw - 1) / kpw;
+  const size_t smem = C::bytes(static_cast<int>(kpw));
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
+  hipError_t e = set_lds_limit(kern, smem);
+  if (e != hipSuccess) return e;
   // x = (sequence, kv head): workgroups are handed to the XCDs round robin in
   // linear order, so one head's workgroups (B*Hkv apart) share an XCD and its
   // L2 copy of the planes whenever B*Hkv is a multiple of 8
   dim3 grid(static_cast<unsigned>(BH), static_cast<unsigned>(gy),
             static_cast<unsigned>(nplanes / NBG));
-  hipLaunchKernelGGL(kern, grid, dim3(kSgnWaves * 64), smem, st, static_cast<const bf16*>(K),
+  hipLaunchKernelGGL(kern, grid, dim3(C::kNT), smem, st, static_cast<const bf16*>(K),
                      static_cast<const bf16*>(W), s.seq_lens, s.Hkv, s.Nmax, nplanes,
                      static_cast<int>(kpw), static_cast<uint32_t*>(out));
   return hipGetLastError();

@@ -29,6 +29,23 @@ __device__ __forceinline__ double to_f64(bf16 x) { return static_cast<double>(to
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Sum over each aligned group of W = 16 or 8 lanes, left in every lane
+// of the group: DPP quad permutes and row mirrors, no LDS traffic.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+  static_assert(W == 8 || W == 16, "group of 8 or 16 lanes");
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1,
+                                                             0xf, 0xf, false));  // quad [1,0,3,2]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E,
+                                                             0xf, 0xf, false));  // quad [2,3,0,1]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141,
+                                                             0xf, 0xf, false));  // row half mirror
+  if (W == 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140,
+                                                               0xf, 0xf, false));  // row mirror
+  return v;
+}
+
 // Context length of sequence b.
 __device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int nmax) {
   if (seq_lens == nullptr) return nmax;
@@ -39,11 +56,13 @@ __device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int nmax)
 // Sign of a sum of float64 values, exactly: Shewchuk's growing expansion
 // ("Adaptive precision floating-point arithmetic", 1997) keeps the running
 // sum as non-overlapping partials, so the sign of the total is the sign of
-// the largest non-zero partial.  Returns true when the sum is >= 0.
+// the largest non-zero partial.  Returns true when the sum is >= 0.  h holds
+// up to hcap partials (products of stored bf16 / float32 values span at most
+// about 600 bits, i.e. a dozen non-overlapping float64 partials).
 template <typename T>
-__device__ __noinline__ bool expansion_dot_nonneg(const T* __restrict__ a,
-                                                  const T* __restrict__ b, int n) {
-  double h[48];
+__device__ __forceinline__ bool expansion_dot_nonneg_in(const T* __restrict__ a,
+                                                     const T* __restrict__ b, int n,
+                                                     double* h, int hcap) {
   int nh = 0;
   for (int c = 0; c < n; ++c) {
     double x = to_f64(a[c]) * to_f64(b[c]);  // exact: at most 48 significant bits
@@ -56,12 +75,19 @@ __device__ __noinline__ bool expansion_dot_nonneg(const T* __restrict__ a,
       if (lo != 0.0) h[k++] = lo;
       x = hi;
     }
-    if (k < 48) h[k++] = x;
+    if (k < hcap) h[k++] = x;
     nh = k;
   }
   for (int i = nh - 1; i >= 0; --i)
     if (h[i] != 0.0) return h[i] > 0.0;
   return true;
+}
+
+template <typename T>
+__device__ __noinline__ bool expansion_dot_nonneg(const T* __restrict__ a,
+                                                  const T* __restrict__ b, int n) {
+  double h[48];
+  return expansion_dot_nonneg_in(a, b, n, h, 48);
 }
 
 // [ a . b >= 0 ] for the exact real dot product of stored float32/bf16
