@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak (prefill projection)
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode tokens/s and % of HBM roofline for hash score+top-k+sparse attn"
 
@@ -201,23 +202,42 @@ def main():
     kp = torch.from_numpy(ks).to(dev) if ragged else None
     stream = torch.cuda.current_stream(dev)
 
-    # prefill metadata, timed separately
+    # prefill metadata (once per key), timed separately: outputs allocated
+    # once, the library call alone inside the events
+    tot_keys = sum(int(n) for n in lens) * w.Hkv
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    pre_reps = 10
     if w.scheme == "softlsh":
         Wp = to_dev(x["W"], w.kv_dtype, dev)
         nd = norm_torch_dtype(w.norm_dtype)
-        hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd, seq_lens=sl)
-        ev[0].record(stream)
         ids, vn = hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd, seq_lens=sl)
-        ev[1].record(stream)
+        pre = lambda: hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd, seq_lens=sl, ids=ids,
+                                                vnorm=vn)
+        planes = w.L * w.P
+        pre_bytes = tot_keys * (2 * w.d * K.element_size() + w.L + vn.element_size())
     else:
         Rp = to_dev(x["R"], w.kv_dtype, dev)
-        hst.hst_hash_keys_binary(K, Rp, seq_lens=sl)
-        ev[0].record(stream)
         codes = hst.hst_hash_keys_binary(K, Rp, seq_lens=sl)
-        ev[1].record(stream)
+        pre = lambda: hst.hst_hash_keys_binary(K, Rp, seq_lens=sl, codes=codes)
+        planes = w.code_bits
+        pre_bytes = tot_keys * (w.d * K.element_size() + w.code_bits // 8)
+    pre()
     torch.cuda.synchronize()
-    prefill_ms = ev[0].elapsed_time(ev[1])
+    ev[0].record(stream)
+    for _ in range(pre_reps):
+        pre()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    prefill_us = ev[0].elapsed_time(ev[1]) * 1e3 / pre_reps
+    pre_flops = 2.0 * tot_keys * planes * w.d
+    prefill = {"us": prefill_us, "keys": tot_keys, "planes": planes,
+               "tflops": pre_flops / (prefill_us * 1e-6) / 1e12,
+               "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+               "mfma_frac": pre_flops / (prefill_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+               "hbm_bytes": pre_bytes,
+               "hbm_frac": pre_bytes / (prefill_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    log(f"prefill hash {prefill_us:.1f} us ({prefill['tflops']:.0f} TFLOP/s, "
+        f"{pre_bytes / (prefill_us * 1e-6) / 1e9:.0f} GB/s)")
 
     meta_b, gath_b, qo_b = alg_bytes(w, lens, ks)
     step_bytes = meta_b + gath_b + qo_b
@@ -284,7 +304,6 @@ def main():
 
     # dominant kernel (the score scan: every key's metadata once), timed alone
     # with events on the stream it is launched on
-    tot_keys = sum(int(n) for n in lens) * w.Hkv
     if w.scheme == "softlsh":
         f16 = "true" if w.norm_dtype == "f16" else "false"
         kname = f"scan_softlsh_kernel<{w.L // 16}, 2, false, {f16}>"  # scores only, no candidate filter
@@ -343,7 +362,7 @@ def main():
                  "hbm_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
                  "p10_us": float(np.percentile(per, 10)), "p50_us": float(np.percentile(per, 50)),
                  "p90_us": float(np.percentile(per, 90)), "rotated_copies": R},
-        "prefill_hash_us": prefill_ms * 1e3,
+        "prefill": prefill,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -139,23 +139,35 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
 # --------------------------------------------------------------------- entry points
 
 def hst_hash_keys_softlsh(K, V, W, L: int, P: int, norm_dtype=torch.float16,
-                          seq_lens=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Bucket ids [B,Hkv,Nmax,L] uint8 and value norms [B,Hkv,Nmax]."""
+                          seq_lens=None, ids=None, vnorm=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Bucket ids [B,Hkv,Nmax,L] uint8 and value norms [B,Hkv,Nmax].
+
+    ``ids`` / ``vnorm`` may be passed in (rows past N_b are left as they are);
+    new ones start zeroed."""
     B, Hkv, Nmax, d = K.shape
     shape = make_shape(K, Hkv, seq_lens)
-    ids = torch.zeros((B, Hkv, Nmax, L), dtype=torch.uint8, device=K.device)
-    vnorm = torch.zeros((B, Hkv, Nmax), dtype=norm_dtype, device=K.device)
+    if ids is None:
+        ids = torch.zeros((B, Hkv, Nmax, L), dtype=torch.uint8, device=K.device)
+    if vnorm is None:
+        vnorm = torch.zeros((B, Hkv, Nmax), dtype=norm_dtype, device=K.device)
+    if ids.shape != (B, Hkv, Nmax, L) or ids.dtype != torch.uint8 or vnorm.dtype != norm_dtype:
+        raise ValueError("ids / vnorm do not match the shape and dtypes")
     _check(_C.hst_hash_keys_softlsh(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(W), L, P,
                                     _norm_code(norm_dtype), _ptr(ids), _ptr(vnorm),
                                     _stream(K.device)), "hst_hash_keys_softlsh")
     return ids, vnorm
 
 
-def hst_hash_keys_binary(K, R, code_bits: int = 128, seq_lens=None) -> torch.Tensor:
-    """Binary codes [B,Hkv,Nmax,code_bits/32] int32 (uint32 bit patterns)."""
+def hst_hash_keys_binary(K, R, code_bits: int = 128, seq_lens=None, codes=None) -> torch.Tensor:
+    """Binary codes [B,Hkv,Nmax,code_bits/32] int32 (uint32 bit patterns).
+
+    ``codes`` may be passed in (rows past N_b are left as they are)."""
     B, Hkv, Nmax, d = K.shape
     shape = make_shape(K, Hkv, seq_lens)
-    codes = torch.zeros((B, Hkv, Nmax, code_bits // 32), dtype=torch.int32, device=K.device)
+    if codes is None:
+        codes = torch.zeros((B, Hkv, Nmax, code_bits // 32), dtype=torch.int32, device=K.device)
+    if codes.shape != (B, Hkv, Nmax, code_bits // 32) or codes.dtype != torch.int32:
+        raise ValueError("codes do not match the shape and dtype")
     _check(_C.hst_hash_keys_binary(ctypes.byref(shape), _ptr(K), _ptr(R), code_bits,
                                    _ptr(codes), _stream(K.device)), "hst_hash_keys_binary")
     return codes
