@@ -60,6 +60,7 @@ __all__ = [
     "exact_projection_signs", "hash_keys_softlsh", "value_norms",
     "binary_codes", "query_tables", "score_softlsh", "score_hamming",
     "select_topk", "attend", "decode_slab_softlsh", "decode_slab_hamming",
+    "append_tokens",
 ]
 
 _U64 = 2.0 ** -53
@@ -262,3 +263,32 @@ def decode_slab_hamming(qg, K, V, R, k, scale=None, kcodes=None) -> dict:
     out, lse = attend(qg, K, V, idx, scale)
     return {"kcodes": kcodes, "qcodes": qcodes, "scores": s, "idx": idx,
             "out": out, "lse": lse}
+
+
+def append_tokens(K, V, lens, k_new, v_new, *, W=None, L=0, P=0, norm_dtype="f16",
+                  ids=None, vnorm=None, R=None, codes=None) -> None:
+    """Decode-time append of one token per sequence, in place.
+
+    SOCKET page, core mechanism, item 1: a key's bucket ids and its value norm
+    are computed once, when it enters the cache; HATA page, section 3: a key's
+    binary code likewise.  For each sequence b with n = max(lens[b], 0) < Nmax
+    the token k_new[b, h] / v_new[b, h] becomes row n of every kv head h, its
+    metadata is hashed (``W`` [Hkv, L*P, d] with ``ids``/``vnorm``, or ``R``
+    [Hkv, nbits, d] with ``codes``), and lens[b] becomes n + 1.  A sequence
+    whose cache is full is left as it is.
+    """
+    B, Hkv, Nmax, _ = K.shape
+    for b in range(B):
+        n = max(int(lens[b]), 0)
+        if n >= Nmax:
+            continue
+        for h in range(Hkv):
+            K[b, h, n] = k_new[b, h]
+            V[b, h, n] = v_new[b, h]
+            key = np.asarray(k_new[b, h], dtype=np.float64)[None]
+            if W is not None:
+                ids[b, h, n] = hash_keys_softlsh(key, W[h], L, P)[0]
+                vnorm[b, h, n] = value_norms(np.asarray(v_new[b, h])[None], norm_dtype)[0]
+            if R is not None:
+                codes[b, h, n] = binary_codes(key, R[h])[0]
+        lens[b] = n + 1

@@ -123,6 +123,57 @@ def test_value_norms_golden():
     assert float(np.float32(math.sqrt(2))) == float.fromhex("0x1.6a09e6p0")
 
 
+def test_append_tokens_rows_lengths_and_metadata():
+    # Decode-time append (SOCKET page, core mechanism, item 1; HATA page,
+    # section 3): each token lands at row max(lens[b], 0), hashed exactly, and
+    # the length advances; a full sequence is left untouched.
+    rng = np.random.default_rng(21)
+    B, Hkv, Nmax, d, L, P = 4, 2, 5, 4, 2, 3
+    lens0 = np.array([-2, 0, 3, 5], dtype=np.int64)
+    K = rng.standard_normal((B, Hkv, Nmax, d))
+    V = rng.standard_normal((B, Hkv, Nmax, d))
+    ids = rng.integers(0, 8, (B, Hkv, Nmax, L)).astype(np.uint8)
+    vnorm = rng.standard_normal((B, Hkv, Nmax))
+    codes = rng.integers(0, 2**32, (B, Hkv, Nmax, 4), dtype=np.uint64).astype(np.uint32)
+    W = rng.standard_normal((Hkv, L * P, d)).astype(np.float32).astype(np.float64)
+    R = rng.standard_normal((Hkv, 128, d)).astype(np.float32).astype(np.float64)
+    toks = [(rng.standard_normal((B, Hkv, d)).astype(np.float32).astype(np.float64),
+             rng.integers(-8, 9, (B, Hkv, d)) / 4.0) for _ in range(3)]
+    toks[1][0][0, 0] = 0.0                      # a zero key: every bit set
+    init = [a.copy() for a in (K, V, ids, vnorm, codes)]
+    lens = lens0.copy()
+    for kn, vn in toks:
+        O.append_tokens(K, V, lens, kn, vn, W=W, L=L, P=P, norm_dtype="f16", ids=ids,
+                        vnorm=vnorm, R=R, codes=codes)
+    np.testing.assert_array_equal(lens, [3, 3, 5, 5])
+    for b in range(B):
+        start = max(int(lens0[b]), 0)
+        rows = {start + t: t for t in range(3) if start + t < Nmax}
+        for h in range(Hkv):
+            for j in range(Nmax):
+                if j not in rows:        # untouched
+                    np.testing.assert_array_equal(K[b, h, j], init[0][b, h, j])
+                    np.testing.assert_array_equal(ids[b, h, j], init[2][b, h, j])
+                    np.testing.assert_array_equal(codes[b, h, j], init[4][b, h, j])
+                    assert vnorm[b, h, j] == init[3][b, h, j]
+                    continue
+                kn, vn = toks[rows[j]][0][b, h], toks[rows[j]][1][b, h]
+                np.testing.assert_array_equal(K[b, h, j], kn)
+                np.testing.assert_array_equal(V[b, h, j], vn)
+                np.testing.assert_array_equal(ids[b, h, j], _brute_ids(kn[None], W[h], L, P)[0])
+                # squares of quarter-integers sum exactly; sqrt then fp16 rounding
+                exact = math.sqrt(float(sum(Fraction(float(x)) ** 2 for x in vn)))
+                assert vnorm[b, h, j] == float(np.float16(exact))
+                want = [0, 0, 0, 0]
+                for i in range(128):
+                    y = sum(Fraction(float(w)) * Fraction(float(x)) for w, x in zip(R[h, i], kn))
+                    if y >= 0:
+                        want[i // 32] |= 1 << (i % 32)
+                np.testing.assert_array_equal(codes[b, h, j].astype(np.int64), want)
+    assert ids[0, 0, 1].tolist() == [(1 << P) - 1] * L
+    assert codes[0, 0, 1].tolist() == [0xFFFFFFFF] * 4
+
+
 # ---------------------------------------------------------------- codes
 
 def test_codes_axes_golden(golden_dir):
