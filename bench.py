@@ -239,6 +239,50 @@ def main():
     log(f"prefill hash {prefill_us:.1f} us ({prefill['tflops']:.0f} TFLOP/s, "
         f"{pre_bytes / (prefill_us * 1e-6) / 1e9:.0f} GB/s)")
 
+    # decode-time append of one token per sequence (rows, metadata, lengths),
+    # timed on a cache of the same batch and heads with room for every call
+    app_reps = 20
+    Ka = torch.zeros((w.B, w.Hkv, app_reps + 1, w.d), dtype=K.dtype, device=dev)
+    Va = torch.zeros_like(Ka)
+    la = torch.zeros((w.B,), dtype=torch.int32, device=dev)
+    kn, vnw = K[:, :, 0].contiguous(), V[:, :, 0].contiguous()
+    if w.scheme == "softlsh":
+        ida = torch.zeros((w.B, w.Hkv, app_reps + 1, w.L), dtype=torch.uint8, device=dev)
+        vna = torch.zeros((w.B, w.Hkv, app_reps + 1), dtype=vn.dtype, device=dev)
+        app = lambda: hst.hst_append_kv_softlsh(kn, vnw, Wp, w.L, w.P, Ka, Va, ida, vna, la)
+    else:
+        ca = torch.zeros((w.B, w.Hkv, app_reps + 1, w.code_bits // 32), dtype=torch.int32,
+                         device=dev)
+        app = lambda: hst.hst_append_kv_binary(kn, vnw, Rp, Ka, Va, ca, la)
+    def app_all():
+        for _ in range(app_reps):
+            app()
+
+    # eager calls (host marshalling included), then replays of a captured
+    # graph of app_reps calls (device time); the lengths restart before each
+    app()  # first launches load the kernels
+    la.zero_()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    app_all()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    append_eager_us = ev[0].elapsed_time(ev[1]) * 1e3 / app_reps
+    la.zero_()
+    app_graph = capture(app_all)
+    app_times = []
+    for _ in range(5):
+        la.zero_()
+        ev[0].record(stream)
+        app_graph.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        app_times.append(ev[0].elapsed_time(ev[1]) * 1e3 / app_reps)
+    append_us = sorted(app_times)[len(app_times) // 2]
+    append = {"us": append_us, "eager_us": append_eager_us, "tokens": w.B, "planes": planes}
+    log(f"append {append_us:.1f} us for {w.B} tokens ({append_eager_us:.1f} us eager)")
+    del Ka, Va, app_graph
+
     meta_b, gath_b, qo_b = alg_bytes(w, lens, ks)
     step_bytes = meta_b + gath_b + qo_b
     R = args.rotate or max(2, min(16, math.ceil(2 * MALL_BYTES / step_bytes) + 1))
@@ -363,6 +407,7 @@ def main():
                  "p10_us": float(np.percentile(per, 10)), "p50_us": float(np.percentile(per, 50)),
                  "p90_us": float(np.percentile(per, 90)), "rotated_copies": R},
         "prefill": prefill,
+        "append": append,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

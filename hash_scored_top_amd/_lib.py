@@ -27,7 +27,7 @@ EXPORTED = (
     "hst_hash_keys_softlsh", "hst_hash_keys_binary", "hst_score_keys_softlsh",
     "hst_score_keys_hamming", "hst_select_topk", "hst_sparse_decode_attention",
     "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
-    "hst_score_scan_softlsh",
+    "hst_score_scan_softlsh", "hst_append_kv_softlsh", "hst_append_kv_binary",
 )
 
 
@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
         "hst_workspace_size": ([I, SH, I, I, I, I, ctypes.POINTER(SZ)], I),
         "hst_hash_keys_softlsh": ([SH, P, P, P, I, I, I, P, P, P], I),
         "hst_hash_keys_binary": ([SH, P, P, I, P, P], I),
+        "hst_append_kv_softlsh": ([SH, P, P, P, I, I, I, P, P, P, P, P], I),
+        "hst_append_kv_binary": ([SH, P, P, P, I, P, P, P, P], I),
         "hst_score_keys_softlsh": ([SH, P, P, I, I, D, P, P, I, P, P, SZ, P], I),
         "hst_score_keys_hamming": ([SH, P, P, I, P, P, P, SZ, P], I),
         "hst_query_tables_softlsh": ([SH, P, P, I, I, D, P, P], I),
@@ -171,6 +173,45 @@ def hst_hash_keys_binary(K, R, code_bits: int = 128, seq_lens=None, codes=None) 
     _check(_C.hst_hash_keys_binary(ctypes.byref(shape), _ptr(K), _ptr(R), code_bits,
                                    _ptr(codes), _stream(K.device)), "hst_hash_keys_binary")
     return codes
+
+
+def _append_checks(K, V, k_new, v_new, seq_lens):
+    B, Hkv, Nmax, d = K.shape
+    if seq_lens is None or seq_lens.shape != (B,) or seq_lens.device != K.device:
+        raise ValueError("seq_lens [B] int32 on the cache's device is required (it advances)")
+    for t in (V, k_new, v_new):
+        if t.dtype != K.dtype or t.device != K.device:
+            raise ValueError("K, V, k_new and v_new must share dtype and device")
+    if V.shape != K.shape or k_new.shape != (B, Hkv, d) or v_new.shape != (B, Hkv, d):
+        raise ValueError("k_new / v_new must be [B, Hkv, d] and V the shape of K")
+
+
+def hst_append_kv_softlsh(k_new, v_new, W, L: int, P: int, K, V, ids, vnorm, seq_lens) -> None:
+    """Writes one token per sequence at row seq_lens[b] of K, V, ids and vnorm
+    (hashed on the way in) and advances seq_lens; full sequences are left as
+    they are.  Everything is updated in place."""
+    _append_checks(K, V, k_new, v_new, seq_lens)
+    B, Hkv, Nmax, d = K.shape
+    if ids.shape != (B, Hkv, Nmax, L) or ids.dtype != torch.uint8 or vnorm.shape != (B, Hkv, Nmax):
+        raise ValueError("ids / vnorm do not match the cache")
+    shape = make_shape(K, Hkv, seq_lens)
+    _check(_C.hst_append_kv_softlsh(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(W), L, P,
+                                    _norm_code(vnorm.dtype), _ptr(K), _ptr(V), _ptr(ids),
+                                    _ptr(vnorm), _stream(K.device)), "hst_append_kv_softlsh")
+
+
+def hst_append_kv_binary(k_new, v_new, R, K, V, codes, seq_lens, code_bits: int = 128) -> None:
+    """Writes one token per sequence at row seq_lens[b] of K, V and codes
+    (hashed on the way in) and advances seq_lens; full sequences are left as
+    they are.  Everything is updated in place."""
+    _append_checks(K, V, k_new, v_new, seq_lens)
+    B, Hkv, Nmax, d = K.shape
+    if codes.shape != (B, Hkv, Nmax, code_bits // 32) or codes.dtype != torch.int32:
+        raise ValueError("codes do not match the cache")
+    shape = make_shape(K, Hkv, seq_lens)
+    _check(_C.hst_append_kv_binary(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(R),
+                                   code_bits, _ptr(K), _ptr(V), _ptr(codes), _stream(K.device)),
+           "hst_append_kv_binary")
 
 
 def hst_score_keys_softlsh(q, W, L: int, P: int, tau: float, ids, vnorm, Nmax_like,

@@ -143,6 +143,33 @@ hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K, const voi
       hst::launch_hash_binary(*shape, K, R, codes, static_cast<hipStream_t>(stream)));
 }
 
+hst_status hst_append_kv_softlsh(const hst_shape* shape, const void* k_new, const void* v_new,
+                                 const void* W, int L, int P, int norm_dtype, void* K, void* V,
+                                 uint8_t* ids, void* vnorm, void* stream) {
+  HST_TRY(check_shape(shape));
+  if (L < 1 || P < 1) return HST_ERR_INVALID_ARG;
+  if (P > 8 || L > 1024) return HST_ERR_UNSUPPORTED;
+  HST_TRY(check_norm_dtype(norm_dtype));
+  if (shape->seq_lens == nullptr) return HST_ERR_INVALID_ARG;  // the lengths advance in place
+  if (!ptr_ok(k_new) || !ptr_ok(v_new) || !ptr_ok(W) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(ids) ||
+      !ptr_ok(vnorm))
+    return HST_ERR_INVALID_ARG;
+  return hip_status(hst::launch_append_softlsh(*shape, k_new, v_new, W, L, P, norm_dtype, K, V, ids,
+                                               vnorm, static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_append_kv_binary(const hst_shape* shape, const void* k_new, const void* v_new,
+                                const void* R, int code_bits, void* K, void* V, uint32_t* codes,
+                                void* stream) {
+  HST_TRY(check_shape(shape));
+  if (code_bits != 128) return HST_ERR_UNSUPPORTED;
+  if (shape->seq_lens == nullptr) return HST_ERR_INVALID_ARG;  // the lengths advance in place
+  if (!ptr_ok(k_new) || !ptr_ok(v_new) || !ptr_ok(R) || !ptr_ok(K) || !ptr_ok(V) || !ptr_ok(codes))
+    return HST_ERR_INVALID_ARG;
+  return hip_status(hst::launch_append_binary(*shape, k_new, v_new, R, K, V, codes,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 static hst_status score_softlsh_checks(const hst_shape* shape, const void* q, const void* W, int L,
                                        int P, double tau, const uint8_t* ids, const void* vnorm,
                                        int norm_dtype) {

@@ -38,7 +38,8 @@
  *     Query head hq reads kv head hq / (Hq / Hkv) (grouped-query attention).
  *   - shape->seq_lens is an optional DEVICE array [B] of context lengths
  *     N_b in [0, Nmax]; NULL means every N_b = Nmax.  Rows j >= N_b are
- *     never read or written by any call.
+ *     never read or written by any call, except that the append calls write
+ *     row N_b and then advance N_b.
  *   - Pointers must be 16-byte aligned.
  *   - Workspaces: a caller-owned device buffer of at least
  *     hst_workspace_size() bytes, 256-byte aligned, with no required initial
@@ -133,6 +134,31 @@ hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K,
 hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K,
                                 const void* R, int code_bits, uint32_t* codes,
                                 void* stream);
+
+/*
+ * Decode-time append of one token per sequence, with incremental hashing
+ * [SOCKET, core mechanism item 1: the per-key hash and value norm are
+ * computed once per key; a decode step adds one key per sequence].
+ * For every b with N_b < Nmax and every kv head h:
+ *   K[b][h][N_b] = k_new[b][h], V[b][h][N_b] = v_new[b][h]   ([B][Hkv][d])
+ *   ids[b][h][N_b], vnorm[b][h][N_b] as hst_hash_keys_softlsh computes them
+ *   (codes[b][h][N_b] as hst_hash_keys_binary, for the binary variant),
+ * then N_b += 1 in shape->seq_lens, which is required (device array, read
+ * and written).  A sequence whose cache is full (N_b == Nmax) is left
+ * unchanged.  The rows are written before the lengths advance (two kernels
+ * on the stream), so a decode step enqueued after the call sees the new
+ * token.  A negative N_b counts as 0.  Same requirements as the prefill
+ * calls (1 <= P <= 8, 1 <= L <= 1024, code_bits == 128); no workspace.
+ * Errors: HST_ERR_INVALID_ARG for a NULL shape->seq_lens or a NULL or
+ * misaligned pointer, HST_ERR_UNSUPPORTED for limits outside those.
+ */
+hst_status hst_append_kv_softlsh(const hst_shape* shape, const void* k_new,
+                                 const void* v_new, const void* W, int L, int P,
+                                 int norm_dtype, void* K, void* V, uint8_t* ids,
+                                 void* vnorm, void* stream);
+hst_status hst_append_kv_binary(const hst_shape* shape, const void* k_new,
+                                const void* v_new, const void* R, int code_bits,
+                                void* K, void* V, uint32_t* codes, void* stream);
 
 /*
  * Soft-collision scores of all keys [SOCKET, core mechanism items 2-3].

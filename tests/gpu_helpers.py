@@ -1,2 +1,33 @@
-"""Device plumbing for the GPU tests (re-exported from workloads.device)."""
+"""Device plumbing and shared input builders for the GPU tests."""
+import numpy as np
+
+import workloads as WL
 from workloads.device import norm_torch_dtype, norms_to_dev, to_dev  # noqa: F401
+
+
+def cancel_case(rng, d, nplanes, n):
+    """bf16-exact planes and keys whose projections are often exactly zero or
+    a tiny residue of large cancelling terms (the float32 sum of such a
+    projection can have either sign)."""
+    h = d // 2
+
+    def bf(x):  # round to bf16 (values are chosen representable or close)
+        return WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+    W = bf(rng.standard_normal((nplanes, d)) * 2.0 ** rng.integers(-2, 3, (nplanes, 1)))
+    dup = rng.random(nplanes) < 0.5          # planes with w[c + d/2] = w[c]
+    W[dup, h:] = W[dup, :h]
+    big = dup & (rng.random(nplanes) < 0.5)  # large entries, one tiny one
+    W[big, :] = bf(np.sign(W[big, :]) * 2.0 ** 10)
+    W[big, h - 1] = W[big, d - 1] = 2.0 ** -6
+    K = bf(rng.standard_normal((n, d)))
+    kind = rng.integers(0, 5, n)
+    anti = kind >= 2                         # k[c + d/2] = -k[c]: zero on duplicated planes
+    K[anti, h:] = -K[anti, :h]
+    K[kind == 1] = 0.0
+    huge = kind == 3                         # large cancelling products
+    K[huge] = bf(np.sign(K[huge]) * 2.0 ** 10)
+    K[huge, h:] = -K[huge, :h]
+    pert = kind == 4                         # antisymmetric but one channel nudged by an ulp
+    K[pert, d - 1] = bf(K[pert, d - 1] * (1.0 + 2.0 ** -7))
+    return W.astype(np.float32), K.astype(np.float32)

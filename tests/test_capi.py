@@ -107,3 +107,29 @@ def test_entry_points_validate_before_launch():
     assert C.hst_decode_step_hamming(by, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 10, None, 0.1, FAKE,
                                      FAKE, None, FAKE, 100, None) == -3
     assert C.hst_last_hip_error() == 0
+
+
+def test_append_entry_points_validate_before_launch():
+    L = _lib()
+    C = L._C
+    sh = _shape(L)                              # no seq_lens: the lengths must advance
+    by = ctypes.byref(sh)
+    assert C.hst_append_kv_softlsh(by, FAKE, FAKE, FAKE, 16, 8, L.HST_F16, FAKE, FAKE, FAKE,
+                                   FAKE, None) == -1
+    assert C.hst_append_kv_binary(by, FAKE, FAKE, FAKE, 128, FAKE, FAKE, FAKE, None) == -1
+    shl = _shape(L, seq_lens=FAKE)
+    byl = ctypes.byref(shl)
+    # L > 1024, P > 8, L < 1, bad norm dtype, misaligned or null pointers
+    assert C.hst_append_kv_softlsh(byl, FAKE, FAKE, FAKE, 1025, 8, L.HST_F16, FAKE, FAKE, FAKE,
+                                   FAKE, None) == -2
+    assert C.hst_append_kv_softlsh(byl, FAKE, FAKE, FAKE, 16, 9, L.HST_F16, FAKE, FAKE, FAKE,
+                                   FAKE, None) == -2
+    assert C.hst_append_kv_softlsh(byl, FAKE, FAKE, FAKE, 0, 8, L.HST_F16, FAKE, FAKE, FAKE,
+                                   FAKE, None) == -1
+    assert C.hst_append_kv_softlsh(byl, FAKE, FAKE, FAKE, 16, 8, L.HST_BF16, FAKE, FAKE, FAKE,
+                                   FAKE, None) == -2
+    assert C.hst_append_kv_softlsh(byl, FAKE + 2, FAKE, FAKE, 16, 8, L.HST_F16, FAKE, FAKE,
+                                   FAKE, FAKE, None) == -1
+    assert C.hst_append_kv_binary(byl, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -2
+    assert C.hst_append_kv_binary(byl, FAKE, None, FAKE, 128, FAKE, FAKE, FAKE, None) == -1
+    assert C.hst_last_hip_error() == 0

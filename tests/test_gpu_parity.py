@@ -14,6 +14,7 @@ import torch
 
 import oracle as O
 import workloads as WL
+from tests.gpu_helpers import cancel_case
 
 pytestmark = pytest.mark.gpu
 
@@ -96,34 +97,6 @@ def test_hash_binary_bit_exact():
                                           O.binary_codes(K64, f64(x["R"][h], w.kv_dtype)))
 
 
-def _cancel_case(rng, d, nplanes, n):
-    """bf16-exact planes and keys whose projections are often exactly zero or
-    a tiny residue of large cancelling terms (the float32 sum of such a
-    projection can have either sign)."""
-    h = d // 2
-
-    def bf(x):  # round to bf16 (values are chosen representable or close)
-        return WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(np.asarray(x, np.float32)))
-
-    W = bf(rng.standard_normal((nplanes, d)) * 2.0 ** rng.integers(-2, 3, (nplanes, 1)))
-    dup = rng.random(nplanes) < 0.5          # planes with w[c + d/2] = w[c]
-    W[dup, h:] = W[dup, :h]
-    big = dup & (rng.random(nplanes) < 0.5)  # large entries, one tiny one
-    W[big, :] = bf(np.sign(W[big, :]) * 2.0 ** 10)
-    W[big, h - 1] = W[big, d - 1] = 2.0 ** -6
-    K = bf(rng.standard_normal((n, d)))
-    kind = rng.integers(0, 5, n)
-    anti = kind >= 2                         # k[c + d/2] = -k[c]: zero on duplicated planes
-    K[anti, h:] = -K[anti, :h]
-    K[kind == 1] = 0.0
-    huge = kind == 3                         # large cancelling products
-    K[huge] = bf(np.sign(K[huge]) * 2.0 ** 10)
-    K[huge, h:] = -K[huge, :h]
-    pert = kind == 4                         # antisymmetric but one channel nudged by an ulp
-    K[pert, d - 1] = bf(K[pert, d - 1] * (1.0 + 2.0 ** -7))
-    return W.astype(np.float32), K.astype(np.float32)
-
-
 @pytest.mark.parametrize("d,L", [(128, 64), (128, 16), (128, 128), (64, 64), (64, 16)])
 def test_hash_mfma_signs_exact_under_cancellation(d, L):
     hst = _hst()
@@ -132,11 +105,11 @@ def test_hash_mfma_signs_exact_under_cancellation(d, L):
     lens = np.array([N, 977], dtype=np.int32)
     Ws, Ks = [], np.zeros((B, Hkv, N, d), np.float32)
     for h in range(Hkv):
-        Wh, _ = _cancel_case(rng, d, L * 8, 1)
+        Wh, _ = cancel_case(rng, d, L * 8, 1)
         Ws.append(Wh)
     for b in range(B):
         for h in range(Hkv):
-            Ks[b, h] = _cancel_case(np.random.default_rng(7 * b + h), d, L * 8, N)[1]
+            Ks[b, h] = cancel_case(np.random.default_rng(7 * b + h), d, L * 8, N)[1]
             Ks[b, h, lens[b]:] = 0.0
     W = np.stack(Ws)
     to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(DEV)
