@@ -60,7 +60,7 @@ __all__ = [
     "exact_projection_signs", "hash_keys_softlsh", "value_norms",
     "binary_codes", "query_tables", "score_softlsh", "score_hamming",
     "select_topk", "attend", "decode_slab_softlsh", "decode_slab_hamming",
-    "append_tokens",
+    "append_tokens", "select_mass",
 ]
 
 _U64 = 2.0 ** -53
@@ -292,3 +292,32 @@ def append_tokens(K, V, lens, k_new, v_new, *, W=None, L=0, P=0, norm_dtype="f16
             if R is not None:
                 codes[b, h, n] = binary_codes(key, R[h])[0]
         lens[b] = n + 1
+
+
+def select_mass(qg: np.ndarray, K: np.ndarray, cand: np.ndarray, p: float,
+                scale: float) -> np.ndarray:
+    """Cumulative-mass selection over a candidate set (Tactic page, sections 1
+    and 3: keep adding tokens until the summed normalised attention score of
+    the chosen set reaches a target, so the count adapts per head and query).
+
+    cand: candidate key indices (entries < 0 are padding).  For the G query
+    heads of the KV head, a_gj = scale * q_g . K_j over the candidates, the
+    softmax pi_gj = exp(a_gj) / sum_i exp(a_gi) per head, and the mass of
+    key j is m_j = (1/G) sum_g pi_gj (the masses sum to 1).  Keys are taken
+    in the order (m_j descending, index ascending) until the running sum is
+    >= p * sum_j m_j; at least one key is taken when there is a candidate.
+    Returns the chosen indices in ascending order.
+    """
+    cand = np.asarray(cand, dtype=np.int64)
+    cand = cand[cand >= 0]
+    if cand.size == 0:
+        return cand
+    qg = np.asarray(qg, dtype=np.float64)
+    a = scale * (qg @ np.asarray(K, dtype=np.float64)[cand].T)       # [G, c]
+    e = np.exp(a - a.max(axis=1, keepdims=True))
+    m = (e / e.sum(axis=1, keepdims=True)).mean(axis=0)              # [c]
+    order = np.lexsort((cand, -m))
+    csum = np.cumsum(m[order])
+    total = csum[-1]
+    count = int(np.searchsorted(csum >= p * total, True)) + 1
+    return np.sort(cand[order[:max(1, min(count, cand.size))]])

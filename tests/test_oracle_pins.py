@@ -413,6 +413,83 @@ def test_select_integer_scores(vals, k):
     assert O.select_topk(s, k).tolist() == _select_brute(vals, k)
 
 
+# ---------------------------------------------------------------- mass selection
+
+def _masses(qg, K, cand, scale):
+    """Per-candidate mass, head by head with math.exp (no numpy reductions)."""
+    G = len(qg)
+    out = [0.0] * len(cand)
+    for g in range(G):
+        a = [scale * sum(float(x) * float(y) for x, y in zip(qg[g], K[j])) for j in cand]
+        mx = max(a)
+        e = [math.exp(v - mx) for v in a]
+        z = math.fsum(e)
+        for i, v in enumerate(e):
+            out[i] += v / z / G
+    return out
+
+
+def test_select_mass_is_the_smallest_set_reaching_the_target():
+    # Tactic page, section 3: tokens are added until the cumulative normalised
+    # score reaches the target; by brute force over all subsets, no smaller
+    # set reaches it, and the chosen set does.
+    rng = np.random.default_rng(17)
+    import itertools
+    for trial in range(30):
+        G, d, c = int(rng.integers(1, 4)), 6, int(rng.integers(1, 9))
+        qg = rng.standard_normal((G, d)) * 2.0
+        K = rng.standard_normal((20, d))
+        cand = np.sort(rng.choice(20, c, replace=False))
+        p = float(rng.choice([0.3, 0.5, 0.8, 0.95, 1.0]))
+        got = O.select_mass(qg, K, cand, p, 0.5)
+        m = dict(zip(cand.tolist(), _masses(qg, K, cand.tolist(), 0.5)))
+        total = math.fsum(m.values())
+        need = min(r for r in range(1, c + 1)
+                   for sub in itertools.combinations(cand.tolist(), r)
+                   if math.fsum(m[j] for j in sub) >= p * total * (1 - 1e-12))
+        assert len(got) == need, (trial, len(got), need)
+        assert math.fsum(m[j] for j in got) >= p * total * (1 - 1e-12)
+        assert set(got.tolist()) <= set(cand.tolist())
+        assert (np.diff(got) > 0).all()
+
+
+def test_select_mass_ties_uniform_and_padding():
+    d = 8
+    K = np.tile(np.arange(1.0, d + 1.0), (12, 1))        # identical keys: equal masses
+    qg = np.ones((2, d))
+    cand = np.array([11, 2, 7, 5, -1, 9, 0, -1])
+    # 6 equal masses of 1/6: half the mass takes the 3 lowest indices
+    np.testing.assert_array_equal(O.select_mass(qg, K, cand, 0.5, 0.1), [0, 2, 5])
+    np.testing.assert_array_equal(O.select_mass(qg, K, cand, 1.0, 0.1), [0, 2, 5, 7, 9, 11])
+    # a target just above k/6 needs k + 1 keys
+    np.testing.assert_array_equal(O.select_mass(qg, K, cand, 2 / 6 + 1e-9, 0.1), [0, 2, 5])
+    assert O.select_mass(qg, K, np.array([-1, -1]), 0.5, 0.1).size == 0
+    # the smallest target still takes one key
+    np.testing.assert_array_equal(O.select_mass(qg, K, cand, 1e-300, 0.1), [0])
+
+
+def test_select_mass_dominant_keys_and_head_average():
+    d = 16
+    K = np.zeros((10, d))
+    K[3, 0] = 1.0
+    K[8, 1] = 1.0
+    q1 = np.zeros((1, d)); q1[0, 0] = 100.0
+    # one head whose softmax sits on key 3
+    np.testing.assert_array_equal(O.select_mass(q1, K, np.arange(10), 0.99, 1.0), [3])
+    # two heads, one on key 3 and one on key 8: each holds half of the mass
+    q2 = np.zeros((2, d)); q2[0, 0] = 100.0; q2[1, 1] = 100.0
+    np.testing.assert_array_equal(O.select_mass(q2, K, np.arange(10), 0.4, 1.0), [3])
+    np.testing.assert_array_equal(O.select_mass(q2, K, np.arange(10), 0.6, 1.0), [3, 8])
+    # the count never falls as the target rises
+    rng = np.random.default_rng(4)
+    qg = rng.standard_normal((4, d)) * 3
+    Kr = rng.standard_normal((300, d))
+    counts = [O.select_mass(qg, Kr, np.arange(300), p, 0.25).size
+              for p in np.linspace(0.05, 1.0, 40)]
+    assert all(a <= b for a, b in zip(counts, counts[1:]))
+    assert counts[-1] == 300
+
+
 # ---------------------------------------------------------------- attention
 
 def test_attend_all_keys_equals_dense_sdpa():
