@@ -300,7 +300,8 @@ def select_mass(qg: np.ndarray, K: np.ndarray, cand: np.ndarray, p: float,
     and 3: keep adding tokens until the summed normalised attention score of
     the chosen set reaches a target, so the count adapts per head and query).
 
-    cand: candidate key indices (entries < 0 are padding).  For the G query
+    cand: candidate key indices (entries outside [0, len(K)) are padding,
+    as the selection pads with -1).  For the G query
     heads of the KV head, a_gj = scale * q_g . K_j over the candidates, the
     softmax pi_gj = exp(a_gj) / sum_i exp(a_gi) per head, and the mass of
     key j is m_j = (1/G) sum_g pi_gj (the masses sum to 1).  Keys are taken
@@ -309,7 +310,7 @@ def select_mass(qg: np.ndarray, K: np.ndarray, cand: np.ndarray, p: float,
     Returns the chosen indices in ascending order.
     """
     cand = np.asarray(cand, dtype=np.int64)
-    cand = cand[cand >= 0]
+    cand = cand[(cand >= 0) & (cand < np.asarray(K).shape[0])]
     if cand.size == 0:
         return cand
     qg = np.asarray(qg, dtype=np.float64)

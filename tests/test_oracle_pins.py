@@ -464,6 +464,8 @@ def test_select_mass_ties_uniform_and_padding():
     # a target just above k/6 needs k + 1 keys
     np.testing.assert_array_equal(O.select_mass(qg, K, cand, 2 / 6 + 1e-9, 0.1), [0, 2, 5])
     assert O.select_mass(qg, K, np.array([-1, -1]), 0.5, 0.1).size == 0
+    # indices past the context are padding too
+    np.testing.assert_array_equal(O.select_mass(qg, K, np.array([0, 2, 12, 40]), 1.0, 0.1), [0, 2])
     # the smallest target still takes one key
     np.testing.assert_array_equal(O.select_mass(qg, K, cand, 1e-300, 0.1), [0])
 
