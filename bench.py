@@ -15,10 +15,14 @@ copy (``--no-graph`` times eager launches instead).
 Prints one JSON line: decode tokens/s (= batch / step time), the roofline of
 the dominant kernel (HBM bytes per launch / event-timed duration), the whole
 step's fraction of the HBM roofline, and the CPU oracle's rate on the host.
+Beside them: the prefill hashing, the decode-time append, the step with a
+cumulative-mass budget instead of a fixed k, and dense attention over every
+cached key (for the sparse/dense ratio).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -33,6 +37,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak (prefill projection)
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode tokens/s and % of HBM roofline for hash score+top-k+sparse attn"
+MASS_P = 0.9  # target of the cumulative-mass variant of the step
 
 
 def parse():
@@ -380,6 +385,67 @@ def main():
     achieved = kbytes / (kus * 1e-6) / 1e9
     traffic = traffic_record(kname.split("<")[0].replace("_kernel", ""), w.name, ksrc)
 
+    def time_graph(fn, reps=10):
+        """Median per-call time (us) of fn over replays of a captured graph of R calls."""
+        g = capture(lambda: [fn(i) for i in range(R)])
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            g.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3 / R)
+        return float(np.median(ts))
+
+    # cumulative-mass variant of the step (soft-LSH): the kmax candidates of
+    # highest hash score, then the smallest set holding MASS_P of their
+    # softmax mass
+    mass = None
+    if w.scheme == "softlsh":
+        mstep = hst.DecodeSoftLSHMass(K, w.Hq, w.L, w.P, w.tau, kmax, MASS_P, vn.dtype,
+                                      seq_lens=sl, k_per_seq=kp)
+        mrun = lambda i: mstep(q, sets[i % R][0], sets[i % R][1], Wp, sets[i % R][2],
+                               sets[i % R][3])
+        mass_us = time_graph(mrun)
+        kept = mstep.counts.cpu().numpy().astype(np.int64)
+        cand_rows = sum(min(int(ks[b]), int(lens[b])) for b in range(w.B)) * w.Hkv
+        e = K.element_size()
+        mbytes = meta_b + qo_b + cand_rows * w.d * e + int(kept.sum()) * 2 * w.d * e
+        mass = {"p": MASS_P, "us": mass_us, "tokens_per_s": w.B / (mass_us * 1e-6),
+                "kept_mean": float(kept.mean()), "kept_max": int(kept.max()),
+                "candidates_per_head": kmax, "alg_bytes": mbytes,
+                "hbm_frac": mbytes / (mass_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        log(f"mass step (p={MASS_P}) {mass_us:.2f} us, kept {kept.mean():.1f} of {kmax} keys "
+            "per head on average")
+        del mstep
+
+    # dense attention over every cached key, for the sparse/dense ratio
+    dense = None
+    if w.B * w.Hkv * w.N <= (1 << 24):
+        didx = torch.arange(w.N, dtype=torch.int32, device=dev).repeat(w.B, w.Hkv, 1)
+        dshape = hst.make_shape(K, w.Hq, sl)
+        dout = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        dws = torch.empty(hst.workspace_size(hst._lib.HST_OP_SPARSE_ATTENTION, dshape, k=w.N),
+                          dtype=torch.uint8, device=dev)
+        dscale = float(w.d ** -0.5)
+
+        def drun(i):
+            hst._lib._check(hst._lib._C.hst_sparse_decode_attention(
+                ctypes.byref(dshape), q.data_ptr(), sets[i % R][0].data_ptr(),
+                sets[i % R][1].data_ptr(), didx.data_ptr(), w.N, dscale, dout.data_ptr(), None,
+                dws.data_ptr(), dws.numel(), torch.cuda.current_stream().cuda_stream),
+                "dense attention")
+        dense_us = time_graph(drun, reps=5)
+        dbytes = tot_keys * 2 * w.d * K.element_size() + qo_b
+        dense = {"us": dense_us, "alg_bytes": dbytes,
+                 "hbm_frac": dbytes / (dense_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+                 "sparse_speedup": dense_us / (ms_per_step * 1e3)}
+        log(f"dense attention over all keys {dense_us:.1f} us "
+            f"({dense['sparse_speedup']:.1f}x the sparse step)")
+        del didx, dws
+
     result = {
         "metric": METRIC,
         "value": w.B / (ms_per_step * 1e-3),
@@ -408,6 +474,8 @@ def main():
                  "p90_us": float(np.percentile(per, 90)), "rotated_copies": R},
         "prefill": prefill,
         "append": append,
+        "mass": mass,
+        "dense": dense,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -20,7 +20,7 @@ HST_OK, HST_ERR_INVALID_ARG, HST_ERR_UNSUPPORTED, HST_ERR_WORKSPACE, HST_ERR_HIP
 HST_F32, HST_BF16, HST_F16, HST_I32 = 0, 1, 2, 3
 (HST_OP_HASH_SOFTLSH, HST_OP_HASH_BINARY, HST_OP_SCORE_SOFTLSH, HST_OP_SCORE_HAMMING,
  HST_OP_SELECT_TOPK, HST_OP_SPARSE_ATTENTION, HST_OP_DECODE_SOFTLSH,
- HST_OP_DECODE_HAMMING) = range(8)
+ HST_OP_DECODE_HAMMING, HST_OP_SELECT_MASS, HST_OP_DECODE_SOFTLSH_MASS) = range(10)
 
 EXPORTED = (
     "hst_version", "hst_status_string", "hst_last_hip_error", "hst_workspace_size",
@@ -28,6 +28,7 @@ EXPORTED = (
     "hst_score_keys_hamming", "hst_select_topk", "hst_sparse_decode_attention",
     "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
     "hst_score_scan_softlsh", "hst_append_kv_softlsh", "hst_append_kv_binary",
+    "hst_select_mass", "hst_decode_step_softlsh_mass",
 )
 
 
@@ -70,6 +71,9 @@ def _load() -> ctypes.CDLL:
         "hst_sparse_decode_attention": ([SH, P, P, P, P, I, F, P, P, P, SZ, P], I),
         "hst_decode_step_softlsh": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, F, P, P, P, P, SZ, P], I),
         "hst_decode_step_hamming": ([SH, P, P, P, P, I, P, I, P, F, P, P, P, P, SZ, P], I),
+        "hst_select_mass": ([SH, P, P, P, I, D, F, P, P, P, SZ, P], I),
+        "hst_decode_step_softlsh_mass": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, D, F, P, P, P,
+                                          P, P, SZ, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -302,6 +306,26 @@ def hst_sparse_decode_attention(q, K, V, idx, scale: Optional[float] = None, seq
     return out, lse
 
 
+def hst_select_mass(q, K, cand, p: float, scale: Optional[float] = None, seq_lens=None):
+    """Cumulative-mass selection over candidates cand [B,Hkv,k] int32 (as
+    hst_select_topk writes them): idx [B,Hkv,k] int32 (-1 padded) and
+    counts [B,Hkv] int32."""
+    B, Hq, d = q.shape
+    shape = make_shape(K, Hq, seq_lens)
+    k = cand.shape[-1]
+    if cand.dtype != torch.int32 or cand.shape != (B, K.shape[1], k):
+        raise ValueError("cand must be int32 [B, Hkv, k]")
+    if scale is None:
+        scale = d ** -0.5
+    idx = torch.empty_like(cand)
+    counts = torch.empty((B, K.shape[1]), dtype=torch.int32, device=q.device)
+    ws = _workspace(workspace_size(HST_OP_SELECT_MASS, shape, k=k), q.device)
+    _check(_C.hst_select_mass(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(cand), k, float(p),
+                              float(scale), _ptr(idx), _ptr(counts), _ptr(ws), ws.numel(),
+                              _stream(q.device)), "hst_select_mass")
+    return idx, counts
+
+
 class DecodeSoftLSH:
     """Pre-sized soft-LSH decode step: outputs and workspace allocated once."""
 
@@ -367,3 +391,35 @@ def hst_decode_step_hamming(q, K, V, R, codes, k: int, seq_lens=None, k_per_seq=
                             scale=None):
     step = DecodeHamming(K, q.shape[1], k, 128, seq_lens, k_per_seq, scale)
     return step(q, K, V, R, codes)
+
+
+class DecodeSoftLSHMass:
+    """Pre-sized soft-LSH decode step with a cumulative-mass budget: the k
+    keys of highest hash score are the candidates, the kept set reaches mass
+    p of their softmax."""
+
+    def __init__(self, K, Hq: int, L: int, P: int, tau: float, k: int, p: float, norm_dtype,
+                 seq_lens=None, k_per_seq=None, scale: Optional[float] = None):
+        B, Hkv, Nmax, d = K.shape
+        self.shape = make_shape(K, Hq, seq_lens)
+        self._keep = (seq_lens, k_per_seq)
+        self.L, self.P, self.tau, self.k, self.p = L, P, float(tau), k, float(p)
+        self.norm_code = _norm_code(norm_dtype)
+        self.scale = float(d ** -0.5 if scale is None else scale)
+        dev = K.device
+        self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.ws = _workspace(workspace_size(HST_OP_DECODE_SOFTLSH_MASS, self.shape, L, P, k=k),
+                             dev)
+        self.k_per_seq = k_per_seq
+
+    def __call__(self, q, K, V, W, ids, vnorm, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_step_softlsh_mass(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), _ptr(W), self.L, self.P,
+            self.tau, _ptr(ids), _ptr(vnorm), self.norm_code, self.k, _ptr(self.k_per_seq),
+            self.p, self.scale, _ptr(self.idx), _ptr(self.counts), _ptr(self.out),
+            _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st), "hst_decode_step_softlsh_mass")
+        return self.idx, self.counts, self.out, self.lse

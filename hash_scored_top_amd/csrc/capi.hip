@@ -94,10 +94,16 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
                    op == HST_OP_HASH_BINARY;
   if (soft) HST_TRY(check_lp(L, P));
   if (bin && code_bits != 128) return HST_ERR_UNSUPPORTED;
+  const bool mass = op == HST_OP_SELECT_MASS || op == HST_OP_DECODE_SOFTLSH_MASS;
   const bool needk = op == HST_OP_SELECT_TOPK || op == HST_OP_SPARSE_ATTENTION ||
-                     op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING;
+                     op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING || mass;
   if (needk && k < 1) return HST_ERR_INVALID_ARG;
   if (needk && k > hst::kMaxSplits * 1024) return HST_ERR_UNSUPPORTED;
+  if (mass && k > hst::kMassCap) return HST_ERR_UNSUPPORTED;
+  if (op == HST_OP_DECODE_SOFTLSH_MASS) {
+    HST_TRY(check_lp(L, P));
+    HST_TRY(check_soft_prep(shape, L, P));
+  }
   if (soft && op != HST_OP_HASH_SOFTLSH) HST_TRY(check_soft_prep(shape, L, P));
   size_t b = 0;
   switch (op) {
@@ -112,6 +118,13 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
       const hst::FusedLayout f = hst::fused_layout(*shape, op, L, P, needk ? k : 1);
       if (f.nchunks > hst::kMaxChunks) return HST_ERR_UNSUPPORTED;
       b = align_up(f.bytes);
+      break;
+    }
+    case HST_OP_SELECT_MASS: b = align_up(hst::mass_logits_bytes(*shape, k)); break;
+    case HST_OP_DECODE_SOFTLSH_MASS: {
+      const hst::FusedLayout f = hst::fused_layout(*shape, HST_OP_DECODE_SOFTLSH, L, P, k);
+      if (f.nchunks > hst::kMaxChunks) return HST_ERR_UNSUPPORTED;
+      b = align_up(hst::decode_mass_bytes(*shape, L, P, k));
       break;
     }
     default: return HST_ERR_INVALID_ARG;
@@ -277,6 +290,44 @@ hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q, co
   HST_TRY(workspace_check(HST_OP_SPARSE_ATTENTION, shape, 0, 0, k, ws, ws_bytes));
   return hip_status(hst::fused_attention(*shape, q, K, V, idx, k, scale, out, lse, ws,
                                          static_cast<hipStream_t>(stream)));
+}
+
+static hst_status mass_p_check(double p) {
+  return (p > 0.0 && p <= 1.0) ? HST_OK : HST_ERR_INVALID_ARG;  // NaN fails both
+}
+
+hst_status hst_select_mass(const hst_shape* shape, const void* q, const void* K,
+                           const int32_t* cand, int k, double p, float scale, int32_t* idx,
+                           int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  HST_TRY(check_shape(shape));
+  if (group(shape) > 8) return HST_ERR_UNSUPPORTED;
+  if (k < 1 || !isfinite(scale)) return HST_ERR_INVALID_ARG;
+  HST_TRY(mass_p_check(p));
+  if (!ptr_ok(q) || !ptr_ok(K) || !ptr_ok(cand) || !ptr_ok(idx) || !ptr_ok(counts))
+    return HST_ERR_INVALID_ARG;
+  if (cand == idx) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_SELECT_MASS, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::launch_select_mass(*shape, q, K, cand, k, p, scale, idx, counts,
+                                            static_cast<double*>(ws),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_step_softlsh_mass(const hst_shape* shape, const void* q, const void* K,
+                                        const void* V, const void* W, int L, int P, double tau,
+                                        const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                        int k, const int32_t* k_per_seq, double p, float scale,
+                                        int32_t* idx, int32_t* counts, float* out, float* lse,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  HST_TRY(mass_p_check(p));
+  if (!ptr_ok(idx) || !ptr_ok(counts)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH_MASS, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::fused_decode_softlsh_mass(*shape, q, K, V, W, L, P, tau, ids, vnorm,
+                                                   norm_dtype, k, k_per_seq, p, scale, idx,
+                                                   counts, out, lse, ws,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q, const void* K,

@@ -79,6 +79,21 @@ hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, 
 hipError_t launch_select_only(const hst_shape& s, const FusedArgs& a, int32_t* idx, const void* scores,
                               int scores_int, int chunk, hipStream_t st);
 
+// cumulative-mass selection (mass.hip): float64 logits of the candidates in
+// `logits` ([B*Hq][kcap] doubles), then the cut and the compaction
+constexpr int kMassCap = 8192;
+size_t mass_logits_bytes(const hst_shape& s, int kcap);
+hipError_t launch_select_mass(const hst_shape& s, const void* q, const void* K,
+                              const int32_t* cand, int kcap, double p, float scale, int32_t* idx,
+                              int32_t* counts, double* logits, hipStream_t st);
+hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const void* K,
+                                     const void* V, const void* W, int L, int P, double tau,
+                                     const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                     int kcap, const int32_t* kps, double p, float scale,
+                                     int32_t* idx, int32_t* counts, float* out, float* lse,
+                                     void* ws, hipStream_t st);
+size_t decode_mass_bytes(const hst_shape& s, int L, int P, int kcap);
+
 hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* W, int L, int P, double tau, const uint8_t* ids,
                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,

@@ -116,6 +116,37 @@ hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K
   return launch_attend(s, a, q, K, V, idx, true, scores, 0, f.chunk, scale, out, lse, st);
 }
 
+// Workspace of the mass decode step: the decode layout, then the candidate
+// list [B*Hkv][kcap] and the logits [B*Hq][kcap] (float64).
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t decode_mass_bytes(const hst_shape& s, int L, int P, int kcap) {
+  const FusedLayout f = fused_layout(s, HST_OP_DECODE_SOFTLSH, L, P, kcap);
+  const size_t cand = static_cast<size_t>(s.B) * s.Hkv * static_cast<size_t>(kcap) * 4;
+  return align256(f.bytes) + align256(cand) + align256(mass_logits_bytes(s, kcap));
+}
+
+hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const void* K,
+                                     const void* V, const void* W, int L, int P, double tau,
+                                     const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                     int kcap, const int32_t* kps, double p, float scale,
+                                     int32_t* idx, int32_t* counts, float* out, float* lse,
+                                     void* ws, hipStream_t st) {
+  const FusedLayout f = fused_layout(s, HST_OP_DECODE_SOFTLSH, L, P, kcap);
+  const FusedArgs a = make_args(s, f, ws, L, P, tau, kcap);
+  const int f16 = norm_dtype == HST_F16;
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + f.off_scores);
+  int32_t* cand = reinterpret_cast<int32_t*>(base + align256(f.bytes));
+  const size_t ncand = static_cast<size_t>(s.B) * s.Hkv * static_cast<size_t>(kcap) * 4;
+  double* logits = reinterpret_cast<double*>(base + align256(f.bytes) + align256(ncand));
+  HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
+  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, kps, st));
+  HST_CHECK(launch_select_only(s, a, cand, scores, 0, f.chunk, st));
+  HST_CHECK(launch_select_mass(s, q, K, cand, kcap, p, scale, idx, counts, logits, st));
+  return launch_attend(s, a, q, K, V, idx, false, nullptr, 0, f.chunk, scale, out, lse, st);
+}
+
 hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,

@@ -89,7 +89,9 @@ typedef enum {
   HST_OP_SELECT_TOPK = 4,
   HST_OP_SPARSE_ATTENTION = 5,
   HST_OP_DECODE_SOFTLSH = 6,
-  HST_OP_DECODE_HAMMING = 7
+  HST_OP_DECODE_HAMMING = 7,
+  HST_OP_SELECT_MASS = 8,
+  HST_OP_DECODE_SOFTLSH_MASS = 9
 } hst_op;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -239,6 +241,29 @@ hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q,
                                        size_t ws_bytes, void* stream);
 
 /*
+ * Cumulative-mass selection over candidates [Tactic, sections 1 and 3:
+ * tokens are added until the summed normalised attention score of the set
+ * reaches a target, so the count adapts per head and query].  For kv head
+ * h of sequence b, the candidates are C = { cand[b][h][i] : i < k,
+ * 0 <= cand[b][h][i] < N_b } (other entries are padding).  With the G query
+ * heads of h,
+ *   a_gj = scale * q[b][h*G+g] . K[b][h][j]             (float64, j in C)
+ *   m_j  = (1/G) sum_g exp(a_gj) / sum_{i in C} exp(a_gi)
+ * the keys are taken in the order (m_j descending, j ascending) until the
+ * running sum of m reaches p * sum_{j in C} m_j (at least one key when C is
+ * not empty).  counts[b][h] receives the number taken; idx[b][h][0..k)
+ * receives them in candidate order (ascending when cand is, as
+ * hst_select_topk writes it), then -1.  0 < p <= 1; 1 <= k <= 8192.
+ * idx must not overlap cand.  The decisions are taken in float64; a
+ * running sum within a few units in the last place of the target may land
+ * on either side.
+ */
+hst_status hst_select_mass(const hst_shape* shape, const void* q, const void* K,
+                           const int32_t* cand, int k, double p, float scale,
+                           int32_t* idx, int32_t* counts, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * One soft-LSH decode step: hst_score_keys_softlsh, hst_select_topk and
  * hst_sparse_decode_attention in sequence on the same stream, with the
  * scores kept in the workspace.  idx (the selection, as hst_select_topk
@@ -261,6 +286,25 @@ hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q,
                                    const int32_t* k_per_seq, float scale,
                                    int32_t* idx, float* out, float* lse,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Soft-LSH decode step with a cumulative-mass budget [Tactic, section 3]:
+ * as hst_decode_step_softlsh up to the selection of the k (or
+ * k_per_seq[b]) keys of highest hash score, which become the candidates of
+ * hst_select_mass; attention then runs over the keys it keeps.  idx and
+ * counts are as hst_select_mass writes them; lse nullable.
+ * 1 <= k <= 8192, 0 < p <= 1.
+ */
+hst_status hst_decode_step_softlsh_mass(const hst_shape* shape, const void* q,
+                                        const void* K, const void* V,
+                                        const void* W, int L, int P,
+                                        double tau, const uint8_t* ids,
+                                        const void* vnorm, int norm_dtype,
+                                        int k, const int32_t* k_per_seq,
+                                        double p, float scale, int32_t* idx,
+                                        int32_t* counts, float* out,
+                                        float* lse, void* ws, size_t ws_bytes,
+                                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -133,3 +133,32 @@ def test_append_entry_points_validate_before_launch():
     assert C.hst_append_kv_binary(byl, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None) == -2
     assert C.hst_append_kv_binary(byl, FAKE, None, FAKE, 128, FAKE, FAKE, FAKE, None) == -1
     assert C.hst_last_hip_error() == 0
+
+
+def test_mass_entry_points_validate_before_launch():
+    L = _lib()
+    C = L._C
+    sh = _shape(L)
+    by = ctypes.byref(sh)
+    big = 1 << 30
+    # p outside (0, 1], NaN, k beyond 8192, idx aliasing cand, workspace too small
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        assert C.hst_select_mass(by, FAKE, FAKE, FAKE, 16, p, 0.1, FAKE + 256, FAKE, FAKE, big,
+                                 None) == -1
+    assert C.hst_select_mass(by, FAKE, FAKE, FAKE, 8193, 0.9, 0.1, FAKE + 256, FAKE, FAKE, big,
+                             None) == -2
+    assert C.hst_select_mass(by, FAKE, FAKE, FAKE, 16, 0.9, 0.1, FAKE, FAKE, FAKE, big,
+                             None) == -1
+    assert C.hst_select_mass(by, FAKE, FAKE, FAKE, 16, 0.9, 0.1, FAKE + 256, FAKE, FAKE, 16,
+                             None) == -3
+    need = L.workspace_size(L.HST_OP_SELECT_MASS, sh, k=100)
+    assert need >= 2 * 8 * 100 * 8          # B * Hq * k float64 logits
+    a = L.workspace_size(L.HST_OP_DECODE_SOFTLSH_MASS, sh, 64, 8, k=100)
+    assert a > L.workspace_size(L.HST_OP_DECODE_SOFTLSH, sh, 64, 8, k=100)
+    assert C.hst_decode_step_softlsh_mass(by, FAKE, FAKE, FAKE, FAKE, 64, 8, 0.3, FAKE, FAKE,
+                                          L.HST_F16, 100, None, 2.0, 0.1, FAKE, FAKE, FAKE, None,
+                                          FAKE, big, None) == -1
+    assert C.hst_decode_step_softlsh_mass(by, FAKE, FAKE, FAKE, FAKE, 64, 8, 0.3, FAKE, FAKE,
+                                          L.HST_F16, 100, None, 0.9, 0.1, FAKE, FAKE, FAKE, None,
+                                          FAKE, 100, None) == -3
+    assert C.hst_last_hip_error() == 0
