@@ -60,7 +60,7 @@ __all__ = [
     "exact_projection_signs", "hash_keys_softlsh", "value_norms",
     "binary_codes", "query_tables", "score_softlsh", "score_hamming",
     "select_topk", "attend", "decode_slab_softlsh", "decode_slab_hamming",
-    "append_tokens", "select_mass",
+    "append_tokens", "select_mass", "chunk_cards_softlsh", "route_slab_softlsh",
 ]
 
 _U64 = 2.0 ** -53
@@ -322,3 +322,73 @@ def select_mass(qg: np.ndarray, K: np.ndarray, cand: np.ndarray, p: float,
     total = csum[-1]
     count = int(np.searchsorted(csum >= p * total, True)) + 1
     return np.sort(cand[order[:max(1, min(count, cand.size))]])
+
+
+CHUNK = 64  # tokens per chunk (HGA page, step 1)
+
+
+def chunk_cards_softlsh(K: np.ndarray, vnorm: np.ndarray, W: np.ndarray, L: int,
+                        P: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Index cards of 64-token chunks (HGA explainer page, section 2, step 1:
+    the context is cut into 64-token chunks, each summarised on a small card
+    that the query scans before it goes back to the exact tokens).
+
+    K [n, d] keys of one (sequence, kv head), vnorm [n] their stored value
+    norms.  The card of chunk c (keys 64c .. min(64c + 64, n) - 1) is the
+    soft-LSH bucket id of the chunk's key sum, bit p of table l set when the
+    exact W[l*P+p] . sum_j k_j >= 0, and its weight is the largest stored
+    value norm in the chunk.  Returns (ids uint8 [nc, L], weights [nc]).
+    """
+    K = np.asarray(K, dtype=np.float64)
+    Wp = np.asarray(W, dtype=np.float64)
+    n, d = K.shape
+    nc = (n + CHUNK - 1) // CHUNK
+    ids = np.zeros((nc, L), dtype=np.uint8)
+    wts = np.zeros(nc)
+    for c in range(nc):
+        Kc = K[c * CHUNK:min(n, (c + 1) * CHUNK)]
+        # float64 projection of the sum; within its error bound, the exact
+        # sign from a correctly rounded sum of every product
+        y = Wp @ Kc.sum(axis=0)
+        bound = 4.0 * (Kc.shape[0] + d + 2) * _U64 * (np.abs(Wp) @ np.abs(Kc).sum(axis=0))
+        for r in np.nonzero(np.abs(y) <= bound)[0]:
+            y[r] = math.fsum((Kc * Wp[r][None, :]).ravel().tolist())
+        bits = (y >= 0.0).reshape(L, P)
+        ids[c] = (bits.astype(np.int64) * (1 << np.arange(P))[None, :]).sum(axis=1)
+        wts[c] = np.max(vnorm[c * CHUNK:min(n, (c + 1) * CHUNK)])
+    return ids, wts
+
+
+def route_slab_softlsh(qg, K, V, W, L, P, tau, k, C, norm_dtype, scale=None, ids=None,
+                       vnorm=None, cards=None) -> dict:
+    """Two-level routed decode step for one (sequence, kv head) slab (HGA
+    page, section 2: chunk routing on the cards, then token routing inside
+    the chosen chunks, and exact attention over the original tokens).
+
+    The cards are scored like keys (card weight times the summed table
+    probability of the card's buckets), the C chunks first in the order
+    (score descending, chunk index ascending) are kept, every key of those
+    chunks is scored, and the k keys first in the order (score descending,
+    index ascending) among them are attended.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    n = K.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(K.shape[1])
+    if ids is None:
+        ids = hash_keys_softlsh(K, W, L, P)
+    if vnorm is None:
+        vnorm = value_norms(V, norm_dtype)
+    if cards is None:
+        cards = chunk_cards_softlsh(K, vnorm, W, L, P)
+    T = query_tables(qg, W, L, P, tau)
+    cscore = score_softlsh(T, cards[0], cards[1])
+    chunks = select_topk(cscore, C)
+    keys = np.concatenate([np.arange(c * CHUNK, min(n, (c + 1) * CHUNK)) for c in chunks]) \
+        if chunks.size else np.zeros(0, dtype=np.int64)
+    s = score_softlsh(T, ids[keys], vnorm[keys])
+    idx = np.sort(keys[select_topk(s, k)])
+    out, lse = attend(qg, K, V, idx, scale)
+    return {"cards": cards, "T": T, "chunk_scores": cscore, "chunks": chunks, "keys": keys,
+            "scores": s, "idx": idx, "out": out, "lse": lse}

@@ -492,6 +492,66 @@ def test_select_mass_dominant_keys_and_head_average():
     assert counts[-1] == 300
 
 
+# ---------------------------------------------------------------- chunk routing
+
+def test_chunk_cards_bruteforce_rational_and_weights():
+    # HGA page, section 2, step 1: one card per 64-token chunk.  The card
+    # bits are the exact signs of the planes against the chunk's key sum,
+    # checked with rational arithmetic; the weight is the chunk's largest
+    # stored value norm; the last chunk may be short.
+    rng = np.random.default_rng(31)
+    L, P, d, n = 3, 4, 5, 150
+    K = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
+    K[64:96] = K[96:128] = 0.0
+    K[64:96] = rng.standard_normal((32, d)).astype(np.float32)
+    K[96:128] = -K[64:96]                     # chunk 1 sums to exactly zero: all bits set
+    W = rng.standard_normal((L * P, d)).astype(np.float32).astype(np.float64)
+    vn = rng.random(n)
+    ids, wts = O.chunk_cards_softlsh(K, vn, W, L, P)
+    assert ids.shape == (3, L) and wts.shape == (3,)
+    for c in range(3):
+        rows = K[c * 64:min(n, c * 64 + 64)]
+        for l in range(L):
+            bid = 0
+            for p in range(P):
+                y = sum(Fraction(float(w)) * Fraction(float(x))
+                        for key in rows for w, x in zip(W[l * P + p], key))
+                bid |= (y >= 0) << p
+            assert ids[c, l] == bid, (c, l)
+        assert wts[c] == vn[c * 64:min(n, c * 64 + 64)].max()
+    assert (ids[1] == (1 << P) - 1).all()
+    # a chunk of one key is that key's own bucket ids
+    one = O.chunk_cards_softlsh(K[:1], vn[:1], W, L, P)[0]
+    np.testing.assert_array_equal(one, O.hash_keys_softlsh(K[:1], W, L, P))
+
+
+def test_routing_reduces_to_plain_topk_and_keeps_chosen_chunks():
+    rng = np.random.default_rng(8)
+    L, P, d, n, G, k, tau = 8, 4, 16, 700, 2, 40, 0.4
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    W = rng.standard_normal((L * P, d))
+    qg = rng.standard_normal((G, d))
+    nc = (n + 63) // 64
+    full = O.decode_slab_softlsh(qg, K, V, W, L, P, tau, k, "f16")
+    # every chunk kept: the plain top-k step
+    r = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, nc, "f16")
+    np.testing.assert_array_equal(r["idx"], full["idx"])
+    np.testing.assert_allclose(r["out"], full["out"], rtol=0, atol=0)
+    # one chunk kept: the best card (lower index on ties) and keys inside it
+    r1 = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, 1, "f16")
+    cs = r1["chunk_scores"]
+    best = min(range(nc), key=lambda c: (-cs[c], c))
+    assert r1["chunks"].tolist() == [best]
+    assert ((r1["idx"] >= 64 * best) & (r1["idx"] < 64 * best + 64)).all()
+    assert r1["idx"].size == min(k, 64, n - 64 * best)
+    # the card score is the card weight times the table mass of its buckets
+    T = r1["T"]
+    cid, cw = r1["cards"]
+    for c in range(nc):
+        assert abs(cs[c] - cw[c] * sum(T[l, cid[c, l]] for l in range(L))) <= 1e-12 * cs[c]
+
+
 # ---------------------------------------------------------------- attention
 
 def test_attend_all_keys_equals_dense_sdpa():
