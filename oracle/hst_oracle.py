@@ -60,7 +60,8 @@ __all__ = [
     "exact_projection_signs", "hash_keys_softlsh", "value_norms",
     "binary_codes", "query_tables", "score_softlsh", "score_hamming",
     "select_topk", "attend", "decode_slab_softlsh", "decode_slab_hamming",
-    "append_tokens", "select_mass", "chunk_cards_softlsh", "route_slab_softlsh",
+    "append_tokens", "select_mass", "chunk_card_keys", "chunk_cards_softlsh",
+    "route_slab_softlsh",
 ]
 
 _U64 = 2.0 ** -53
@@ -327,40 +328,51 @@ def select_mass(qg: np.ndarray, K: np.ndarray, cand: np.ndarray, p: float,
 CHUNK = 64  # tokens per chunk (HGA page, step 1)
 
 
-def chunk_cards_softlsh(K: np.ndarray, vnorm: np.ndarray, W: np.ndarray, L: int,
-                        P: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Index cards of 64-token chunks (HGA explainer page, section 2, step 1:
-    the context is cut into 64-token chunks, each summarised on a small card
-    that the query scans before it goes back to the exact tokens).
+def chunk_card_keys(K: np.ndarray, storage: str) -> np.ndarray:
+    """Card keys of 64-token chunks (HGA explainer page, section 2, step 1:
+    the context is cut into 64-token chunks, each summarised on a small
+    card that the query scans before it goes back to the exact tokens).
 
-    K [n, d] keys of one (sequence, kv head), vnorm [n] their stored value
-    norms.  The card of chunk c (keys 64c .. min(64c + 64, n) - 1) is the
-    soft-LSH bucket id of the chunk's key sum, bit p of table l set when the
-    exact W[l*P+p] . sum_j k_j >= 0, and its weight is the largest stored
-    value norm in the chunk.  Returns (ids uint8 [nc, L], weights [nc]).
+    The card key of chunk c is the sum of its keys (64c .. min(64c + 64,
+    n) - 1), accumulated in float64 in index order and rounded to the key
+    storage type ("f32": float32; "bf16": float32, then bf16, both to
+    nearest even), so that a card is itself a stored key.  Returns float64
+    [nc, d] holding the stored values.
     """
     K = np.asarray(K, dtype=np.float64)
-    Wp = np.asarray(W, dtype=np.float64)
     n, d = K.shape
     nc = (n + CHUNK - 1) // CHUNK
-    ids = np.zeros((nc, L), dtype=np.uint8)
-    wts = np.zeros(nc)
+    out = np.zeros((nc, d))
     for c in range(nc):
-        Kc = K[c * CHUNK:min(n, (c + 1) * CHUNK)]
-        # float64 projection of the sum; within its error bound, the exact
-        # sign from a correctly rounded sum of every product
-        y = Wp @ Kc.sum(axis=0)
-        bound = 4.0 * (Kc.shape[0] + d + 2) * _U64 * (np.abs(Wp) @ np.abs(Kc).sum(axis=0))
-        for r in np.nonzero(np.abs(y) <= bound)[0]:
-            y[r] = math.fsum((Kc * Wp[r][None, :]).ravel().tolist())
-        bits = (y >= 0.0).reshape(L, P)
-        ids[c] = (bits.astype(np.int64) * (1 << np.arange(P))[None, :]).sum(axis=1)
-        wts[c] = np.max(vnorm[c * CHUNK:min(n, (c + 1) * CHUNK)])
+        acc = np.zeros(d)
+        for j in range(c * CHUNK, min(n, (c + 1) * CHUNK)):
+            acc = acc + K[j]
+        x32 = acc.astype(np.float32)
+        if storage == "bf16":
+            b = x32.view(np.uint32).astype(np.uint64)
+            b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16          # nearest even
+            x32 = (b.astype(np.uint32) << 16).view(np.float32)
+        elif storage != "f32":
+            raise ValueError(storage)
+        out[c] = x32.astype(np.float64)
+    return out
+
+
+def chunk_cards_softlsh(K: np.ndarray, vnorm: np.ndarray, W: np.ndarray, L: int, P: int,
+                        storage: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Index cards: the soft-LSH bucket ids of each chunk's card key (hashed
+    like any key, exact signs) and, as its weight, the largest stored value
+    norm in the chunk.  Returns (ids uint8 [nc, L], weights [nc])."""
+    keys = chunk_card_keys(K, storage)
+    ids = hash_keys_softlsh(keys, W, L, P)
+    n = np.asarray(K).shape[0]
+    wts = np.array([np.max(vnorm[c * CHUNK:min(n, (c + 1) * CHUNK)])
+                    for c in range(keys.shape[0])])
     return ids, wts
 
 
-def route_slab_softlsh(qg, K, V, W, L, P, tau, k, C, norm_dtype, scale=None, ids=None,
-                       vnorm=None, cards=None) -> dict:
+def route_slab_softlsh(qg, K, V, W, L, P, tau, k, C, norm_dtype, storage, scale=None,
+                       ids=None, vnorm=None, cards=None) -> dict:
     """Two-level routed decode step for one (sequence, kv head) slab (HGA
     page, section 2: chunk routing on the cards, then token routing inside
     the chosen chunks, and exact attention over the original tokens).
@@ -381,7 +393,7 @@ def route_slab_softlsh(qg, K, V, W, L, P, tau, k, C, norm_dtype, scale=None, ids
     if vnorm is None:
         vnorm = value_norms(V, norm_dtype)
     if cards is None:
-        cards = chunk_cards_softlsh(K, vnorm, W, L, P)
+        cards = chunk_cards_softlsh(K, vnorm, W, L, P, storage)
     T = query_tables(qg, W, L, P, tau)
     cscore = score_softlsh(T, cards[0], cards[1])
     chunks = select_topk(cscore, C)

@@ -15,6 +15,7 @@ import torch
 from hypothesis import given, settings, strategies as st
 
 import oracle as O
+import workloads as WL
 
 
 def _read_golden(golden_dir, name):
@@ -495,33 +496,35 @@ def test_select_mass_dominant_keys_and_head_average():
 # ---------------------------------------------------------------- chunk routing
 
 def test_chunk_cards_bruteforce_rational_and_weights():
-    # HGA page, section 2, step 1: one card per 64-token chunk.  The card
-    # bits are the exact signs of the planes against the chunk's key sum,
-    # checked with rational arithmetic; the weight is the chunk's largest
-    # stored value norm; the last chunk may be short.
+    # HGA page, section 2, step 1: one card per 64-token chunk.  The card key
+    # is the chunk's key sum rounded to the storage type (checked against an
+    # exact rational sum and the rounding rule), its bits are exact signs
+    # (rational brute force), its weight the largest stored value norm; the
+    # last chunk may be short.
     rng = np.random.default_rng(31)
     L, P, d, n = 3, 4, 5, 150
-    K = rng.standard_normal((n, d)).astype(np.float32).astype(np.float64)
-    K[64:96] = K[96:128] = 0.0
-    K[64:96] = rng.standard_normal((32, d)).astype(np.float32)
+    K = WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(
+        rng.standard_normal((n, d)).astype(np.float32))).astype(np.float64)
     K[96:128] = -K[64:96]                     # chunk 1 sums to exactly zero: all bits set
     W = rng.standard_normal((L * P, d)).astype(np.float32).astype(np.float64)
     vn = rng.random(n)
-    ids, wts = O.chunk_cards_softlsh(K, vn, W, L, P)
-    assert ids.shape == (3, L) and wts.shape == (3,)
-    for c in range(3):
-        rows = K[c * 64:min(n, c * 64 + 64)]
-        for l in range(L):
-            bid = 0
-            for p in range(P):
-                y = sum(Fraction(float(w)) * Fraction(float(x))
-                        for key in rows for w, x in zip(W[l * P + p], key))
-                bid |= (y >= 0) << p
-            assert ids[c, l] == bid, (c, l)
-        assert wts[c] == vn[c * 64:min(n, c * 64 + 64)].max()
-    assert (ids[1] == (1 << P) - 1).all()
+    for storage in ("f32", "bf16"):
+        keys = O.chunk_card_keys(K, storage)
+        assert keys.shape == (3, d)
+        for c in range(3):
+            exact = [sum(Fraction(float(x)) for x in K[c * 64:min(n, c * 64 + 64), i])
+                     for i in range(d)]
+            want = np.array([float(v) for v in exact], dtype=np.float64).astype(np.float32)
+            if storage == "bf16":
+                want = WL.bf16_bits_to_f32(WL.f32_to_bf16_bits(want))
+            np.testing.assert_array_equal(keys[c], want.astype(np.float64))
+        ids, wts = O.chunk_cards_softlsh(K, vn, W, L, P, storage)
+        np.testing.assert_array_equal(ids, _brute_ids(keys, W, L, P))
+        assert (ids[1] == (1 << P) - 1).all()
+        for c in range(3):
+            assert wts[c] == vn[c * 64:min(n, c * 64 + 64)].max()
     # a chunk of one key is that key's own bucket ids
-    one = O.chunk_cards_softlsh(K[:1], vn[:1], W, L, P)[0]
+    one = O.chunk_cards_softlsh(K[:1], vn[:1], W, L, P, "bf16")[0]
     np.testing.assert_array_equal(one, O.hash_keys_softlsh(K[:1], W, L, P))
 
 
@@ -535,11 +538,11 @@ def test_routing_reduces_to_plain_topk_and_keeps_chosen_chunks():
     nc = (n + 63) // 64
     full = O.decode_slab_softlsh(qg, K, V, W, L, P, tau, k, "f16")
     # every chunk kept: the plain top-k step
-    r = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, nc, "f16")
+    r = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, nc, "f16", "f32")
     np.testing.assert_array_equal(r["idx"], full["idx"])
     np.testing.assert_allclose(r["out"], full["out"], rtol=0, atol=0)
     # one chunk kept: the best card (lower index on ties) and keys inside it
-    r1 = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, 1, "f16")
+    r1 = O.route_slab_softlsh(qg, K, V, W, L, P, tau, k, 1, "f16", "f32")
     cs = r1["chunk_scores"]
     best = min(range(nc), key=lambda c: (-cs[c], c))
     assert r1["chunks"].tolist() == [best]
