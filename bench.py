@@ -16,8 +16,9 @@ Prints one JSON line: decode tokens/s (= batch / step time), the roofline of
 the dominant kernel (HBM bytes per launch / event-timed duration), the whole
 step's fraction of the HBM roofline, and the CPU oracle's rate on the host.
 Beside them: the prefill hashing, the decode-time append, the step with a
-cumulative-mass budget instead of a fixed k, and dense attention over every
-cached key (for the sparse/dense ratio).
+cumulative-mass budget instead of a fixed k, the step with two-level chunk
+routing, and dense attention over every cached key (for the sparse/dense
+ratio).
 """
 from __future__ import annotations
 
@@ -38,6 +39,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak (prefill projection)
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "decode tokens/s and % of HBM roofline for hash score+top-k+sparse attn"
 MASS_P = 0.9  # target of the cumulative-mass variant of the step
+ROUTE_OVERSAMPLE = 4  # chunks kept by the routed step, per 64 selected keys
 
 
 def parse():
@@ -421,6 +423,30 @@ def main():
             "per head on average")
         del mstep
 
+    # two-level routed variant of the step (soft-LSH): cards of 64-token
+    # chunks first, ROUTE_OVERSAMPLE * ceil(k / 64) chunks kept, then the k
+    # best keys inside them
+    routed = None
+    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128):
+        C = min(256, ROUTE_OVERSAMPLE * math.ceil(kmax / 64))
+        cards = [hst.hst_build_cards_softlsh(st_[0], st_[3], Wp, w.L, w.P, seq_lens=sl)
+                 for st_ in sets]
+        rstep = hst.DecodeSoftLSHRouted(K, w.Hq, w.L, w.P, w.tau, kmax, C, vn.dtype, seq_lens=sl,
+                                        k_per_seq=kp)
+        rrun = lambda i: rstep(q, sets[i % R][0], sets[i % R][1], Wp, sets[i % R][2],
+                               sets[i % R][3], cards[i % R][1], cards[i % R][2])
+        routed_us = time_graph(rrun)
+        e = K.element_size()
+        m = w.L + vn.element_size()
+        ncards = sum((int(n) + 63) // 64 for n in lens) * w.Hkv
+        kept_keys = sum(min(C * 64, int(n)) for n in lens) * w.Hkv
+        rbytes = ncards * m + kept_keys * m + gath_b + qo_b
+        routed = {"chunks_kept": C, "us": routed_us, "tokens_per_s": w.B / (routed_us * 1e-6),
+                  "alg_bytes": rbytes,
+                  "hbm_frac": rbytes / (routed_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        log(f"routed step (C={C}) {routed_us:.2f} us, {rbytes / 1e6:.1f} MB")
+        del rstep, cards
+
     # dense attention over every cached key, for the sparse/dense ratio
     dense = None
     if w.B * w.Hkv * w.N <= (1 << 24):
@@ -475,6 +501,7 @@ def main():
         "prefill": prefill,
         "append": append,
         "mass": mass,
+        "routed": routed,
         "dense": dense,
     }
     if not args.no_cpu_baseline:

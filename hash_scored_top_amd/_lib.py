@@ -20,7 +20,9 @@ HST_OK, HST_ERR_INVALID_ARG, HST_ERR_UNSUPPORTED, HST_ERR_WORKSPACE, HST_ERR_HIP
 HST_F32, HST_BF16, HST_F16, HST_I32 = 0, 1, 2, 3
 (HST_OP_HASH_SOFTLSH, HST_OP_HASH_BINARY, HST_OP_SCORE_SOFTLSH, HST_OP_SCORE_HAMMING,
  HST_OP_SELECT_TOPK, HST_OP_SPARSE_ATTENTION, HST_OP_DECODE_SOFTLSH,
- HST_OP_DECODE_HAMMING, HST_OP_SELECT_MASS, HST_OP_DECODE_SOFTLSH_MASS) = range(10)
+ HST_OP_DECODE_HAMMING, HST_OP_SELECT_MASS, HST_OP_DECODE_SOFTLSH_MASS,
+ HST_OP_DECODE_SOFTLSH_ROUTED) = range(11)
+CHUNK = 64  # tokens per routing chunk
 
 EXPORTED = (
     "hst_version", "hst_status_string", "hst_last_hip_error", "hst_workspace_size",
@@ -28,7 +30,8 @@ EXPORTED = (
     "hst_score_keys_hamming", "hst_select_topk", "hst_sparse_decode_attention",
     "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
     "hst_score_scan_softlsh", "hst_append_kv_softlsh", "hst_append_kv_binary",
-    "hst_select_mass", "hst_decode_step_softlsh_mass",
+    "hst_select_mass", "hst_decode_step_softlsh_mass", "hst_build_cards_softlsh",
+    "hst_decode_step_softlsh_routed",
 )
 
 
@@ -72,6 +75,9 @@ def _load() -> ctypes.CDLL:
         "hst_decode_step_softlsh": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, F, P, P, P, P, SZ, P], I),
         "hst_decode_step_hamming": ([SH, P, P, P, P, I, P, I, P, F, P, P, P, P, SZ, P], I),
         "hst_select_mass": ([SH, P, P, P, I, D, F, P, P, P, SZ, P], I),
+        "hst_build_cards_softlsh": ([SH, P, P, I, P, I, I, P, P, P, P, P], I),
+        "hst_decode_step_softlsh_routed": ([SH, P, P, P, P, I, I, D, P, P, I, P, P, I, I, P, F, P,
+                                            P, P, P, SZ, P], I),
         "hst_decode_step_softlsh_mass": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, D, F, P, P, P,
                                           P, P, SZ, P], I),
     }
@@ -423,3 +429,51 @@ class DecodeSoftLSHMass:
             self.p, self.scale, _ptr(self.idx), _ptr(self.counts), _ptr(self.out),
             _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st), "hst_decode_step_softlsh_mass")
         return self.idx, self.counts, self.out, self.lse
+
+
+def hst_build_cards_softlsh(K, vnorm, W, L: int, P: int, seq_lens=None):
+    """Index cards of 64-token chunks: card keys [B,Hkv,Nc,d] (KV dtype),
+    card ids [B,Hkv,Nc,L] uint8, card weights [B,Hkv,Nc] (vnorm dtype) and
+    card counts [B] int32, with Nc = ceil(Nmax / 64)."""
+    B, Hkv, Nmax, d = K.shape
+    Nc = (Nmax + CHUNK - 1) // CHUNK
+    shape = make_shape(K, Hkv, seq_lens)
+    ckeys = torch.zeros((B, Hkv, Nc, d), dtype=K.dtype, device=K.device)
+    cids = torch.zeros((B, Hkv, Nc, L), dtype=torch.uint8, device=K.device)
+    cw = torch.zeros((B, Hkv, Nc), dtype=vnorm.dtype, device=K.device)
+    clens = torch.zeros((B,), dtype=torch.int32, device=K.device)
+    _check(_C.hst_build_cards_softlsh(ctypes.byref(shape), _ptr(K), _ptr(vnorm),
+                                      _norm_code(vnorm.dtype), _ptr(W), L, P, _ptr(ckeys),
+                                      _ptr(cids), _ptr(cw), _ptr(clens), _stream(K.device)),
+           "hst_build_cards_softlsh")
+    return ckeys, cids, cw, clens
+
+
+class DecodeSoftLSHRouted:
+    """Pre-sized soft-LSH decode step with two-level routing: C chunks by
+    their cards, then the k best keys inside them."""
+
+    def __init__(self, K, Hq: int, L: int, P: int, tau: float, k: int, C: int, norm_dtype,
+                 seq_lens=None, k_per_seq=None, scale: Optional[float] = None):
+        B, Hkv, Nmax, d = K.shape
+        self.shape = make_shape(K, Hq, seq_lens)
+        self._keep = (seq_lens, k_per_seq)
+        self.L, self.P, self.tau, self.k, self.C = L, P, float(tau), k, C
+        self.norm_code = _norm_code(norm_dtype)
+        self.scale = float(d ** -0.5 if scale is None else scale)
+        dev = K.device
+        self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        self.ws = _workspace(workspace_size(HST_OP_DECODE_SOFTLSH_ROUTED, self.shape, L, P, k=k),
+                             dev)
+        self.k_per_seq = k_per_seq
+
+    def __call__(self, q, K, V, W, ids, vnorm, card_ids, card_w, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_step_softlsh_routed(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), _ptr(W), self.L, self.P,
+            self.tau, _ptr(ids), _ptr(vnorm), self.norm_code, _ptr(card_ids), _ptr(card_w),
+            self.C, self.k, _ptr(self.k_per_seq), self.scale, _ptr(self.idx), _ptr(self.out),
+            _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st), "hst_decode_step_softlsh_routed")
+        return self.idx, self.out, self.lse

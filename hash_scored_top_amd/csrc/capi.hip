@@ -58,12 +58,24 @@ hst_status check_soft_prep(const hst_shape* s, int L, int P) {
   return HST_OK;
 }
 
-
 #define HST_TRY(x)                       \
   do {                                   \
     hst_status _st = (x);                \
     if (_st != HST_OK) return _st;       \
   } while (0)
+
+// the routed step: fast table scan shapes, tables that fit the scan LDS,
+// at most 16384 cards per head
+hst_status check_route(const hst_shape* s, int L, int P) {
+  HST_TRY(check_lp(L, P));
+  if (L != 16 && L != 32 && L != 64 && L != 128) return HST_ERR_UNSUPPORTED;
+  if ((static_cast<long long>(L) << P) * 4 > 131072) return HST_ERR_UNSUPPORTED;
+  if (hst::route_chunks(s->Nmax) > hst::kRouteMaxCards) return HST_ERR_UNSUPPORTED;
+  if (hst::card_route_smem(L, P, hst::route_chunks(s->Nmax)) > 160 * 1024 - 2048)
+    return HST_ERR_UNSUPPORTED;  // the card step holds table, keys and histogram in LDS
+  return HST_OK;
+}
+
 
 }  // namespace
 
@@ -100,6 +112,11 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
   if (needk && k < 1) return HST_ERR_INVALID_ARG;
   if (needk && k > hst::kMaxSplits * 1024) return HST_ERR_UNSUPPORTED;
   if (mass && k > hst::kMassCap) return HST_ERR_UNSUPPORTED;
+  const bool routed = op == HST_OP_DECODE_SOFTLSH_ROUTED;
+  if (routed) {
+    if (k < 1) return HST_ERR_INVALID_ARG;
+    HST_TRY(check_route(shape, L, P));
+  }
   if (op == HST_OP_DECODE_SOFTLSH_MASS) {
     HST_TRY(check_lp(L, P));
     HST_TRY(check_soft_prep(shape, L, P));
@@ -121,6 +138,7 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
       break;
     }
     case HST_OP_SELECT_MASS: b = align_up(hst::mass_logits_bytes(*shape, k)); break;
+    case HST_OP_DECODE_SOFTLSH_ROUTED: b = align_up(hst::route_ws_bytes(*shape, L, P, k)); break;
     case HST_OP_DECODE_SOFTLSH_MASS: {
       const hst::FusedLayout f = hst::fused_layout(*shape, HST_OP_DECODE_SOFTLSH, L, P, k);
       if (f.nchunks > hst::kMaxChunks) return HST_ERR_UNSUPPORTED;
@@ -290,6 +308,43 @@ hst_status hst_sparse_decode_attention(const hst_shape* shape, const void* q, co
   HST_TRY(workspace_check(HST_OP_SPARSE_ATTENTION, shape, 0, 0, k, ws, ws_bytes));
   return hip_status(hst::fused_attention(*shape, q, K, V, idx, k, scale, out, lse, ws,
                                          static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_build_cards_softlsh(const hst_shape* shape, const void* K, const void* vnorm,
+                                   int norm_dtype, const void* W, int L, int P, void* card_keys,
+                                   uint8_t* card_ids, void* card_w, int32_t* card_lens,
+                                   void* stream) {
+  HST_TRY(check_shape(shape));
+  if (L < 1 || P < 1) return HST_ERR_INVALID_ARG;
+  if (P > 8 || L > 1024) return HST_ERR_UNSUPPORTED;
+  HST_TRY(check_norm_dtype(norm_dtype));
+  if (!ptr_ok(K) || !ptr_ok(vnorm) || !ptr_ok(W) || !ptr_ok(card_keys) || !ptr_ok(card_ids) ||
+      !ptr_ok(card_w) || !ptr_ok(card_lens))
+    return HST_ERR_INVALID_ARG;
+  return hip_status(hst::build_cards_softlsh(*shape, K, vnorm, norm_dtype, W, L, P, card_keys,
+                                             card_ids, card_w, card_lens,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_step_softlsh_routed(const hst_shape* shape, const void* q, const void* K,
+                                          const void* V, const void* W, int L, int P, double tau,
+                                          const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                          const uint8_t* card_ids, const void* card_w, int C,
+                                          int k, const int32_t* k_per_seq, float scale,
+                                          int32_t* idx, float* out, float* lse, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  HST_TRY(check_route(shape, L, P));
+  if (C < 1) return HST_ERR_INVALID_ARG;
+  if (C > hst::kRouteMaxChunks) return HST_ERR_UNSUPPORTED;
+  if (!ptr_ok(idx) || !ptr_ok(card_ids) || !ptr_ok(card_w)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH_ROUTED, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::fused_decode_softlsh_routed(*shape, q, K, V, W, L, P, tau, ids, vnorm,
+                                                     norm_dtype, card_ids, card_w, C, k,
+                                                     k_per_seq, scale, idx, out, lse, ws,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 static hst_status mass_p_check(double p) {

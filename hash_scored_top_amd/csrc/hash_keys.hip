@@ -614,9 +614,8 @@ static hipError_t launch_value_norms(const hst_shape& s, const void* V, int norm
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V,
-                               const void* W, int L, int P, int norm_dtype,
-                               uint8_t* ids, void* vnorm, hipStream_t st) {
+hipError_t launch_hash_ids_softlsh(const hst_shape& s, const void* K, const void* W, int L, int P,
+                                   uint8_t* ids, hipStream_t st) {
   const int BH = s.B * s.Hkv;
   hipError_t e;
   if (P == 8 && signs_mfma_ok(s, L * 8, K, W, ids)) {
@@ -634,6 +633,13 @@ hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V,
                          s.seq_lens, s.Hkv, s.Nmax, s.d, L, P, ids);
     e = hipGetLastError();
   }
+  return e;
+}
+
+hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V,
+                               const void* W, int L, int P, int norm_dtype,
+                               uint8_t* ids, void* vnorm, hipStream_t st) {
+  const hipError_t e = launch_hash_ids_softlsh(s, K, W, L, P, ids, st);
   if (e != hipSuccess) return e;
   return launch_value_norms(s, V, norm_dtype, vnorm, st);
 }

@@ -94,6 +94,33 @@ hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const vo
                                      void* ws, hipStream_t st);
 size_t decode_mass_bytes(const hst_shape& s, int L, int P, int kcap);
 
+// two-level chunk routing (route.hip)
+constexpr int kRouteMaxChunks = 256;      // chunks one routed step keeps per head
+constexpr int kRouteMaxCards = 16384;     // cards per head (Nmax <= 1M)
+int route_chunks(int Nmax);
+hipError_t launch_card_sums(const hst_shape& s, const void* K, const void* vnorm, int norm_f16,
+                            void* ckeys, void* cw, int32_t* clens, hipStream_t st);
+hipError_t launch_route_scan(const hst_shape& s, const float* tables, const int32_t* chunks, int C,
+                             const uint8_t* ids, const void* vnorm, int norm_f16, int L, int P,
+                             int out_stride, float* out, hipStream_t st);
+size_t card_route_smem(int L, int P, int Nc);
+hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint8_t* cids,
+                             const void* cw, int norm_f16, int L, int P, int C, int32_t* chunks,
+                             hipStream_t st);
+hipError_t launch_token_route(const hst_shape& s, const float* scores, int nitems,
+                              const int32_t* chunks, int C, int k, const int32_t* kps,
+                              int32_t* out, hipStream_t st);
+hipError_t build_cards_softlsh(const hst_shape& s, const void* K, const void* vnorm, int norm_dtype,
+                               const void* W, int L, int P, void* ckeys, uint8_t* cids, void* cw,
+                               int32_t* clens, hipStream_t st);
+size_t route_ws_bytes(const hst_shape& s, int L, int P, int kcap);
+hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const void* K,
+                                       const void* V, const void* W, int L, int P, double tau,
+                                       const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                       const uint8_t* cids, const void* cw, int C, int kcap,
+                                       const int32_t* kps, float scale, int32_t* idx, float* out,
+                                       float* lse, void* ws, hipStream_t st);
+
 hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* W, int L, int P, double tau, const uint8_t* ids,
                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,

@@ -147,6 +147,70 @@ hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const vo
   return launch_attend(s, a, q, K, V, idx, false, nullptr, 0, f.chunk, scale, out, lse, st);
 }
 
+hipError_t build_cards_softlsh(const hst_shape& s, const void* K, const void* vnorm, int norm_dtype,
+                               const void* W, int L, int P, void* ckeys, uint8_t* cids, void* cw,
+                               int32_t* clens, hipStream_t st) {
+  HST_CHECK(launch_card_sums(s, K, vnorm, norm_dtype == HST_F16, ckeys, cw, clens, st));
+  hst_shape sc = s;
+  sc.Nmax = route_chunks(s.Nmax);
+  sc.seq_lens = clens;
+  return launch_hash_ids_softlsh(sc, ckeys, W, L, P, cids, st);
+}
+
+// Workspace of the routed step: tables, the attention partials, the kept
+// chunks and the scores of their keys.
+struct RouteLayout {
+  size_t tables, attn, chunks, tscore, bytes;
+};
+
+static RouteLayout route_layout(const hst_shape& s, int L, int P, int kcap) {
+  RouteLayout r{};
+  const size_t BH = static_cast<size_t>(s.B) * s.Hkv;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  r.tables = take(BH * (static_cast<size_t>(L) << P) * 4);
+  r.attn = take(fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap).bytes);
+  r.chunks = take(BH * kRouteMaxChunks * 4);
+  r.tscore = take(BH * kRouteMaxChunks * 64 * 4);
+  r.bytes = o;
+  return r;
+}
+
+size_t route_ws_bytes(const hst_shape& s, int L, int P, int kcap) {
+  return route_layout(s, L, P, kcap).bytes;
+}
+
+hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const void* K,
+                                       const void* V, const void* W, int L, int P, double tau,
+                                       const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                       const uint8_t* cids, const void* cw, int C, int kcap,
+                                       const int32_t* kps, float scale, int32_t* idx, float* out,
+                                       float* lse, void* ws, hipStream_t st) {
+  const RouteLayout r = route_layout(s, L, P, kcap);
+  char* base = static_cast<char*>(ws);
+  float* tables = reinterpret_cast<float*>(base + r.tables);
+  int32_t* chunks = reinterpret_cast<int32_t*>(base + r.chunks);
+  float* tscore = reinterpret_cast<float*>(base + r.tscore);
+  const int f16 = norm_dtype == HST_F16;
+  // query tables
+  const FusedLayout fs = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
+  FusedArgs as = make_args(s, fs, nullptr, L, P, tau, 1);
+  as.tables = tables;
+  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, 0, nullptr, st));
+  // every card scored, the C best chunks kept; then the k best keys inside
+  HST_CHECK(launch_card_route(s, tables, cids, cw, f16, L, P, C, chunks, st));
+  HST_CHECK(launch_route_scan(s, tables, chunks, C, ids, vnorm, f16, L, P, C * 64, tscore, st));
+  HST_CHECK(launch_token_route(s, tscore, C * 64, chunks, C, kcap, kps, idx, st));
+  // exact attention over the original rows
+  const FusedLayout fa = fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap);
+  const FusedArgs aa = make_args(s, fa, base + r.attn, 0, 0, 0.0, kcap);
+  return launch_attend(s, aa, q, K, V, idx, false, nullptr, 0, fa.chunk, scale, out, lse, st);
+}
+
 hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,

@@ -91,7 +91,8 @@ typedef enum {
   HST_OP_DECODE_SOFTLSH = 6,
   HST_OP_DECODE_HAMMING = 7,
   HST_OP_SELECT_MASS = 8,
-  HST_OP_DECODE_SOFTLSH_MASS = 9
+  HST_OP_DECODE_SOFTLSH_MASS = 9,
+  HST_OP_DECODE_SOFTLSH_ROUTED = 10
 } hst_op;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -305,6 +306,52 @@ hst_status hst_decode_step_softlsh_mass(const hst_shape* shape, const void* q,
                                         int32_t* counts, float* out,
                                         float* lse, void* ws, size_t ws_bytes,
                                         void* stream);
+
+/*
+ * Index cards of 64-token chunks [HGA, section 2, step 1: the context is
+ * cut into 64-token chunks, each summarised on a small card that the query
+ * scans first].  For chunk c of (b, h) (keys 64c .. min(64c+64, N_b) - 1):
+ *   card_keys[b][h][c] = sum of the chunk's keys, accumulated in float64 in
+ *                        index order and rounded to the KV type (bf16: to
+ *                        float32, then to bf16, both to nearest even)
+ *   card_ids[b][h][c]  = bucket ids of that card key, as
+ *                        hst_hash_keys_softlsh computes them for a key
+ *   card_w[b][h][c]    = the largest stored value norm of the chunk
+ *                        (norm_dtype, as vnorm)
+ *   card_lens[b]       = ceil(N_b / 64)
+ * Arrays have Nc = ceil(Nmax / 64) cards per head; cards c >= card_lens[b]
+ * are not written.  vnorm is the output of hst_hash_keys_softlsh.  Same
+ * requirements as hst_hash_keys_softlsh; no workspace.
+ */
+hst_status hst_build_cards_softlsh(const hst_shape* shape, const void* K,
+                                   const void* vnorm, int norm_dtype,
+                                   const void* W, int L, int P, void* card_keys,
+                                   uint8_t* card_ids, void* card_w,
+                                   int32_t* card_lens, void* stream);
+
+/*
+ * Soft-LSH decode step with two-level routing [HGA, section 2: chunk
+ * routing on the cards, token routing inside the chosen chunks, exact
+ * attention over the original tokens].  The query tables of
+ * hst_score_keys_softlsh score every card (card_w times the table mass of
+ * its buckets); the C cards first in the order (score descending, chunk
+ * ascending) are kept; every key of those chunks is scored as in
+ * hst_score_keys_softlsh; the k (or k_per_seq[b]) keys first in the order
+ * (score descending, index ascending) among them are attended as in
+ * hst_sparse_decode_attention.  idx [B][Hkv][k] receives them ascending,
+ * then -1.  1 <= C <= 256; L in {16, 32, 64, 128}; Nmax <= 1048576.
+ */
+hst_status hst_decode_step_softlsh_routed(const hst_shape* shape, const void* q,
+                                          const void* K, const void* V,
+                                          const void* W, int L, int P,
+                                          double tau, const uint8_t* ids,
+                                          const void* vnorm, int norm_dtype,
+                                          const uint8_t* card_ids,
+                                          const void* card_w, int C, int k,
+                                          const int32_t* k_per_seq, float scale,
+                                          int32_t* idx, float* out, float* lse,
+                                          void* ws, size_t ws_bytes,
+                                          void* stream);
 
 #ifdef __cplusplus
 }
