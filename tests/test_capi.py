@@ -162,3 +162,27 @@ def test_mass_entry_points_validate_before_launch():
                                           L.HST_F16, 100, None, 0.9, 0.1, FAKE, FAKE, FAKE, None,
                                           FAKE, 100, None) == -3
     assert C.hst_last_hip_error() == 0
+
+
+def test_routing_entry_points_validate_before_launch():
+    L = _lib()
+    C = L._C
+    sh = _shape(L)
+    by = ctypes.byref(sh)
+    big = 1 << 30
+    args = lambda Lt, Cc, ws: (by, FAKE, FAKE, FAKE, FAKE, Lt, 8, 0.3, FAKE, FAKE, L.HST_F16,
+                               FAKE, FAKE, Cc, 100, None, 0.1, FAKE, FAKE, None, FAKE, ws, None)
+    assert C.hst_decode_step_softlsh_routed(*args(64, 0, big)) == -1      # C < 1
+    assert C.hst_decode_step_softlsh_routed(*args(64, 257, big)) == -2    # C > 256
+    assert C.hst_decode_step_softlsh_routed(*args(48, 8, big)) == -2      # L not 16/32/64/128
+    assert C.hst_decode_step_softlsh_routed(*args(64, 8, 100)) == -3      # workspace
+    need = L.workspace_size(L.HST_OP_DECODE_SOFTLSH_ROUTED, sh, 64, 8, k=100)
+    assert need > 2 * 2 * 256 * 64 * 4                                    # key scores of 256 chunks
+    # cards: null output, bad norm dtype, P > 8
+    assert C.hst_build_cards_softlsh(by, FAKE, FAKE, L.HST_F16, FAKE, 64, 8, FAKE, FAKE, FAKE,
+                                     None, None) == -1
+    assert C.hst_build_cards_softlsh(by, FAKE, FAKE, L.HST_BF16, FAKE, 64, 8, FAKE, FAKE, FAKE,
+                                     FAKE, None) == -2
+    assert C.hst_build_cards_softlsh(by, FAKE, FAKE, L.HST_F16, FAKE, 64, 9, FAKE, FAKE, FAKE,
+                                     FAKE, None) == -2
+    assert C.hst_last_hip_error() == 0
