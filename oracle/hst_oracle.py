@@ -61,7 +61,7 @@ __all__ = [
     "binary_codes", "query_tables", "score_softlsh", "score_hamming",
     "select_topk", "attend", "decode_slab_softlsh", "decode_slab_hamming",
     "append_tokens", "select_mass", "chunk_card_keys", "chunk_cards_softlsh",
-    "route_slab_softlsh",
+    "route_slab_softlsh", "decode_shared_prefix_softlsh",
 ]
 
 _U64 = 2.0 ** -53
@@ -404,3 +404,18 @@ def route_slab_softlsh(qg, K, V, W, L, P, tau, k, C, norm_dtype, storage, scale=
     out, lse = attend(qg, K, V, idx, scale)
     return {"cards": cards, "T": T, "chunk_scores": cscore, "chunks": chunks, "keys": keys,
             "scores": s, "idx": idx, "out": out, "lse": lse}
+
+
+def decode_shared_prefix_softlsh(qg, Kp, Vp, Ks, Vs, W, L, P, tau, k, norm_dtype,
+                                 scale=None) -> dict:
+    """Decode step of one sequence whose context is a prefix shared by the
+    batch followed by its own suffix (bifurcated-attention page, sections 1
+    and 3: the shared context and each sample's incremental part are kept
+    apart so the shared part is read once for the whole batch).
+
+    The result is the plain step over the concatenated context: key j < Np
+    is prefix key j, key Np + j is suffix key j.
+    """
+    K = np.concatenate([np.asarray(Kp, dtype=np.float64), np.asarray(Ks, dtype=np.float64)])
+    V = np.concatenate([np.asarray(Vp, dtype=np.float64), np.asarray(Vs, dtype=np.float64)])
+    return decode_slab_softlsh(qg, K, V, W, L, P, tau, k, norm_dtype, scale=scale)

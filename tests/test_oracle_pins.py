@@ -555,6 +555,32 @@ def test_routing_reduces_to_plain_topk_and_keeps_chosen_chunks():
         assert abs(cs[c] - cw[c] * sum(T[l, cid[c, l]] for l in range(L))) <= 1e-12 * cs[c]
 
 
+def test_shared_prefix_is_the_step_over_the_concatenated_context():
+    # The prefix comes first: a planted key at suffix position j is index
+    # Np + j, and a batch of sequences sharing a prefix gives, sequence by
+    # sequence, the plain step over prefix + own suffix.
+    rng = np.random.default_rng(12)
+    L, P, d, G, tau = 8, 4, 16, 2, 0.3
+    Np, Ns = 150, 40
+    W = rng.standard_normal((L * P, d))
+    Kp, Vp = rng.standard_normal((Np, d)), rng.standard_normal((Np, d))
+    qg = np.repeat(rng.standard_normal((1, d)) * 3.0, G, axis=0)
+    Ks, Vs = rng.standard_normal((Ns, d)), rng.standard_normal((Ns, d))
+    Ks[7] = 4.0 * qg[0] / np.linalg.norm(qg[0])   # in every query bucket
+    Vs[7] *= 10.0                                  # and the largest value norm
+    r = O.decode_shared_prefix_softlsh(qg, Kp, Vp, Ks, Vs, W, L, P, tau, 1, "f32")
+    np.testing.assert_array_equal(r["idx"], [Np + 7])
+    r2 = O.decode_shared_prefix_softlsh(qg, Kp, Vp, Ks, Vs, W, L, P, tau, 12, "f32")
+    full = O.decode_slab_softlsh(qg, np.concatenate([Kp, Ks]), np.concatenate([Vp, Vs]), W, L,
+                                 P, tau, 12, "f32")
+    np.testing.assert_array_equal(r2["idx"], full["idx"])
+    # no suffix: the step over the prefix alone
+    r3 = O.decode_shared_prefix_softlsh(qg, Kp, Vp, Ks[:0], Vs[:0], W, L, P, tau, 12, "f32")
+    alone = O.decode_slab_softlsh(qg, Kp, Vp, W, L, P, tau, 12, "f32")
+    np.testing.assert_array_equal(r3["idx"], alone["idx"])
+    np.testing.assert_allclose(r3["out"], alone["out"], rtol=0, atol=0)
+
+
 # ---------------------------------------------------------------- attention
 
 def test_attend_all_keys_equals_dense_sdpa():
