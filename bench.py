@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of a captured graph")
@@ -166,6 +167,75 @@ def cpu_baseline(w, x, seconds):
                        f"(tables/codes, scores, top-k, attention) x{reps}, float64 numpy, one "
                        f"thread; step time = mean slab time x {w.B * w.Hkv}"),
             "seconds": round(dt, 2), "step_s": t_step}
+
+
+SHARED_B, SHARED_NP, SHARED_NS = 8, 32768, 2048
+
+
+def shared_leg(hst, w, Wp, dev, stream, capture, copies=3, reps=10):
+    """Shared-prefix step against the plain step on the same data laid out
+    whole, each timed over `copies` rotated input copies by graph replay.
+    Data: seeded normal keys, values and queries in the KV dtype; suffix
+    lengths uniform in [SHARED_NS / 4, SHARED_NS]; k_b = ceil(N_b / 33)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(20260101)
+    B, Hkv, Hq, d, Np, Ns = SHARED_B, w.Hkv, w.Hq, w.d, SHARED_NP, SHARED_NS
+    dt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    nd = torch.float16 if w.norm_dtype == "f16" else torch.float32
+    slens = torch.randint(Ns // 4, Ns + 1, (B,), generator=g, device=dev, dtype=torch.int32)
+    ctx = (Np + slens).to(torch.int64)
+    kps = ((ctx + 32) // 33).to(torch.int32)
+    kmax = int(kps.max())
+    q = torch.randn((B, Hq, d), generator=g, device=dev).to(dt)
+    sets, whole = [], []
+    for _ in range(copies):
+        Kp = torch.randn((1, Hkv, Np, d), generator=g, device=dev).to(dt)
+        Vp = torch.randn((1, Hkv, Np, d), generator=g, device=dev).to(dt)
+        Ks = torch.randn((B, Hkv, Ns, d), generator=g, device=dev).to(dt)
+        Vs = torch.randn((B, Hkv, Ns, d), generator=g, device=dev).to(dt)
+        ip, vp = hst.hst_hash_keys_softlsh(Kp, Vp, Wp, w.L, w.P, nd)
+        is_, vs_ = hst.hst_hash_keys_softlsh(Ks, Vs, Wp, w.L, w.P, nd, seq_lens=slens)
+        sets.append((Kp, Vp, ip, vp, Ks, Vs, is_, vs_))
+        Kc = torch.cat([Kp.expand(B, -1, -1, -1), Ks], dim=2).contiguous()
+        Vc = torch.cat([Vp.expand(B, -1, -1, -1), Vs], dim=2).contiguous()
+        clen = (Np + slens).to(torch.int32)
+        ic, vc = hst.hst_hash_keys_softlsh(Kc, Vc, Wp, w.L, w.P, nd, seq_lens=clen)
+        whole.append((Kc, Vc, ic, vc))
+    clen = (Np + slens).to(torch.int32)
+    sstep = hst.DecodeSoftLSHShared(sets[0][4], Np, Hq, w.L, w.P, w.tau, kmax, nd, seq_lens=slens,
+                                    k_per_seq=kps)
+    pstep = hst.DecodeSoftLSH(whole[0][0], Hq, w.L, w.P, w.tau, kmax, nd, seq_lens=clen,
+                              k_per_seq=kps)
+    srun = lambda i: sstep(q, *sets[i % copies][:4], *sets[i % copies][4:], Wp)
+    prun = lambda i: pstep(q, whole[i % copies][0], whole[i % copies][1], Wp, whole[i % copies][2],
+                           whole[i % copies][3])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        gr = capture(lambda: [fn(i) for i in range(copies)])
+        gr.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record(stream)
+            gr.replay()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e3 / copies)
+        return sorted(ts)[len(ts) // 2]
+
+    sus, pus = timed(srun), timed(prun)
+    e = torch.tensor([], dtype=dt).element_size()
+    m = w.L + torch.tensor([], dtype=nd).element_size()
+    ktot = int(kps.sum()) * Hkv
+    gath = ktot * 2 * d * e
+    qo = B * Hq * d * (e + 4)
+    sbytes = Hkv * Np * m + int(slens.sum()) * Hkv * m + gath + qo
+    pbytes = int(ctx.sum()) * Hkv * m + gath + qo
+    return {"B": B, "prefix": Np, "suffix_max": Ns, "us": sus, "plain_us": pus,
+            "speedup": pus / sus, "alg_bytes": sbytes, "plain_alg_bytes": pbytes,
+            "hbm_frac": sbytes / (sus * 1e-6) / (HBM_PEAK_GBS * 1e9)}
 
 
 def main():
@@ -447,6 +517,15 @@ def main():
         log(f"routed step (C={C}) {routed_us:.2f} us, {rbytes / 1e6:.1f} MB")
         del rstep, cards
 
+    # shared-prefix variant (soft-LSH): a batch of SHARED_B sequences with a
+    # common SHARED_NP-key prefix and ragged own suffixes, against the plain
+    # step on the materialised concatenation of the same data
+    shared = None
+    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128) and not args.no_shared:
+        shared = shared_leg(hst, w, Wp, dev, stream, capture)
+        log(f"shared-prefix step {shared['us']:.2f} us vs {shared['plain_us']:.2f} us "
+            f"materialised ({shared['speedup']:.2f}x)")
+
     # dense attention over every cached key, for the sparse/dense ratio
     dense = None
     if w.B * w.Hkv * w.N <= (1 << 24):
@@ -502,6 +581,7 @@ def main():
         "append": append,
         "mass": mass,
         "routed": routed,
+        "shared": shared,
         "dense": dense,
     }
     if not args.no_cpu_baseline:

@@ -31,7 +31,7 @@ EXPORTED = (
     "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
     "hst_score_scan_softlsh", "hst_append_kv_softlsh", "hst_append_kv_binary",
     "hst_select_mass", "hst_decode_step_softlsh_mass", "hst_build_cards_softlsh",
-    "hst_decode_step_softlsh_routed",
+    "hst_decode_step_softlsh_routed", "hst_decode_step_softlsh_shared", "hst_workspace_size_shared",
 )
 
 
@@ -76,6 +76,9 @@ def _load() -> ctypes.CDLL:
         "hst_decode_step_hamming": ([SH, P, P, P, P, I, P, I, P, F, P, P, P, P, SZ, P], I),
         "hst_select_mass": ([SH, P, P, P, I, D, F, P, P, P, SZ, P], I),
         "hst_build_cards_softlsh": ([SH, P, P, I, P, I, I, P, P, P, P, P], I),
+        "hst_decode_step_softlsh_shared": ([SH, I, P, P, P, P, P, P, P, P, P, P, I, I, D, I, I, P,
+                                            F, P, P, P, P, SZ, P], I),
+        "hst_workspace_size_shared": ([SH, I, I, I, I, ctypes.POINTER(SZ)], I),
         "hst_decode_step_softlsh_routed": ([SH, P, P, P, P, I, I, D, P, P, I, P, P, I, I, P, F, P,
                                             P, P, P, SZ, P], I),
         "hst_decode_step_softlsh_mass": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, D, F, P, P, P,
@@ -476,4 +479,39 @@ class DecodeSoftLSHRouted:
             self.tau, _ptr(ids), _ptr(vnorm), self.norm_code, _ptr(card_ids), _ptr(card_w),
             self.C, self.k, _ptr(self.k_per_seq), self.scale, _ptr(self.idx), _ptr(self.out),
             _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st), "hst_decode_step_softlsh_routed")
+        return self.idx, self.out, self.lse
+
+
+class DecodeSoftLSHShared:
+    """Pre-sized soft-LSH decode step for a batch sharing a prefix: K / V /
+    ids / vnorm of the suffixes [B,Hkv,Ns,...] plus the prefix cache
+    [Hkv,Np,...] (a batch of one); indices are into prefix + suffix."""
+
+    def __init__(self, Ks, Np: int, Hq: int, L: int, P: int, tau: float, k: int, norm_dtype,
+                 seq_lens=None, k_per_seq=None, scale: Optional[float] = None):
+        B, Hkv, Ns, d = Ks.shape
+        self.shape = make_shape(Ks, Hq, seq_lens)
+        self._keep = (seq_lens, k_per_seq)
+        self.Np, self.L, self.P, self.tau, self.k = Np, L, P, float(tau), k
+        self.norm_code = _norm_code(norm_dtype)
+        self.scale = float(d ** -0.5 if scale is None else scale)
+        dev = Ks.device
+        self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        nbytes = ctypes.c_size_t(0)
+        _check(_C.hst_workspace_size_shared(ctypes.byref(self.shape), Np, L, P, k,
+                                            ctypes.byref(nbytes)), "hst_workspace_size_shared")
+        self.ws = _workspace(nbytes.value, dev)
+        self.k_per_seq = k_per_seq
+
+    def __call__(self, q, Kp, Vp, ids_p, vn_p, Ks, Vs, ids_s, vn_s, W,
+                 stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_step_softlsh_shared(
+            ctypes.byref(self.shape), self.Np, _ptr(q), _ptr(Kp), _ptr(Vp), _ptr(ids_p),
+            _ptr(vn_p), _ptr(Ks), _ptr(Vs), _ptr(ids_s), _ptr(vn_s), _ptr(W), self.L, self.P,
+            self.tau, self.norm_code, self.k, _ptr(self.k_per_seq), self.scale, _ptr(self.idx),
+            _ptr(self.out), _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st),
+            "hst_decode_step_softlsh_shared")
         return self.idx, self.out, self.lse

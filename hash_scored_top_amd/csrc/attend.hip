@@ -93,7 +93,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   int32_t* rows = reinterpret_cast<int32_t*>(sm + 65536 + 8192 + (nchunks + 1) * 4);
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
-  const int n = seq_len(seq_lens, b, a.Nmax);
+  const int n = seq_len(seq_lens, b, a.Nmax) + (SELECT ? 0 : a.np);
   const int split = blockIdx.x, nsplit = gridDim.x;
   const int r0 = split * a.rps, r1 = min(r0 + a.rps, a.kcap);
   const int t = threadIdx.x, sub = t & 15, grp = t >> 4, lane = t & 63, wave = t >> 6;
@@ -151,18 +151,25 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     // whenever the head exists) and is skipped below
     typename RowLd<T, EPL>::raw kr[U], vr[U];
     bool ok[U];
-    long long off[U];
+    const T* kp[U];
+    const T* vp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = rb + u * NG;
       const int j = r < nrows ? rows[r] : -1;
       ok[u] = j >= 0 && j < n;
-      off[u] = (kvb + (ok[u] ? j : 0)) * D + sub * EPL;
+      const int jj = ok[u] ? j : 0;
+      // a shared prefix row, or a row of the sequence's own cache
+      const bool pre = !SELECT && jj < a.np;
+      const long long off = pre ? (static_cast<long long>(h) * a.np + jj) * D + sub * EPL
+                                : (kvb + (jj - (SELECT ? 0 : (ok[u] ? a.np : 0)))) * D + sub * EPL;
+      kp[u] = (pre ? static_cast<const T*>(a.pk) : K) + off;
+      vp[u] = (pre ? static_cast<const T*>(a.pv) : V) + off;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      kr[u] = RowLd<T, EPL>::load(K + off[u]);
-      vr[u] = RowLd<T, EPL>::load(V + off[u]);
+      kr[u] = RowLd<T, EPL>::load(kp[u]);
+      vr[u] = RowLd<T, EPL>::load(vp[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

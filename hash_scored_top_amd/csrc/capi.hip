@@ -347,6 +347,59 @@ hst_status hst_decode_step_softlsh_routed(const hst_shape* shape, const void* q,
                                                      static_cast<hipStream_t>(stream)));
 }
 
+static hst_status shared_checks(const hst_shape* shape, int Np, int L, int P, int k,
+                                size_t* need) {
+  HST_TRY(check_shape(shape));
+  if (Np < 0 || k < 1) return HST_ERR_INVALID_ARG;
+  if (static_cast<long long>(Np) + shape->Nmax > (1 << 30)) return HST_ERR_UNSUPPORTED;
+  HST_TRY(check_lp(L, P));
+  if (L != 16 && L != 32 && L != 64 && L != 128) return HST_ERR_UNSUPPORTED;
+  if ((static_cast<long long>(L) * ((1 << P) + 1)) * 4 > 160 * 1024 - 1024) return HST_ERR_UNSUPPORTED;
+  HST_TRY(check_soft_prep(shape, L, P));
+  // the selection runs over the whole context
+  hst_shape v = *shape;
+  v.Nmax = Np + shape->Nmax;
+  v.seq_lens = nullptr;
+  size_t sel = 0;
+  HST_TRY(hst_workspace_size(HST_OP_SELECT_TOPK, &v, 0, 0, 128, k, &sel));
+  size_t att = 0;
+  HST_TRY(hst_workspace_size(HST_OP_SPARSE_ATTENTION, shape, 0, 0, 128, k, &att));
+  *need = align_up(hst::shared_ws_bytes(*shape, Np, L, P, k));
+  return HST_OK;
+}
+
+hst_status hst_workspace_size_shared(const hst_shape* shape, int Np, int L, int P, int k,
+                                     size_t* bytes) {
+  if (bytes == nullptr) return HST_ERR_INVALID_ARG;
+  size_t need = 0;
+  HST_TRY(shared_checks(shape, Np, L, P, k, &need));
+  *bytes = need;
+  return HST_OK;
+}
+
+hst_status hst_decode_step_softlsh_shared(const hst_shape* shape, int Np, const void* q,
+                                          const void* Kp, const void* Vp, const uint8_t* ids_p,
+                                          const void* vnorm_p, const void* Ks, const void* Vs,
+                                          const uint8_t* ids_s, const void* vnorm_s,
+                                          const void* W, int L, int P, double tau,
+                                          int norm_dtype, int k, const int32_t* k_per_seq,
+                                          float scale, int32_t* idx, float* out, float* lse,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  HST_TRY(shared_checks(shape, Np, L, P, k, &need));
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids_s, vnorm_s, norm_dtype));
+  HST_TRY(attention_checks(shape, q, Ks, Vs, k, scale, out, lse));
+  if (Np > 0 && (!ptr_ok(Kp) || !ptr_ok(Vp) || !ptr_ok(ids_p) || !ptr_ok(vnorm_p)))
+    return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  if (ws_bytes < need) return HST_ERR_WORKSPACE;
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return HST_ERR_INVALID_ARG;
+  return hip_status(hst::fused_decode_softlsh_shared(
+      *shape, Np, q, Kp, Vp, ids_p, vnorm_p, Ks, Vs, ids_s, vnorm_s, W, L, P, tau, norm_dtype, k,
+      k_per_seq, scale, idx, out, lse, ws, static_cast<hipStream_t>(stream)));
+}
+
 static hst_status mass_p_check(double p) {
   return (p > 0.0 && p <= 1.0) ? HST_OK : HST_ERR_INVALID_ARG;  // NaN fails both
 }

@@ -51,6 +51,11 @@ struct FusedArgs {
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index)
   float* part_o;     // [B*Hq][nsplit][d]
   float* part_ml;    // [B*Hq][nsplit][2]
+  // shared prefix (attention over given rows only): rows j < np come from
+  // pk / pv [Hkv][np][d], rows np + j from K / V row j of the sequence
+  const void* pk;
+  const void* pv;
+  int np;
 };
 __host__ __device__ inline int a_nsplit(const FusedArgs& a) { return a.nsplit; }
 __host__ __device__ inline size_t hst_align16(size_t x) { return (x + 15) / 16 * 16; }
@@ -120,6 +125,20 @@ hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const 
                                        const uint8_t* cids, const void* cw, int C, int kcap,
                                        const int32_t* kps, float scale, int32_t* idx, float* out,
                                        float* lse, void* ws, hipStream_t st);
+
+// shared-prefix decode (shared.hip)
+hipError_t launch_shared_lens(const hst_shape& s, int Np, int32_t* v_lens, hipStream_t st);
+hipError_t launch_scan_shared(const hst_shape& s, const FusedArgs& a, int Np,
+                              const uint8_t* ids_p, const void* vn_p, const uint8_t* ids_s,
+                              const void* vn_s, int norm_f16, float* scores_out, hipStream_t st);
+size_t shared_ws_bytes(const hst_shape& s, int Np, int L, int P, int kcap);
+hipError_t fused_decode_softlsh_shared(const hst_shape& s, int Np, const void* q, const void* Kp,
+                                       const void* Vp, const uint8_t* ids_p, const void* vn_p,
+                                       const void* Ks, const void* Vs, const uint8_t* ids_s,
+                                       const void* vn_s, const void* W, int L, int P, double tau,
+                                       int norm_dtype, int kcap, const int32_t* kps, float scale,
+                                       int32_t* idx, float* out, float* lse, void* ws,
+                                       hipStream_t st);
 
 hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* W, int L, int P, double tau, const uint8_t* ids,

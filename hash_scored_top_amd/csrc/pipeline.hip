@@ -211,6 +211,75 @@ hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const 
   return launch_attend(s, aa, q, K, V, idx, false, nullptr, 0, fa.chunk, scale, out, lse, st);
 }
 
+// Workspace of the shared-prefix step: tables, the context lengths, the
+// scores of every context key, the selection's workspace, the attention
+// partials.
+struct SharedLayout {
+  size_t tables, vlens, scores, select, attn, bytes;
+};
+
+static hst_shape shared_context_shape(const hst_shape& s, int Np, const int32_t* vlens) {
+  hst_shape v = s;
+  v.Nmax = Np + s.Nmax;
+  v.seq_lens = s.seq_lens != nullptr ? vlens : nullptr;
+  return v;
+}
+
+static SharedLayout shared_layout(const hst_shape& s, int Np, int L, int P, int kcap) {
+  SharedLayout r{};
+  const size_t BH = static_cast<size_t>(s.B) * s.Hkv;
+  const hst_shape v = shared_context_shape(s, Np, nullptr);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  r.tables = take(BH * (static_cast<size_t>(L) << P) * 4);
+  r.vlens = take(static_cast<size_t>(s.B) * 4);
+  r.scores = take(BH * static_cast<size_t>(v.Nmax) * 4);
+  r.select = take(fused_layout(v, HST_OP_SELECT_TOPK, 0, 0, kcap).bytes);
+  r.attn = take(fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap).bytes);
+  r.bytes = o;
+  return r;
+}
+
+size_t shared_ws_bytes(const hst_shape& s, int Np, int L, int P, int kcap) {
+  return shared_layout(s, Np, L, P, kcap).bytes;
+}
+
+hipError_t fused_decode_softlsh_shared(const hst_shape& s, int Np, const void* q, const void* Kp,
+                                       const void* Vp, const uint8_t* ids_p, const void* vn_p,
+                                       const void* Ks, const void* Vs, const uint8_t* ids_s,
+                                       const void* vn_s, const void* W, int L, int P, double tau,
+                                       int norm_dtype, int kcap, const int32_t* kps, float scale,
+                                       int32_t* idx, float* out, float* lse, void* ws,
+                                       hipStream_t st) {
+  const SharedLayout r = shared_layout(s, Np, L, P, kcap);
+  char* base = static_cast<char*>(ws);
+  float* tables = reinterpret_cast<float*>(base + r.tables);
+  int32_t* vlens = reinterpret_cast<int32_t*>(base + r.vlens);
+  float* scores = reinterpret_cast<float*>(base + r.scores);
+  const hst_shape v = shared_context_shape(s, Np, vlens);
+  // query tables, context lengths, the scores of every context key
+  const FusedLayout fs = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
+  FusedArgs as = make_args(s, fs, nullptr, L, P, tau, 1);
+  as.tables = tables;
+  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, 0, nullptr, st));
+  if (s.seq_lens != nullptr) HST_CHECK(launch_shared_lens(s, Np, vlens, st));
+  HST_CHECK(launch_scan_shared(s, as, Np, ids_p, vn_p, ids_s, vn_s, norm_dtype == HST_F16, scores,
+                               st));
+  // exact top-k over the whole context
+  HST_CHECK(fused_select(v, HST_F32, scores, kcap, kps, idx, base + r.select, st));
+  // attention: rows below Np from the prefix cache
+  const FusedLayout fa = fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap);
+  FusedArgs aa = make_args(s, fa, base + r.attn, 0, 0, 0.0, kcap);
+  aa.pk = Kp;
+  aa.pv = Vp;
+  aa.np = Np;
+  return launch_attend(s, aa, q, Ks, Vs, idx, false, nullptr, 0, fa.chunk, scale, out, lse, st);
+}
+
 hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,

@@ -30,6 +30,7 @@
 #include "hst_common.h"
 #include "hst_fused.h"
 #include "hst_launch.h"
+#include "table_lds.h"
 
 namespace hst {
 
@@ -82,35 +83,6 @@ card_sum_kernel(const T* __restrict__ K, const void* __restrict__ vnorm, int nor
   }
 }
 
-// The head's bucket-major table [2^P][L] (global) into LDS as table-major
-// rows of pitch 2^P + 1 (the pad puts consecutive tables of one bucket in
-// consecutive banks).  Vector loads, four per thread in flight before any
-// store.
-template <int NT>
-__device__ __forceinline__ void load_table_t(const float* __restrict__ Tg, float* tl, int L, int nb) {
-  const int n4 = (nb * L) / 4;  // nb * L is a multiple of 16
-  const u32x4* src = reinterpret_cast<const u32x4*>(Tg);
-  for (int base = 0; base < n4; base += 4 * NT) {
-    u32x4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * NT + static_cast<int>(threadIdx.x);
-      if (i < n4) v[u] = src[i];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * NT + static_cast<int>(threadIdx.x);
-      if (i < n4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = 4 * i + q, bk = e / L, l = e % L;
-          tl[l * (nb + 1) + bk] = __uint_as_float(v[u][q]);
-        }
-      }
-    }
-  }
-}
-
 // Scores of the keys of the chosen chunks: out[bh][slot * 64 + i] for key
 // chunk * 64 + i of the slot-th chosen chunk; -1 where there is no key.
 template <int L>
@@ -138,19 +110,7 @@ route_scan_kernel(const float* __restrict__ tables, const int32_t* __restrict__ 
                            : static_cast<const float*>(vnorm)[row];
   load_table_t<kRouteNT>(Tg, tl, L, nb);
   __syncthreads();
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < L / 16; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t word = idv[i][q];
-#pragma unroll
-      for (int by = 0; by < 4; ++by) {
-        const int l = i * 16 + q * 4 + by;
-        s += tl[l * (nb + 1) + ((word >> (8 * by)) & 0xffu)];
-      }
-    }
-  }
+  const float s = table_sum<L>(idv, tl, nb);
   if (slot < C)
     out[static_cast<long long>(bh) * out_stride + slot * kChunkTok + (t % kChunkTok)] = ok ? w * s : -1.0f;
 }

@@ -305,6 +305,74 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 
+// Soft-LSH scan of a batch that shares a prefix (scores only).  The
+// context of sequence b is the Np prefix keys (metadata [Hkv][Np], one copy)
+// then its own suffix (metadata [B*Hkv][Ns]); scores of (b, h) go to row
+// bh of `scores_out` (pitch Np + Ns): prefix key j at j, suffix key j at
+// Np + j.  1-D grid: prefix chunks first, B workgroups per (kv head, chunk)
+// with block ids congruent modulo 8 and within 8*B consecutive ids, so they
+// run on one XCD at about the same time and the prefix metadata is fetched
+// from HBM once; then B*Hkv*nchs suffix chunks.
+template <int LANES, int U, bool F16>
+__global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))
+scan_shared_kernel(const uint8_t* __restrict__ ids_p, const void* __restrict__ vn_p, int Np,
+                   const uint8_t* __restrict__ ids_s, const void* __restrict__ vn_s,
+                   const int32_t* __restrict__ s_lens, int Ns, int B, int nchp, int pitems_pad,
+                   int nchs, float* __restrict__ scores_out, FusedArgs a) {
+  constexpr int NT = kScanNT;
+  using S = SoftScorer<LANES, NT, U, F16>;
+  constexpr int CH = kSoftChunk;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ BlockScratch<NT> sc;
+  float* tbl = reinterpret_cast<float*>(smem_raw);
+  float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);
+  const int w = blockIdx.x, Hkv = a.Hkv;
+  const int npre = pitems_pad * B;
+  int b, h, chunk;
+  bool pre;
+  if (w < npre) {
+    const int grp = w / (8 * B), rem = w % (8 * B);
+    b = rem / 8;
+    const int item = grp * 8 + rem % 8;
+    if (item >= Hkv * nchp) return;  // padding of the last group
+    h = item / nchp;
+    chunk = item % nchp;
+    pre = true;
+  } else {
+    const int v = w - npre, bhv = v / nchs;
+    chunk = v % nchs;
+    b = bhv / Hkv;
+    h = bhv % Hkv;
+    pre = false;
+  }
+  const int bh = b * Hkv + h;
+  const int n = pre ? Np : seq_len(s_lens, b, Ns);
+  const int j0 = chunk * CH;
+  if (j0 >= n) return;
+  const int jend = min(j0 + CH, n);
+  const long long mbase = pre ? static_cast<long long>(h) * Np : static_cast<long long>(bh) * Ns;
+  S sco;
+  sco.idv = reinterpret_cast<const uint4*>(pre ? ids_p : ids_s);
+  sco.vnorm = pre ? vn_p : vn_s;
+  sco.tbl = tbl;
+  sco.idmask = (1u << a.P) - 1u;
+  sco.setup();
+  uint4 wv[U];
+  uint32_t nr[U];
+  sco.load(wv, nr, mbase, j0 + sco.grp, jend);
+  {
+    const int nflt = S::L << a.P;
+    copy_to_lds<NT, 4>(reinterpret_cast<u32x4*>(tbl),
+                       reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt), nflt / 4);
+  }
+  __syncthreads();
+  soft_score_tiles<CH / S::TILE>(sco, mbase, j0, jend, wv, nr, tile);
+  __syncthreads();
+  const long long obase = static_cast<long long>(bh) * (Np + Ns) + (pre ? 0 : Np);
+  scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, obase,
+                                 reinterpret_cast<uint32_t*>(scores_out), 0u, false, nullptr, sc);
+}
+
 // One-lane-per-key scans: soft-LSH with any L, binary codes, given scores.
 template <int KIND>
 __global__ void __launch_bounds__(kScanNT)
@@ -480,6 +548,49 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
     default:
       return launch_scan_lane_t<kScanGivenI32>(grid, a, src, nullptr, 0, sl, kps, nullptr, filter, nch, st);
   }
+}
+
+template <int LANES, bool F16>
+static hipError_t launch_scan_shared_t(dim3 grid, const FusedArgs& a, const uint8_t* ids_p,
+                                       const void* vn_p, int Np, const uint8_t* ids_s,
+                                       const void* vn_s, const int32_t* sl, int Ns, int B,
+                                       int nchp, int pitems_pad, int nchs, float* sout,
+                                       hipStream_t st) {
+  const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
+  auto kern = scan_shared_kernel<LANES, kScanSoftU, F16>;
+  hipError_t e = lds_limit(kern, smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids_p, vn_p, Np, ids_s, vn_s, sl, Ns, B,
+                     nchp, pitems_pad, nchs, sout, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_shared(const hst_shape& s, const FusedArgs& a_in, int Np,
+                              const uint8_t* ids_p, const void* vn_p, const uint8_t* ids_s,
+                              const void* vn_s, int norm_f16, float* scores_out, hipStream_t st) {
+  FusedArgs a = a_in;
+  a.region_bytes = static_cast<int>(hst_align16(static_cast<size_t>(a.L << a.P) * 4));
+  const int nchp = (Np + kSoftChunk - 1) / kSoftChunk;
+  const int nchs = (s.Nmax + kSoftChunk - 1) / kSoftChunk;
+  const int pitems_pad = (s.Hkv * nchp + 7) / 8 * 8;
+  const long long nblk = static_cast<long long>(pitems_pad) * s.B +
+                         static_cast<long long>(s.B) * s.Hkv * nchs;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(nblk));
+#define HST_SSH(LN)                                                                           \
+  return norm_f16 ? launch_scan_shared_t<LN, true>(grid, a, ids_p, vn_p, Np, ids_s, vn_s,     \
+                                                  s.seq_lens, s.Nmax, s.B, nchp, pitems_pad, \
+                                                  nchs, scores_out, st)                      \
+                  : launch_scan_shared_t<LN, false>(grid, a, ids_p, vn_p, Np, ids_s, vn_s,    \
+                                                   s.seq_lens, s.Nmax, s.B, nchp,            \
+                                                   pitems_pad, nchs, scores_out, st)
+  switch (a.L) {
+    case 16: HST_SSH(1);
+    case 32: HST_SSH(2);
+    case 64: HST_SSH(4);
+    default: HST_SSH(8);
+  }
+#undef HST_SSH
 }
 
 }  // namespace hst

@@ -353,6 +353,40 @@ hst_status hst_decode_step_softlsh_routed(const hst_shape* shape, const void* q,
                                           void* ws, size_t ws_bytes,
                                           void* stream);
 
+/*
+ * Soft-LSH decode step for a batch that shares a prefix [bifurcated
+ * attention, sections 1 and 3: the shared context is kept apart from each
+ * sample's own part and read once for the whole batch].  shape describes
+ * the suffix caches (Nmax = suffix capacity, seq_lens = suffix lengths).
+ * The context of sequence b is the Np prefix keys followed by its own
+ * N_b suffix keys; key j < Np is prefix key j, key Np + j is suffix key j.
+ *   Kp, Vp  [Hkv][Np][d], ids_p [Hkv][Np][L], vnorm_p [Hkv][Np] (the
+ *           prefix cache and its metadata, as hst_hash_keys_softlsh writes
+ *           them for a batch of one)
+ *   Ks, Vs, ids_s, vnorm_s: the suffix caches, [B][Hkv][Nmax]...
+ * The result is hst_decode_step_softlsh's over the concatenated context:
+ * idx [B][Hkv][k] holds context indices, ascending, then -1.  The prefix
+ * metadata is scanned once per kv head for the whole batch.  L in {16, 32,
+ * 64, 128}; Np >= 0; Np + Nmax <= 2^30.  Workspace from
+ * hst_workspace_size_shared.
+ */
+hst_status hst_decode_step_softlsh_shared(const hst_shape* shape, int Np,
+                                          const void* q, const void* Kp,
+                                          const void* Vp, const uint8_t* ids_p,
+                                          const void* vnorm_p, const void* Ks,
+                                          const void* Vs, const uint8_t* ids_s,
+                                          const void* vnorm_s, const void* W,
+                                          int L, int P, double tau,
+                                          int norm_dtype, int k,
+                                          const int32_t* k_per_seq, float scale,
+                                          int32_t* idx, float* out, float* lse,
+                                          void* ws, size_t ws_bytes,
+                                          void* stream);
+
+/* Workspace bytes of hst_decode_step_softlsh_shared. */
+hst_status hst_workspace_size_shared(const hst_shape* shape, int Np, int L,
+                                     int P, int k, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif
