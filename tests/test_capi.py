@@ -186,3 +186,23 @@ def test_routing_entry_points_validate_before_launch():
     assert C.hst_build_cards_softlsh(by, FAKE, FAKE, L.HST_F16, FAKE, 64, 9, FAKE, FAKE, FAKE,
                                      FAKE, None) == -2
     assert C.hst_last_hip_error() == 0
+
+
+def test_shared_prefix_entry_points_validate_before_launch():
+    L = _lib()
+    C = L._C
+    sh = _shape(L)
+    by = ctypes.byref(sh)
+    out = ctypes.c_size_t(0)
+    assert C.hst_workspace_size_shared(by, 4096, 64, 8, 100, ctypes.byref(out)) == 0
+    assert out.value > 2 * 2 * (4096 + 1024) * 4          # the context scores alone
+    assert C.hst_workspace_size_shared(by, -1, 64, 8, 100, ctypes.byref(out)) == -1
+    assert C.hst_workspace_size_shared(by, 4096, 48, 8, 100, ctypes.byref(out)) == -2
+    assert C.hst_workspace_size_shared(by, 4096, 64, 8, 0, ctypes.byref(out)) == -1
+    assert C.hst_workspace_size_shared(by, 4096, 64, 8, 100, None) == -1
+    call = lambda Np, ws: C.hst_decode_step_softlsh_shared(
+        by, Np, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, 8, 0.3,
+        L.HST_F16, 100, None, 0.1, FAKE, FAKE, None, FAKE, ws, None)
+    assert call(4096, 100) == -3                           # workspace too small
+    assert call(1 << 30, 1 << 40) == -2                    # context too long
+    assert C.hst_last_hip_error() == 0
