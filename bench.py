@@ -517,6 +517,23 @@ def main():
         log(f"routed step (C={C}) {routed_us:.2f} us, {rbytes / 1e6:.1f} MB")
         del rstep, cards
 
+    # code-length sweep (binary codes): the same step with 64- and 256-bit
+    # codes from seeded projections of the same keys (128 bits: the step)
+    codes_sweep = None
+    if w.scheme == "hamming":
+        codes_sweep = {"128": {"us": ms_per_step * 1e3, "meta_bytes_per_key": 16}}
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(20260202)
+        for bits in (64, 256):
+            Rb = torch.randn((w.Hkv, bits, w.d), generator=gen, device=dev).to(K.dtype)
+            cb = [hst.hst_hash_keys_binary(st_[0], Rb, code_bits=bits, seq_lens=sl) for st_ in sets]
+            bstep = hst.DecodeHamming(K, w.Hq, kmax, code_bits=bits, seq_lens=sl, k_per_seq=kp)
+            brun = lambda i, bstep=bstep, Rb=Rb, cb=cb: bstep(q, sets[i % R][0], sets[i % R][1], Rb,
+                                                              cb[i % R])
+            codes_sweep[str(bits)] = {"us": time_graph(brun), "meta_bytes_per_key": bits // 8}
+            del cb, bstep
+        log("code lengths: " + ", ".join(f"{b} bits {v['us']:.1f} us" for b, v in codes_sweep.items()))
+
     # shared-prefix variant (soft-LSH): a batch of SHARED_B sequences with a
     # common SHARED_NP-key prefix and ragged own suffixes, against the plain
     # step on the materialised concatenation of the same data
@@ -582,6 +599,7 @@ def main():
         "mass": mass,
         "routed": routed,
         "shared": shared,
+        "codes_sweep": codes_sweep,
         "dense": dense,
     }
     if not args.no_cpu_baseline:

@@ -274,7 +274,7 @@ def hst_score_keys_hamming(q, R, codes, Nmax_like, code_bits: int = 128,
     B, Hq, d = q.shape
     shape = make_shape(Nmax_like, Hq, seq_lens)
     scores = torch.zeros((shape.B, shape.Hkv, shape.Nmax), dtype=torch.int32, device=q.device)
-    ws = _workspace(workspace_size(HST_OP_SCORE_HAMMING, shape), q.device)
+    ws = _workspace(workspace_size(HST_OP_SCORE_HAMMING, shape, code_bits=code_bits), q.device)
     _check(_C.hst_score_keys_hamming(ctypes.byref(shape), _ptr(q), _ptr(R), code_bits,
                                      _ptr(codes), _ptr(scores), _ptr(ws), ws.numel(),
                                      _stream(q.device)), "hst_score_keys_hamming")
@@ -377,7 +377,8 @@ class DecodeHamming:
         self.idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-        self.ws = _workspace(workspace_size(HST_OP_DECODE_HAMMING, self.shape, k=k), dev)
+        self.ws = _workspace(workspace_size(HST_OP_DECODE_HAMMING, self.shape, code_bits=code_bits,
+                                            k=k), dev)
         self.k_per_seq = k_per_seq
 
     def __call__(self, q, K, V, R, codes, stream: Optional[int] = None):

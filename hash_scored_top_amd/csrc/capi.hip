@@ -105,7 +105,7 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
   const bool bin = op == HST_OP_SCORE_HAMMING || op == HST_OP_DECODE_HAMMING ||
                    op == HST_OP_HASH_BINARY;
   if (soft) HST_TRY(check_lp(L, P));
-  if (bin && code_bits != 128) return HST_ERR_UNSUPPORTED;
+  if (bin && code_bits != 64 && code_bits != 128 && code_bits != 256) return HST_ERR_UNSUPPORTED;
   const bool mass = op == HST_OP_SELECT_MASS || op == HST_OP_DECODE_SOFTLSH_MASS;
   const bool needk = op == HST_OP_SELECT_TOPK || op == HST_OP_SPARSE_ATTENTION ||
                      op == HST_OP_DECODE_SOFTLSH || op == HST_OP_DECODE_HAMMING || mass;
@@ -126,12 +126,21 @@ hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int 
   switch (op) {
     case HST_OP_HASH_SOFTLSH:
     case HST_OP_HASH_BINARY: b = 0; break;
-    case HST_OP_SCORE_SOFTLSH:
     case HST_OP_SCORE_HAMMING:
+    case HST_OP_DECODE_HAMMING:
+      if (code_bits != 128) {  // 64 / 256 bits: query codes, scan, selection, attention
+        if (op == HST_OP_DECODE_HAMMING &&
+            hst::fused_layout(*shape, HST_OP_SELECT_TOPK, 0, 0, k).nchunks > hst::kMaxChunks)
+          return HST_ERR_UNSUPPORTED;
+        b = align_up(hst::codes_ws_bytes(*shape, code_bits, needk ? k : 1,
+                                         op == HST_OP_DECODE_HAMMING));
+        break;
+      }
+      [[fallthrough]];
+    case HST_OP_SCORE_SOFTLSH:
     case HST_OP_SELECT_TOPK:
     case HST_OP_SPARSE_ATTENTION:
-    case HST_OP_DECODE_SOFTLSH:
-    case HST_OP_DECODE_HAMMING: {
+    case HST_OP_DECODE_SOFTLSH: {
       const hst::FusedLayout f = hst::fused_layout(*shape, op, L, P, needk ? k : 1);
       if (f.nchunks > hst::kMaxChunks) return HST_ERR_UNSUPPORTED;
       b = align_up(f.bytes);
@@ -168,10 +177,10 @@ hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K, const vo
 hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K, const void* R,
                                 int code_bits, uint32_t* codes, void* stream) {
   HST_TRY(check_shape(shape));
-  if (code_bits != 128) return HST_ERR_UNSUPPORTED;
+  if (code_bits != 64 && code_bits != 128 && code_bits != 256) return HST_ERR_UNSUPPORTED;
   if (!ptr_ok(K) || !ptr_ok(R) || !ptr_ok(codes)) return HST_ERR_INVALID_ARG;
   return hip_status(
-      hst::launch_hash_binary(*shape, K, R, codes, static_cast<hipStream_t>(stream)));
+      hst::launch_hash_binary(*shape, K, R, code_bits, codes, static_cast<hipStream_t>(stream)));
 }
 
 hst_status hst_append_kv_softlsh(const hst_shape* shape, const void* k_new, const void* v_new,
@@ -216,8 +225,8 @@ static hst_status score_softlsh_checks(const hst_shape* shape, const void* q, co
 static hst_status score_hamming_checks(const hst_shape* shape, const void* q, const void* R,
                                        int code_bits, const uint32_t* codes) {
   HST_TRY(check_shape(shape));
-  if (code_bits != 128) return HST_ERR_UNSUPPORTED;
-  if (group(shape) > 64) return HST_ERR_UNSUPPORTED;
+  if (code_bits != 64 && code_bits != 128 && code_bits != 256) return HST_ERR_UNSUPPORTED;
+  if (group(shape) > (code_bits == 128 ? 64 : 8)) return HST_ERR_UNSUPPORTED;
   if (!ptr_ok(q) || !ptr_ok(R) || !ptr_ok(codes)) return HST_ERR_INVALID_ARG;
   return HST_OK;
 }
@@ -233,9 +242,9 @@ static hst_status attention_checks(const hst_shape* shape, const void* q, const 
 }
 
 static hst_status workspace_check(int op, const hst_shape* shape, int L, int P, int k, void* ws,
-                                  size_t ws_bytes) {
+                                  size_t ws_bytes, int code_bits = 128) {
   size_t need = 0;
-  HST_TRY(hst_workspace_size(op, shape, L, P, 128, k, &need));
+  HST_TRY(hst_workspace_size(op, shape, L, P, code_bits, k, &need));
   if (ws_bytes < need) return HST_ERR_WORKSPACE;
   if (need > 0 && (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0))
     return HST_ERR_INVALID_ARG;
@@ -281,7 +290,10 @@ hst_status hst_score_keys_hamming(const hst_shape* shape, const void* q, const v
                                   size_t ws_bytes, void* stream) {
   HST_TRY(score_hamming_checks(shape, q, R, code_bits, codes));
   if (!ptr_ok(scores)) return HST_ERR_INVALID_ARG;
-  HST_TRY(workspace_check(HST_OP_SCORE_HAMMING, shape, 0, 0, 1, ws, ws_bytes));
+  HST_TRY(workspace_check(HST_OP_SCORE_HAMMING, shape, 0, 0, 1, ws, ws_bytes, code_bits));
+  if (code_bits != 128)
+    return hip_status(hst::codes_score(*shape, q, R, code_bits, codes, scores, ws,
+                                       static_cast<hipStream_t>(stream)));
   return hip_status(hst::fused_score_hamming(*shape, q, R, codes, scores, ws,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -463,7 +475,10 @@ hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const 
   HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
   if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
   if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
-  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
+  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes, code_bits));
+  if (code_bits != 128)
+    return hip_status(hst::codes_decode(*shape, q, K, V, R, code_bits, codes, k, k_per_seq, scale,
+                                        idx, out, lse, ws, static_cast<hipStream_t>(stream)));
   return hip_status(hst::fused_decode_hamming(*shape, q, K, V, R, codes, k, k_per_seq, scale, idx,
                                               out, lse, ws, static_cast<hipStream_t>(stream)));
 }

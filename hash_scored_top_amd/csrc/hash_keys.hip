@@ -75,15 +75,16 @@ hash_softlsh_generic_kernel(const T* __restrict__ K, const T* __restrict__ W,
 // Binary codes: a block of 2*64 threads handles keys one at a time; thread i
 // decides bit i, a wave ballot packs 64 bits into two words.
 template <typename T>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 binary_codes_generic_kernel(const T* __restrict__ X, const T* __restrict__ R,
                             const int32_t* __restrict__ seq_lens, int Hkv, int Nmax,
                             int d, int keys_per_block, uint32_t* __restrict__ codes) {
   const int bh = blockIdx.y;
   const int b = bh / Hkv, h = bh % Hkv;
   const int n = seq_len(seq_lens, b, Nmax);
-  const int i = threadIdx.x;  // bit index 0..127
-  const T* rrow = R + (static_cast<long long>(h) * 128 + i) * d;
+  const int nbits = blockDim.x;  // 64, 128 or 256: one thread per bit
+  const int i = threadIdx.x;
+  const T* rrow = R + (static_cast<long long>(h) * nbits + i) * d;
   const long long j0 = static_cast<long long>(blockIdx.x) * keys_per_block;
   for (int u = 0; u < keys_per_block; ++u) {
     const long long j = j0 + u;
@@ -92,7 +93,7 @@ binary_codes_generic_kernel(const T* __restrict__ X, const T* __restrict__ R,
     bool bit = dot_nonneg_exact(rrow, x, d);
     unsigned long long m = __ballot(bit);
     if ((i & 63) == 0) {
-      uint32_t* dst = codes + (static_cast<long long>(bh) * Nmax + j) * 4 + (i >> 6) * 2;
+      uint32_t* dst = codes + (static_cast<long long>(bh) * Nmax + j) * (nbits / 32) + (i >> 6) * 2;
       dst[0] = static_cast<uint32_t>(m);
       dst[1] = static_cast<uint32_t>(m >> 32);
     }
@@ -644,17 +645,17 @@ hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V,
   return launch_value_norms(s, V, norm_dtype, vnorm, st);
 }
 
-hipError_t launch_hash_binary(const hst_shape& s, const void* K, const void* R,
+hipError_t launch_hash_binary(const hst_shape& s, const void* K, const void* R, int code_bits,
                               uint32_t* codes, hipStream_t st) {
-  if (signs_mfma_ok(s, 128, K, R, codes)) return launch_signs(s, K, R, 128, codes, st);
+  if (signs_mfma_ok(s, code_bits, K, R, codes)) return launch_signs(s, K, R, code_bits, codes, st);
   const int kpb = 16;
   dim3 grid(static_cast<unsigned>((s.Nmax + kpb - 1) / kpb), s.B * s.Hkv);
   if (s.kv_dtype == HST_F32)
-    hipLaunchKernelGGL(binary_codes_generic_kernel<float>, grid, dim3(128), 0, st,
+    hipLaunchKernelGGL(binary_codes_generic_kernel<float>, grid, dim3(code_bits), 0, st,
                        static_cast<const float*>(K), static_cast<const float*>(R),
                        s.seq_lens, s.Hkv, s.Nmax, s.d, kpb, codes);
   else
-    hipLaunchKernelGGL(binary_codes_generic_kernel<bf16>, grid, dim3(128), 0, st,
+    hipLaunchKernelGGL(binary_codes_generic_kernel<bf16>, grid, dim3(code_bits), 0, st,
                        static_cast<const bf16*>(K), static_cast<const bf16*>(R),
                        s.seq_lens, s.Hkv, s.Nmax, s.d, kpb, codes);
   return hipGetLastError();

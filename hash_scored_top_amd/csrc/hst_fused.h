@@ -140,6 +140,19 @@ hipError_t fused_decode_softlsh_shared(const hst_shape& s, int Np, const void* q
                                        int32_t* idx, float* out, float* lse, void* ws,
                                        hipStream_t st);
 
+// binary codes of 64 or 256 bits (codes.hip, pipeline.hip)
+hipError_t launch_hamming_scan(const hst_shape& s, int code_bits, const uint32_t* qcodes,
+                               const uint32_t* kcodes, int32_t* scores, hipStream_t st);
+hipError_t launch_query_codes(const hst_shape& s, const void* q, const void* R, int code_bits,
+                              uint32_t* qcodes, hipStream_t st);
+size_t codes_ws_bytes(const hst_shape& s, int code_bits, int kcap, bool decode);
+hipError_t codes_score(const hst_shape& s, const void* q, const void* R, int code_bits,
+                       const uint32_t* codes, int32_t* scores, void* ws, hipStream_t st);
+hipError_t codes_decode(const hst_shape& s, const void* q, const void* K, const void* V,
+                        const void* R, int code_bits, const uint32_t* codes, int kcap,
+                        const int32_t* kps, float scale, int32_t* idx, float* out, float* lse,
+                        void* ws, hipStream_t st);
+
 hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* W, int L, int P, double tau, const uint8_t* ids,
                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,

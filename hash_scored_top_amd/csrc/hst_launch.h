@@ -14,8 +14,8 @@ namespace hst {
 hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V, const void* W,
                                int L, int P, int norm_dtype, uint8_t* ids, void* vnorm,
                                hipStream_t st);
-hipError_t launch_hash_binary(const hst_shape& s, const void* K, const void* R, uint32_t* codes,
-                              hipStream_t st);
+hipError_t launch_hash_binary(const hst_shape& s, const void* K, const void* R, int code_bits,
+                              uint32_t* codes, hipStream_t st);
 // bucket ids only (no value norms)
 hipError_t launch_hash_ids_softlsh(const hst_shape& s, const void* K, const void* W, int L, int P,
                                    uint8_t* ids, hipStream_t st);

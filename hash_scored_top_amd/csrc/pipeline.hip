@@ -280,6 +280,59 @@ hipError_t fused_decode_softlsh_shared(const hst_shape& s, int Np, const void* q
   return launch_attend(s, aa, q, Ks, Vs, idx, false, nullptr, 0, fa.chunk, scale, out, lse, st);
 }
 
+// Workspace of the binary-code path for 64 / 256-bit codes: query codes,
+// then (decode) the scores, the selection's workspace and the attention
+// partials.
+struct CodesLayout {
+  size_t qcodes, scores, select, attn, bytes;
+};
+
+static CodesLayout codes_layout(const hst_shape& s, int code_bits, int kcap, bool decode) {
+  CodesLayout r{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  r.qcodes = take(static_cast<size_t>(s.B) * s.Hq * (code_bits / 32) * 4);
+  if (decode) {
+    r.scores = take(static_cast<size_t>(s.B) * s.Hkv * s.Nmax * 4);
+    r.select = take(fused_layout(s, HST_OP_SELECT_TOPK, 0, 0, kcap).bytes);
+    r.attn = take(fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap).bytes);
+  }
+  r.bytes = o;
+  return r;
+}
+
+size_t codes_ws_bytes(const hst_shape& s, int code_bits, int kcap, bool decode) {
+  return codes_layout(s, code_bits, kcap, decode).bytes;
+}
+
+hipError_t codes_score(const hst_shape& s, const void* q, const void* R, int code_bits,
+                       const uint32_t* codes, int32_t* scores, void* ws, hipStream_t st) {
+  const CodesLayout r = codes_layout(s, code_bits, 1, false);
+  uint32_t* qc = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + r.qcodes);
+  HST_CHECK(launch_query_codes(s, q, R, code_bits, qc, st));
+  return launch_hamming_scan(s, code_bits, qc, codes, scores, st);
+}
+
+hipError_t codes_decode(const hst_shape& s, const void* q, const void* K, const void* V,
+                        const void* R, int code_bits, const uint32_t* codes, int kcap,
+                        const int32_t* kps, float scale, int32_t* idx, float* out, float* lse,
+                        void* ws, hipStream_t st) {
+  const CodesLayout r = codes_layout(s, code_bits, kcap, true);
+  char* base = static_cast<char*>(ws);
+  uint32_t* qc = reinterpret_cast<uint32_t*>(base + r.qcodes);
+  int32_t* scores = reinterpret_cast<int32_t*>(base + r.scores);
+  HST_CHECK(launch_query_codes(s, q, R, code_bits, qc, st));
+  HST_CHECK(launch_hamming_scan(s, code_bits, qc, codes, scores, st));
+  HST_CHECK(fused_select(s, HST_I32, scores, kcap, kps, idx, base + r.select, st));
+  const FusedLayout fa = fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap);
+  const FusedArgs aa = make_args(s, fa, base + r.attn, 0, 0, 0.0, kcap);
+  return launch_attend(s, aa, q, K, V, idx, false, nullptr, 0, fa.chunk, scale, out, lse, st);
+}
+
 hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,

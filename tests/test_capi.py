@@ -83,7 +83,7 @@ def test_entry_points_validate_before_launch():
     # unsupported P / norm dtype / code bits
     assert C.hst_hash_keys_softlsh(by, FAKE, FAKE, FAKE, 64, 9, L.HST_F16, FAKE, FAKE, None) == -2
     assert C.hst_hash_keys_softlsh(by, FAKE, FAKE, FAKE, 64, 8, L.HST_BF16, FAKE, FAKE, None) == -2
-    assert C.hst_hash_keys_binary(by, FAKE, FAKE, 64, FAKE, None) == -2
+    assert C.hst_hash_keys_binary(by, FAKE, FAKE, 96, FAKE, None) == -2
     # tau must be positive and finite
     for tau in (0.0, -1.0, float("inf"), float("nan")):
         assert C.hst_score_keys_softlsh(by, FAKE, FAKE, 64, 8, tau, FAKE, FAKE, L.HST_F16, FAKE,
