@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix leg")
+    ap.add_argument("--core-only", action="store_true",
+                    help="time the step and the roofline kernel only (no variant legs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of a captured graph")
@@ -475,7 +477,7 @@ def main():
     # highest hash score, then the smallest set holding MASS_P of their
     # softmax mass
     mass = None
-    if w.scheme == "softlsh":
+    if w.scheme == "softlsh" and not args.core_only:
         mstep = hst.DecodeSoftLSHMass(K, w.Hq, w.L, w.P, w.tau, kmax, MASS_P, vn.dtype,
                                       seq_lens=sl, k_per_seq=kp)
         mrun = lambda i: mstep(q, sets[i % R][0], sets[i % R][1], Wp, sets[i % R][2],
@@ -497,7 +499,7 @@ def main():
     # chunks first, ROUTE_OVERSAMPLE * ceil(k / 64) chunks kept, then the k
     # best keys inside them
     routed = None
-    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128):
+    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128) and not args.core_only:
         C = min(256, ROUTE_OVERSAMPLE * math.ceil(kmax / 64))
         cards = [hst.hst_build_cards_softlsh(st_[0], st_[3], Wp, w.L, w.P, seq_lens=sl)
                  for st_ in sets]
@@ -520,7 +522,7 @@ def main():
     # code-length sweep (binary codes): the same step with 64- and 256-bit
     # codes from seeded projections of the same keys (128 bits: the step)
     codes_sweep = None
-    if w.scheme == "hamming":
+    if w.scheme == "hamming" and not args.core_only:
         codes_sweep = {"128": {"us": ms_per_step * 1e3, "meta_bytes_per_key": 16}}
         gen = torch.Generator(device=dev)
         gen.manual_seed(20260202)
@@ -538,14 +540,14 @@ def main():
     # common SHARED_NP-key prefix and ragged own suffixes, against the plain
     # step on the materialised concatenation of the same data
     shared = None
-    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128) and not args.no_shared:
+    if w.scheme == "softlsh" and w.L in (16, 32, 64, 128) and not (args.no_shared or args.core_only):
         shared = shared_leg(hst, w, Wp, dev, stream, capture)
         log(f"shared-prefix step {shared['us']:.2f} us vs {shared['plain_us']:.2f} us "
             f"materialised ({shared['speedup']:.2f}x)")
 
     # dense attention over every cached key, for the sparse/dense ratio
     dense = None
-    if w.B * w.Hkv * w.N <= (1 << 24):
+    if w.B * w.Hkv * w.N <= (1 << 24) and not args.core_only:
         didx = torch.arange(w.N, dtype=torch.int32, device=dev).repeat(w.B, w.Hkv, 1)
         dshape = hst.make_shape(K, w.Hq, sl)
         dout = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
