@@ -315,6 +315,197 @@ __device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, i
   }
 }
 
+// Exact selection over M <= NT * PERW candidates held in LDS in index order,
+// on keys held in registers: wave w holds the entries at positions
+// [lo_w, hi_w) (lane l's entry u at lo_w + 64u + l), the order in which the
+// compaction walks them, so the counts and the compaction come from ballots
+// over registers instead of a second pass over LDS.  Radix passes of up to
+// 11 bits below the keys' common prefix narrow the bin of the k-th largest
+// key; once that bin holds at most kRankBin entries they are ranked directly
+// by (key descending, position ascending), which resolves the k-th key and
+// how many keys equal to it are taken, without further passes.  The result
+// is the masked-prefix rule of radix_select_regs.  Writes the selected
+// indices at output positions [r0, r1).  hist: 2048 words of LDS.
+constexpr int kRankBin = 64;
+template <int NT, int PERW>
+__device__ void select_lds_regs(const uint32_t* candk, const int32_t* candi, int M, int k, int r0, int r1,
+                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+  constexpr int NW = NT / 64;
+  constexpr int MAXPER = (2048 + NT - 1) / NT;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int span = ((M + NW - 1) / NW + 63) & ~63;
+  const int lo = min(M, wave * span), hi = min(M, lo + span);
+  uint32_t key[PERW];
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const int p = lo + 64 * u + lane;
+    key[u] = p < hi ? candk[p] : 0u;
+  }
+  // rule: selected iff (key & mask) > prefix, or (key & mask) == prefix among
+  // the first krem such entries in index order
+  uint32_t mask = 0u, prefix = 0u;
+  int krem = k < M ? k : M;
+  if (k < M) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int u = 0; u < PERW; ++u)
+      if (lo + 64 * u + lane < hi) {
+        mn = min(mn, key[u]);
+        mx = max(mx, key[u]);
+      }
+    block_minmax<NT>(mn, mx, sc);
+    if (mn != mx) {
+      const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
+      mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
+      prefix = mn & mask;
+      int lob = hb + 1;
+      while (lob > 0) {
+        const int width = lob < 11 ? lob : 11;
+        const int sh = lob - width;
+        const int nb = 1 << width;
+        const uint32_t dm = static_cast<uint32_t>(nb - 1);
+        for (int i = t; i < nb; i += NT) hist[i] = 0u;
+        if (t == 0) sc.found[3] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < PERW; ++u)
+          if (lo + 64 * u + lane < hi && (key[u] & mask) == prefix) atomicAdd(&hist[(key[u] >> sh) & dm], 1u);
+        __syncthreads();
+        // the bin holding rank krem, counted from the top digit down: thread t
+        // owns bins [t*per, t*per + per) of that order
+        const int per = (nb + NT - 1) / NT;
+        int c[MAXPER];
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+          const int r = t * per + i;
+          c[i] = (i < per && r < nb) ? static_cast<int>(hist[nb - 1 - r]) : 0;
+          mine += c[i];
+        }
+        int incl = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        if (lane == 63) sc.wsum[wave] = incl;
+        __syncthreads();
+        int above = incl - mine;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+          if (i < wave) above += sc.wsum[i];
+        if (above < krem && krem <= above + mine) {
+          int cum = above;
+          bool hit = false;
+#pragma unroll
+          for (int i = 0; i < MAXPER; ++i) {
+            if (!hit && i < per && cum + c[i] >= krem) {
+              sc.found[0] = nb - 1 - (t * per + i);
+              sc.found[1] = krem - cum;
+              sc.found[2] = c[i];
+              hit = true;
+            }
+            if (!hit) cum += c[i];
+          }
+        }
+        __syncthreads();
+        const int digit = sc.found[0], cnt = sc.found[2];
+        krem = sc.found[1];
+        prefix |= static_cast<uint32_t>(digit) << sh;
+        mask |= dm << sh;
+        lob = sh;
+        if (cnt == krem || lob == 0) break;  // the whole bin is taken, or every bit is resolved
+        if (cnt <= kRankBin) {
+          // the bin's entries (key, position), in any order, over the histogram
+          uint2* bl = reinterpret_cast<uint2*>(hist);
+          __syncthreads();  // every thread has read its bins
+          {
+            // this wave's entries of the bin, then one slot reservation per wave
+            int nw = 0;
+#pragma unroll
+            for (int u = 0; u < PERW; ++u) nw += __popcll(__ballot(lo + 64 * u + lane < hi && (key[u] & mask) == prefix));
+            int base = 0;
+            if (lane == 0 && nw > 0) base = atomicAdd(&sc.found[3], nw);
+            base = __shfl(base, 0, 64);
+#pragma unroll
+            for (int u = 0; u < PERW; ++u) {
+              const int p = lo + 64 * u + lane;
+              const bool in = p < hi && (key[u] & mask) == prefix;
+              const unsigned long long b = __ballot(in);
+              if (in) bl[base + lanes_below(b)] = make_uint2(key[u], static_cast<uint32_t>(p));
+              base += __popcll(b);
+            }
+          }
+          __syncthreads();
+          if (t < cnt) {
+            // rank of this entry by (key descending, position ascending): the
+            // bin's entries with a larger key, then its equal keys earlier
+            const uint2 me = bl[t];
+            int gt = 0, eq = 0;
+            for (int j = 0; j < cnt; ++j) {
+              const uint2 o = bl[j];
+              gt += o.x > me.x ? 1 : 0;
+              eq += (o.x == me.x && o.y < me.y) ? 1 : 0;
+            }
+            if (gt + eq == krem - 1) {  // the k-th entry: its key, and how many
+              sc.found[0] = static_cast<int>(me.x);  // entries equal to it are taken
+              sc.found[1] = eq + 1;
+            }
+          }
+          __syncthreads();
+          // the k-th key is now fully resolved: take the keys above it and the
+          // first krem keys equal to it (index order)
+          prefix = static_cast<uint32_t>(sc.found[0]);
+          mask = 0xffffffffu;
+          krem = sc.found[1];
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();  // sc.found is read above; sc.red is written below
+  // counts per wave (strictly above, tied at the prefix), then the waves before
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const bool ok = lo + 64 * u + lane < hi;
+    const uint32_t m = key[u] & mask;
+    gtc += __popcll(__ballot(ok && m > prefix));
+    eqc += __popcll(__ballot(ok && m == prefix));
+  }
+  if (lane == 0) {
+    sc.red[0][wave] = static_cast<uint32_t>(gtc);
+    sc.red[1][wave] = static_cast<uint32_t>(eqc);
+  }
+  __syncthreads();
+  int gt_before = 0, eq_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += static_cast<int>(sc.red[0][w]);
+    eq_run += static_cast<int>(sc.red[1][w]);
+  }
+  __syncthreads();  // sc is reused by the caller
+  int run = gt_before + min(eq_run, krem);
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const int p = lo + 64 * u + lane;
+    const bool ok = p < hi;
+    const uint32_t m = key[u] & mask;
+    const bool top = ok && m > prefix;
+    const bool eq = ok && m == prefix;
+    const unsigned long long eqb = __ballot(eq);
+    const bool sel = top || (eq && eq_run + lanes_below(eqb) < krem);
+    const unsigned long long selb = __ballot(sel);
+    const int pos = run + lanes_below(selb);
+    if (sel && pos >= r0 && pos < r1) {
+      const int32_t v = candi[p];
+      if (out_g != nullptr) out_g[pos] = v;
+      if (out_l != nullptr) out_l[pos - r0] = v;
+    }
+    run += __popcll(selb);
+    eq_run += __popcll(eqb);
+  }
+}
+
 // Lower bound of the r-th largest (1 <= r <= count) of the keys held PER per
 // thread: two 11-bit radix passes below the common prefix of the keys, then
 // the low edge of the bin holding rank r (the common key if all are equal).
@@ -397,7 +588,7 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
         }
       }
       __syncthreads();
-      select_lds<NT, kSelCap / NT>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
+      select_lds_regs<NT, kSelCap / NT>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
     } else if (M >= k_eff) {
       path = 1;
       const SlotSrc src{slots, ws.offs, nch, chunk};
