@@ -4,8 +4,9 @@
 //  * Soft-collision score (SOCKET overview page, "Core mechanism: soft LSH",
 //    item 3): score_j = ||v_j|| * sum_l T[id_{j,l}][l], the kv head's
 //    bucket-major table T resident in LDS.  Each key's L ids are split over
-//    L/16 lanes; lane groups visit their 16 tables in an order rotated by the
-//    key's slot in the wave so the 64 lanes of a wave hit distinct LDS banks.
+//    L/16 lanes; lane groups visit their 16 tables in an order rotated (L = 64:
+//    XOR-skewed) by the key's slot in the wave so the 64 lanes of a wave hit
+//    distinct LDS banks.
 //  * Code similarity (HATA explainer page, section 3): XOR + popcount of
 //    128-bit codes against the G query codes.
 //  * Given scores (the stand-alone top-k): the scores are only filtered.
@@ -28,9 +29,24 @@ constexpr int kSoftChunk = 2048;
 constexpr int kLaneChunk = 4096;
 static_assert(kSoftChunk >= kSample && kLaneChunk >= kSample && kSample >= 2048,
               "chunk tile holds the sample scores and doubles as the select histogram");
+// block scratch of a scan workgroup, after its table and score tile in LDS
+template <int NT>
+struct ScanTail {
+  BlockScratch<NT> sc;
+  uint32_t theta;
+};
 constexpr int kScanSoftU = 2;        // key batches per lane group in flight (two workgroups fit a CU)
 constexpr int kThetaSpin = 1 << 16;  // polls of the threshold word before falling back
 constexpr int kMaxParts = 16;        // partial sample scores per head (prep workgroups)
+
+// LDS offset of an LDS-resident object, and a float read at an LDS byte
+// address (no base to add).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((const __attribute__((address_space(3))) char*)p));
+}
+__device__ __forceinline__ float lds_f32_at(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) float*)static_cast<size_t>(addr);
+}
 
 // F16: value norms stored as binary16 (else float32); the raw bits are loaded
 // and converted only when used, so a load never waits for its own result.
@@ -44,10 +60,37 @@ struct SoftScorer {
   const float* tbl;  // LDS
   uint32_t idmask;   // 2^P - 1: ids outside the table cannot leave it
   int sub, grp;
+  // L = 64 (LANES == 4): lookup i of a lane reads table 16*sub + (i ^ k), k
+  // the key's slot among the 16 keys of its wave, so the 64 lanes of a wave
+  // hit 64 distinct banks.  Entry (id, l) of the bucket-major table sits at
+  // byte id*256 + 4l: the address is the id byte over the byte 4l, one byte
+  // permutation (v_perm) of the lane's id word and a word of four 4l bytes.
+  uint32_t lc[4];   // byte b of lc[m]: 4 * (16*sub + ((4m + b) ^ k))
+  uint32_t sel[4];  // permutation of lookup i (by i & 3): byte 0 <- lc byte, byte 1 <- id byte, 0, 0
+  uint32_t idm4;    // idmask in every byte
+  bool x1, x2;      // the lane's id words are taken XOR-permuted by (k >> 2)
+  bool at0;         // the table starts at LDS address 0: a permuted address is the LDS address
 
   __device__ __forceinline__ void setup() {
     sub = threadIdx.x % LANES;
     grp = threadIdx.x / LANES;
+    if constexpr (LANES == 4) {
+      const int k = grp & 15;
+      x1 = ((k >> 2) & 1) != 0;
+      x2 = ((k >> 3) & 1) != 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) v |= static_cast<uint32_t>((sub * 16 + ((4 * m + b) ^ k)) * 4) << (8 * b);
+        lc[m] = v;
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        sel[b] = static_cast<uint32_t>(b) | (static_cast<uint32_t>(4 + (b ^ (k & 3))) << 8) | 0x0c0c0000u;
+      idm4 = idmask * 0x01010101u;
+      at0 = lds_offset(tbl) == 0u;
+    }
   }
   // Loads of a batch; keys past jend (>= 1) read key jend - 1 instead, so the
   // loads carry no branch and all are in flight together.
@@ -65,6 +108,11 @@ struct SoftScorer {
   // scores of the batch held in (w, nr) into out[j - j0]
   __device__ __forceinline__ void compute(const uint4 (&w)[U], const uint32_t (&nr)[U], int jb, int jend,
                                           int j0, float* out) const {
+    if constexpr (LANES == 4) {
+      if (at0) compute64<true>(w, nr, jb, jend, j0, out);
+      else compute64<false>(w, nr, jb, jend, j0, out);
+      return;
+    }
     const int k = grp & 15;
     const int qw = k >> 2, sh = k & 3;
     const char* tb = reinterpret_cast<const char*>(tbl);
@@ -90,6 +138,36 @@ struct SoftScorer {
           const int l0 = sub * 16 + ((i + k) & 15), l1 = sub * 16 + ((i + 1 + k) & 15);
           acc0 += *reinterpret_cast<const float*>(tb + (id0 * L + l0) * 4);
           acc1 += *reinterpret_cast<const float*>(tb + (id1 * L + l1) * 4);
+        }
+        const float vn = F16 ? f16_bits_to_f32(static_cast<uint16_t>(nr[u])) : __uint_as_float(nr[u]);
+        const float sv = group_sum<LANES>(acc0 + acc1) * vn;
+        if (sub == 0) out[j - j0] = sv;
+      }
+    }
+  }
+  template <bool AT0>
+  __device__ __forceinline__ void compute64(const uint4 (&w)[U], const uint32_t (&nr)[U], int jb, int jend,
+                                            int j0, float* out) const {
+    const char* tb = reinterpret_cast<const char*>(tbl);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * KPI;
+      if (j < jend) {  // uniform over the LANES lanes of a key
+        // id words in the order (m ^ (k >> 2)), ids clamped into the table
+        const uint32_t e0 = x1 ? w[u].y : w[u].x, e1 = x1 ? w[u].x : w[u].y;
+        const uint32_t e2 = x1 ? w[u].w : w[u].z, e3 = x1 ? w[u].z : w[u].w;
+        uint32_t d[4];
+        d[0] = (x2 ? e2 : e0) & idm4;
+        d[1] = (x2 ? e3 : e1) & idm4;
+        d[2] = (x2 ? e0 : e2) & idm4;
+        d[3] = (x2 ? e1 : e3) & idm4;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const uint32_t o0 = __builtin_amdgcn_perm(d[i >> 2], lc[i >> 2], sel[i & 3]);
+          const uint32_t o1 = __builtin_amdgcn_perm(d[(i + 1) >> 2], lc[(i + 1) >> 2], sel[(i + 1) & 3]);
+          acc0 += AT0 ? lds_f32_at(o0) : *reinterpret_cast<const float*>(tb + o0);
+          acc1 += AT0 ? lds_f32_at(o1) : *reinterpret_cast<const float*>(tb + o1);
         }
         const float vn = F16 ? f16_bits_to_f32(static_cast<uint16_t>(nr[u])) : __uint_as_float(nr[u]);
         const float sv = group_sum<LANES>(acc0 + acc1) * vn;
@@ -262,11 +340,14 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   using S = SoftScorer<LANES, NT, U, F16>;
   constexpr int CH = kSoftChunk;
   static_assert(CH % S::TILE == 0, "whole tiles per chunk");
+  // no static LDS: the table starts at LDS address 0, so a lookup's address
+  // is the byte permutation alone
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ BlockScratch<NT> sc;
-  __shared__ uint32_t s_theta;
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
+  ScanTail<NT>& tl = *reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftChunk * 4);
+  BlockScratch<NT>& sc = tl.sc;
+  uint32_t& s_theta = tl.theta;
   constexpr bool filt = FILTER;
   const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
   const ScanWork wk = scan_work(filt, BH, nch);
@@ -323,9 +404,9 @@ scan_shared_kernel(const uint8_t* __restrict__ ids_p, const void* __restrict__ v
   using S = SoftScorer<LANES, NT, U, F16>;
   constexpr int CH = kSoftChunk;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ BlockScratch<NT> sc;
   float* tbl = reinterpret_cast<float*>(smem_raw);
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);
+  BlockScratch<NT>& sc = reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftChunk * 4)->sc;
   const int w = blockIdx.x, Hkv = a.Hkv;
   const int npre = pitems_pad * B;
   int b, h, chunk;
@@ -461,7 +542,9 @@ int scan_chunk(int L) {
   return (L == 16 || L == 32 || L == 64 || L == 128) ? kSoftChunk : kLaneChunk;
 }
 
-size_t scan_smem(int region, int chunk) { return static_cast<size_t>(region) + static_cast<size_t>(chunk) * 4; }
+size_t scan_smem(int region, int chunk) {
+  return static_cast<size_t>(region) + static_cast<size_t>(chunk) * 4 + hst_align16(sizeof(ScanTail<kScanNT>));
+}
 
 // Raises a kernel's dynamic LDS limit once per device (the largest size
 // requested so far).
