@@ -536,7 +536,7 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
                             const void* scores_row, bool scores_int, const SelectScratch& ws,
                             int r0, int r1, int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc,
                             int* cand_total) {
-  const int nch = (n + chunk - 1) / chunk;
+  const int nch = (n + a.span - 1) / a.span;  // chunk c: keys [c*span, (c+1)*span), slots at c*chunk
   const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
   const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
   int run = 0;

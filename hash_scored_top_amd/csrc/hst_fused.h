@@ -33,13 +33,16 @@ static_assert(sizeof(HeadState) == 64, "head state stride");
 struct FusedLayout {
   size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_scores, off_counts,
       off_slots, off_part_o, off_part_ml, bytes;
-  int chunk, nchunks, sample, xparts, rps, nsplit, kind;
+  int chunk;    // candidate slots per scan chunk (the stride of the slot array)
+  int nchunks;  // scan chunks per head at the default chunk length (the most there can be)
+  int sample, xparts, rps, nsplit, kind;
 };
 
 struct FusedArgs {
   int Hq, Hkv, d, Nmax, L, P;
   double inv_tau;
   int kcap, sample, xparts, nchunks, rps, nsplit, region_bytes;
+  int span;  // keys per scan chunk (at most the slot stride; see scan_span)
   HeadState* heads;
   float* tables;     // [B*Hkv][2^P][L] bucket-major
   uint32_t* qcodes;  // [B*Hkv][G][4]
@@ -48,7 +51,7 @@ struct FusedArgs {
                      //   given scores: part 0 holds the order keys' bits)
   float* svn;        // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
   uint32_t* counts;  // [B*Hkv][nchunks]
-  uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index)
+  uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index), chunk c holding keys [c*span, (c+1)*span)
   float* part_o;     // [B*Hq][nsplit][d]
   float* part_ml;    // [B*Hq][nsplit][2]
   // shared prefix (attention over given rows only): rows j < np come from
@@ -71,7 +74,11 @@ hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const voi
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,
                              const void* scores, const int32_t* kps, hipStream_t st);
 int prep_parts(int kind, int L);  // partial sample scores per head (prep workgroups)
-int scan_chunk(int L);
+int scan_chunk(int L);  // default keys per scan chunk
+int scan_cap(int L);    // candidate slots per chunk: the longest chunk a scan workgroup takes
+// keys per chunk of a filtering scan over s (slot stride cap, default length
+// chunk): lengthened (up to cap) when that fits the grid in one resident round
+int scan_span(const hst_shape& s, int chunk, int cap, bool filter);
 // filter != 0: the scan also derives each head's candidate threshold from the
 // partial sample scores (prep with sampling must precede it) and fills the
 // candidate slots

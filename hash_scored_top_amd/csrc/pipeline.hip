@@ -25,8 +25,9 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
   const bool attn = op == HST_OP_SPARSE_ATTENTION || decode;
   f.kind = soft ? ((L == 16 || L == 32 || L == 64 || L == 128) ? kScanSoftFast : kScanSoftAny)
                : (ham ? kScanHamming : kScanGivenF32);
-  f.chunk = soft ? scan_chunk(L) : scan_chunk(0);
-  f.nchunks = select ? static_cast<int>((s.Nmax + f.chunk - 1) / f.chunk) : 0;
+  const int dchunk = soft ? scan_chunk(L) : scan_chunk(0);
+  f.chunk = soft ? scan_cap(L) : scan_cap(0);
+  f.nchunks = select ? static_cast<int>((s.Nmax + dchunk - 1) / dchunk) : 0;
   f.sample = select ? kSample : 0;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -81,6 +82,8 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   a.nsplit = f.nsplit;
   a.xparts = f.xparts;
   a.region_bytes = 65536;
+  const int dchunk = f.kind == kScanSoftFast ? scan_chunk(L) : scan_chunk(0);
+  a.span = f.nchunks > 0 ? scan_span(s, dchunk, f.chunk, true) : dchunk;
   char* p = static_cast<char*>(ws);
   if (p != nullptr) {
     a.heads = reinterpret_cast<HeadState*>(p + f.off_heads);

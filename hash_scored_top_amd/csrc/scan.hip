@@ -25,10 +25,13 @@
 namespace hst {
 
 constexpr int kScanNT = 1024;
-constexpr int kSoftChunk = 2048;
-constexpr int kLaneChunk = 4096;
+constexpr int kSoftChunk = 2048;  // default keys per chunk (table lookups)
+constexpr int kSoftCap = 2560;    // longest chunk: candidate slots per chunk, LDS score tile
+constexpr int kLaneChunk = 4096;  // the same for one-lane-per-key scans
+constexpr int kLaneCap = 5120;
 static_assert(kSoftChunk >= kSample && kLaneChunk >= kSample && kSample >= 2048,
               "chunk tile holds the sample scores and doubles as the select histogram");
+static_assert(kSoftCap >= kSoftChunk && kLaneCap >= kLaneChunk, "chunk caps");
 // block scratch of a scan workgroup, after its table and score tile in LDS
 template <int NT>
 struct ScanTail {
@@ -330,22 +333,24 @@ __device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, uint3
   return *s_theta;
 }
 
-// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]).
-template <int LANES, int U, bool FILTER, bool F16>
+// Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]);
+// chunk c of a head holds keys [c*span, (c+1)*span), span at most the default
+// chunk length (LONG false) or kSoftCap (LONG true).
+template <int LANES, int U, bool FILTER, bool F16, bool LONG>
 __global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
 scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm,
                     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
                     float* __restrict__ scores_out, int nch, FusedArgs a) {
   constexpr int NT = kScanNT;
   using S = SoftScorer<LANES, NT, U, F16>;
-  constexpr int CH = kSoftChunk;
-  static_assert(CH % S::TILE == 0, "whole tiles per chunk");
+  static_assert(kSoftChunk % S::TILE == 0, "whole tiles per default chunk");
+  constexpr int NTILES = LONG ? (kSoftCap + S::TILE - 1) / S::TILE : kSoftChunk / S::TILE;
   // no static LDS: the table starts at LDS address 0, so a lookup's address
   // is the byte permutation alone
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* tbl = reinterpret_cast<float*>(smem_raw);                      // table region
-  float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // CH scores
-  ScanTail<NT>& tl = *reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftChunk * 4);
+  float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);    // the chunk's scores
+  ScanTail<NT>& tl = *reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftCap * 4);
   BlockScratch<NT>& sc = tl.sc;
   uint32_t& s_theta = tl.theta;
   constexpr bool filt = FILTER;
@@ -357,9 +362,9 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   }
   const int bh = wk.bh, chunk = wk.chunk, b = bh / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = chunk * CH;
+  const int j0 = chunk * a.span;
   if (j0 >= n) return;
-  const int jend = min(j0 + CH, n);
+  const int jend = min(j0 + a.span, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   S sco;
   sco.idv = reinterpret_cast<const uint4*>(ids);
@@ -376,10 +381,10 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
                        reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt), nflt / 4);
   }
   __syncthreads();
-  soft_score_tiles<CH / S::TILE>(sco, base, j0, jend, w, nr, tile);
+  soft_score_tiles<NTILES>(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
   const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
+  uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kSoftCap;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
                                                    slot, sc);
@@ -406,7 +411,7 @@ scan_shared_kernel(const uint8_t* __restrict__ ids_p, const void* __restrict__ v
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* tbl = reinterpret_cast<float*>(smem_raw);
   float* tile = reinterpret_cast<float*>(smem_raw + a.region_bytes);
-  BlockScratch<NT>& sc = reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftChunk * 4)->sc;
+  BlockScratch<NT>& sc = reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftCap * 4)->sc;
   const int w = blockIdx.x, Hkv = a.Hkv;
   const int npre = pitems_pad * B;
   int b, h, chunk;
@@ -462,7 +467,6 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
                  uint32_t* __restrict__ scores_out, int filter, int nch, FusedArgs a) {
   constexpr int NT = kScanNT;
   constexpr bool KINT = KIND == kScanHamming || KIND == kScanGivenI32;
-  constexpr int CH = kLaneChunk;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ BlockScratch<NT> sc;
   __shared__ uint32_t qc[64 * 4];
@@ -479,9 +483,9 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   const int bh = wk.bh, chunk = wk.chunk, b = bh / a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax);
-  const int j0 = chunk * CH;
+  const int j0 = chunk * a.span;
   if (j0 >= n) return;
-  const int jend = min(j0 + CH, n);
+  const int jend = min(j0 + a.span, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
   if (KIND == kScanSoftAny) {
     const int nflt = a.L << a.P;
@@ -532,7 +536,7 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   }
   __syncthreads();
   const uint32_t theta = filt ? theta_wait(a, bh, &s_theta) : 0u;
-  uint2* slot = a.slots + static_cast<long long>(bh) * a.nchunks * CH + static_cast<long long>(chunk) * CH;
+  uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kLaneCap;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
                                                   slot, sc);
   if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
@@ -540,6 +544,45 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
 
 int scan_chunk(int L) {
   return (L == 16 || L == 32 || L == 64 || L == 128) ? kSoftChunk : kLaneChunk;
+}
+
+int scan_cap(int L) {
+  return (L == 16 || L == 32 || L == 64 || L == 128) ? kSoftCap : kLaneCap;
+}
+
+// Scan workgroups resident at once on the current device: two 1024-thread
+// workgroups per CU (cached per device).
+static int resident_scan_groups() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = 2 * cus;
+  }
+  return cached[dev];
+}
+
+// A filtering scan runs B*Hkv*nch chunk workgroups plus B*Hkv threshold
+// workgroups.  When that just overflows one resident round, the few chunks
+// left over start only once a threshold workgroup finishes, well into the
+// stream, and end the kernel late.  Lengthening the chunks (up to the slot
+// capacity) so that one round holds everything removes that tail.  With
+// several rounds the dispatcher already balances whole chunks, and shorter
+// chunks balance better, so the default length stays.
+int scan_span(const hst_shape& s, int chunk, int cap, bool filter) {
+  const long long BH = static_cast<long long>(s.B) * s.Hkv;
+  const long long N = s.Nmax;
+  if (!filter || BH <= 0 || N <= 0) return chunk;
+  const long long R0 = resident_scan_groups();
+  const long long nch0 = (N + chunk - 1) / chunk;
+  if (BH * (nch0 + 1) <= R0 || BH * (nch0 + 1) > 2 * R0) return chunk;
+  const long long nch = R0 / BH - 1;
+  if (nch < 1) return chunk;
+  const long long span = ((N + nch - 1) / nch + 63) / 64 * 64;
+  return span <= cap ? static_cast<int>(span) : chunk;
 }
 
 size_t scan_smem(int region, int chunk) {
@@ -565,8 +608,10 @@ template <int LANES, bool FILTER, bool F16>
 static hipError_t launch_scan_soft_f(dim3 grid, const FusedArgs& a, const uint8_t* ids,
                                      const void* vnorm, const int32_t* sl, const int32_t* kps,
                                      float* sout, int nch, hipStream_t st) {
-  const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
-  auto kern = scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16>;
+  const size_t smem = scan_smem(a.region_bytes, kSoftCap);
+  // chunks up to the default length take the default tile count
+  auto kern = a.span > kSoftChunk ? scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, true>
+                                  : scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, false>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, sl, kps, sout, nch, a);
@@ -588,7 +633,7 @@ template <int KIND>
 static hipError_t launch_scan_lane_t(dim3 grid, const FusedArgs& a, const void* src, const void* vnorm,
                                      int f16, const int32_t* sl, const int32_t* kps, void* sout,
                                      int filter, int nch, hipStream_t st) {
-  const size_t smem = scan_smem(a.region_bytes, kLaneChunk);
+  const size_t smem = scan_smem(a.region_bytes, kLaneCap);
   auto kern = scan_lane_kernel<KIND>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
@@ -600,9 +645,10 @@ static hipError_t launch_scan_lane_t(dim3 grid, const FusedArgs& a, const void* 
 hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, const void* src,
                        const void* vnorm, int norm_f16, void* scores_out, int filter,
                        const int32_t* kps, hipStream_t st) {
-  const int chunk = kind == kScanSoftFast ? kSoftChunk : kLaneChunk;
   // LDS ahead of the chunk tile: the kv head's table (soft-LSH) or nothing
   FusedArgs a = a_in;
+  const int chunk = a.span;
+  if (chunk < 1 || chunk > (kind == kScanSoftFast ? kSoftCap : kLaneCap)) return hipErrorInvalidValue;
   a.region_bytes = (kind == kScanSoftFast || kind == kScanSoftAny)
                        ? static_cast<int>(hst_align16(static_cast<size_t>(a.L << a.P) * 4))
                        : 0;
@@ -639,7 +685,7 @@ static hipError_t launch_scan_shared_t(dim3 grid, const FusedArgs& a, const uint
                                        const void* vn_s, const int32_t* sl, int Ns, int B,
                                        int nchp, int pitems_pad, int nchs, float* sout,
                                        hipStream_t st) {
-  const size_t smem = scan_smem(a.region_bytes, kSoftChunk);
+  const size_t smem = scan_smem(a.region_bytes, kSoftCap);  // the scratch sits past a longest tile
   auto kern = scan_shared_kernel<LANES, kScanSoftU, F16>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;

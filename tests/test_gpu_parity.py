@@ -252,6 +252,21 @@ def test_select_signs_zero_and_narrow_band():
     _check_select(tiny, 777)
 
 
+def test_select_long_chunks():
+    # 64 heads of 30000 keys: at the default chunk length the chunk and
+    # threshold workgroups just overflow one resident round, so the scan takes
+    # fewer, longer chunks (candidate slots at the longer stride)
+    rng = np.random.default_rng(12)
+    B, H, N = 8, 8, 30000
+    s = rng.random((B, H, N)).astype(np.float32)
+    lens = rng.integers(N // 2, N + 1, B)
+    lens[0] = N
+    got = _select_gpu(s, 900, seq_lens=lens)
+    for b, h in ((0, 0), (0, 7), (3, 2), (7, 5)):
+        ref = O.select_topk(s[b, h, :lens[b]].astype(np.float64), 900)
+        np.testing.assert_array_equal(got[b, h], ref, err_msg=f"b={b} h={h}")
+
+
 def test_select_empty_sequence():
     s = np.random.default_rng(1).random((2, 1, 5000)).astype(np.float32)
     _check_select(s, 10, seq_lens=[0, 5000])
