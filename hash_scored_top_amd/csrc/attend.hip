@@ -358,19 +358,10 @@ select_kernel(int32_t* __restrict__ idx, const void* __restrict__ scores, int sc
   }
 }
 
-// Raises a kernel's dynamic LDS limit once per device (the largest size
-// requested so far).
+// Raises a kernel's dynamic LDS limit (kept per kernel and device).
 template <typename K>
 static hipError_t lds_limit(K kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 template <typename T, int D, bool SELECT>

@@ -38,15 +38,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename Kern>
 static hipError_t set_lds_limit(Kern kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 // ---------------------------------------------------------------- generic path

@@ -11,6 +11,10 @@
 
 namespace hst {
 
+// Raises the dynamic LDS limit of kernel `kern` on the current device to at
+// least `bytes` (each kernel and device keeps the largest size asked so far).
+hipError_t raise_lds_limit(const void* kern, size_t bytes);
+
 hipError_t launch_hash_softlsh(const hst_shape& s, const void* K, const void* V, const void* W,
                                int L, int P, int norm_dtype, uint8_t* ids, void* vnorm,
                                hipStream_t st);

@@ -490,15 +490,7 @@ size_t mass_logits_bytes(const hst_shape& s, int kcap) {
 
 template <typename K>
 static hipError_t mass_lds_limit(K kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 hipError_t launch_select_mass(const hst_shape& s, const void* q, const void* K,

@@ -25,22 +25,15 @@
 namespace hst {
 
 constexpr int kPrepNT = 512;
-constexpr int kTabGroup = 8;  // hash tables per prep workgroup
+// hash tables per prep workgroup: 4 (8 from L = 128 on, so that a head has
+// at most 16 parts of its sample scores)
+__host__ __device__ constexpr int tab_group(int L) { return L > 64 ? 8 : 4; }
 constexpr int kSPer = kSample / kPrepNT;  // sampled keys per thread
 
-// Raises a kernel's dynamic LDS limit once per device (the largest size
-// requested so far).
+// Raises a kernel's dynamic LDS limit (kept per kernel and device).
 template <typename K>
 static hipError_t set_smem(K kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 // Sample size of head b (0 when no top-k follows or nothing is selected).
@@ -60,27 +53,29 @@ __device__ __forceinline__ void reset_scan_state(const FusedArgs& a, int bh) {
 // soft-LSH tables (+ partial sample scores)
 
 struct TabSmem {
-  int wrows, qn, z, sg, half, tl, bytes;
+  int wrows, qn, z, sg, lpair, half, tl, bytes;
 };
 
-// LDS map of one table group: W rows (padded by 16 bytes), q [G][d] and the
-// query norms [G] (float64), z [G][8P] (float64, unnormalised), half
-// products [G][hw][8] (float64), the group's float32 table [2^P][8].
-__host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P) {
+// LDS map of one group of TG tables: W rows (padded by 16 bytes), q [G][d]
+// and the query norms [G] (float64), z [G][TG*P] (float64, unnormalised), the
+// logistic pairs [G][TG*P] (float64 x 2), half products [G][hw][TG]
+// (float64), the group's float32 table [2^P][TG].
+__host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int TG) {
   const int plo = P < 4 ? P : 4;
   const int hw = (1 << plo) + (1 << (P - plo));
   TabSmem m{};
   m.wrows = 0;
-  m.qn = m.wrows + kTabGroup * P * (d * esize + 16);
+  m.qn = m.wrows + TG * P * (d * esize + 16);
   m.sg = m.qn + G * d * 8;  // the G query norms
   m.z = m.sg + G * 8;
-  m.half = m.z + G * kTabGroup * P * 8;
-  m.tl = m.half + G * hw * kTabGroup * 8;
-  m.bytes = m.tl + (kTabGroup << P) * 4;
+  m.lpair = m.z + G * TG * P * 8;
+  m.half = m.lpair + G * TG * P * 16;
+  m.tl = m.half + G * hw * TG * 8;
+  m.bytes = m.tl + (TG << P) * 4;
   return m;
 }
 
-template <typename T>
+template <typename T, int TG>
 __global__ void __launch_bounds__(kPrepNT)
 prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8_t* __restrict__ ids,
                    const void* __restrict__ vnorm, int norm_f16, const int32_t* __restrict__ seq_lens,
@@ -92,11 +87,11 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const int bh = blockIdx.x, b = bh / a.Hkv, h = bh % a.Hkv, j = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   reset_scan_state(a, bh);
-  const int l0 = j * kTabGroup, lg = min(kTabGroup, L - l0), R = lg * P;
-  const bool full8 = lg == kTabGroup && (L & 7) == 0;
+  const int l0 = j * TG, lg = min(TG, L - l0), R = lg * P;
+  const bool fullg = lg == TG && L % TG == 0;  // the group's ids are one aligned word (pair)
 
   const int plo = P < 4 ? P : 4, phi = P - plo, nlo = 1 << plo, hw = nlo + (1 << phi);
-  const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P);
+  const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P, TG);
   const int rowb = d * static_cast<int>(sizeof(T)) + 16;
   double* qn = reinterpret_cast<double*>(sm + mp.qn);
   double* zl = reinterpret_cast<double*>(sm + mp.z);
@@ -126,18 +121,26 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     qv[u] = to_f32(qsrc[e < G * d ? e : G * d - 1]);
   }
 
-  // sampled keys' ids of this table group (8 bytes per key), loads issued now
+  // sampled keys' ids of this table group (TG bytes per key), loads issued now
   int n;
   const int S = sample_size(a, seq_lens, k_per_seq, b, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
-  uint2 sid[kSPer];
+  uint32_t sid[kSPer][TG / 4];
   uint32_t svr[kSPer];
   if (S > 0) {
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
       const int i = t + u * NT;
       const long long row = base + sample_pos(i < S ? i : S - 1, S, n);
-      if (full8) sid[u] = *reinterpret_cast<const uint2*>(ids + row * L + l0);
+      if (fullg) {
+        if constexpr (TG == 8) {
+          const uint2 v = *reinterpret_cast<const uint2*>(ids + row * L + l0);
+          sid[u][0] = v.x;
+          sid[u][1] = v.y;
+        } else {
+          sid[u][0] = *reinterpret_cast<const uint32_t*>(ids + row * L + l0);
+        }
+      }
       if (j == 0)
         svr[u] = norm_f16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(vnorm)[row])
                           : static_cast<const uint32_t*>(vnorm)[row];
@@ -170,6 +173,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
       const int g = pr / R, r = pr % R;
       const unsigned char* wr = sm + mp.wrows + r * rowb;
       const double* qq = qn + g * d;
+      double ac[4] = {0.0, 0.0, 0.0, 0.0};  // four independent chains
       for (int cb = part; cb < d / E; cb += 4) {
         const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + cb * 16);
         const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -178,9 +182,10 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
           float f;
           if (sizeof(T) == 2) f = (x & 1) ? bf16_hi(ww[x >> 1]) : bf16_lo(ww[x >> 1]);
           else f = __uint_as_float(ww[x]);
-          acc += static_cast<double>(f) * qq[cb * E + x];
+          ac[x & 3] += static_cast<double>(f) * qq[cb * E + x];
         }
       }
+      acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
     }
     const double a1 = acc + __shfl_xor(acc, 1, 64);
     const double a2 = a1 + __shfl_xor(a1, 2, 64);
@@ -194,47 +199,46 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   }
   __syncthreads();
 
-  // one thread per (query head g, table ll, half of the planes): the logistic
-  // pairs of its planes (one exp each: with e = exp(-|x|), sigma(|x|) =
-  // 1 / (1 + e) and sigma(-|x|) = e / (1 + e)), then the products over those
-  // planes for every bit pattern of the half: half[(g*hw + c)*8 + ll]
-  if (t < G * lg * 2) {
-    const int g = t / (lg * 2), rem = t % (lg * 2), ll = rem >> 1, hi = rem & 1;
-    const int p0 = hi ? plo : 0, m = hi ? phi : plo, c0 = hi ? nlo : 0;
-    const double nq = nrm[g];
-    double vals[16];
-    vals[0] = 1.0;
+  // one thread per (query head g, table ll, plane p): the logistic pair of
+  // the plane (one exp: with e = exp(-|x|), sigma(|x|) = 1 / (1 + e) and
+  // sigma(-|x|) = e / (1 + e)), kept in the z slot as (bit set, bit clear)
+  double2* lp = reinterpret_cast<double2*>(sm + mp.lpair);
+  for (int r = t; r < G * R; r += NT) {
+    const double nq = nrm[r / R];
+    const double x = nq > 0.0 ? 2.0 * (zl[r] / nq) * a.inv_tau : 0.0;
+    const double e = exp(-fabs(x));
+    const double big = 1.0 / (1.0 + e), small = e * big;
+    lp[r] = x >= 0.0 ? make_double2(big, small) : make_double2(small, big);
+  }
+  __syncthreads();
+  // one thread per (query head g, table ll, half of the planes, bit pattern
+  // b of the half): the product over the half's planes in plane order,
+  // half[(g*hw + c)*8 + ll]
+  for (int e = t; e < G * lg * hw; e += NT) {
+    const int g = e / (lg * hw), rem = e % (lg * hw), ll = rem / hw, c = rem % hw;
+    const bool hi = c >= nlo;
+    const int p0 = hi ? plo : 0, m = hi ? phi : plo, b = hi ? c - nlo : c;
+    const double2* pp = lp + g * R + ll * P + p0;
+    double v = 1.0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < m) {
-        const double x = nq > 0.0 ? 2.0 * (zl[g * R + ll * P + p0 + k] / nq) * a.inv_tau : 0.0;
-        const double e = exp(-fabs(x));
-        const double big = 1.0 / (1.0 + e), small = e * big;
-        const double set = x >= 0.0 ? big : small;    // sigma(x): bit set
-        const double clear = x >= 0.0 ? small : big;  // sigma(-x): bit clear
-#pragma unroll
-        for (int b = 0; b < (1 << k); ++b) {
-          vals[b | (1 << k)] = vals[b] * set;
-          vals[b] = vals[b] * clear;
-        }
-      }
-    }
-    for (int b = 0; b < (1 << m); ++b) half[(g * hw + c0 + b) * kTabGroup + ll] = vals[b];
+    for (int k = 0; k < 4; ++k)
+      if (k < m) v *= ((b >> k) & 1) ? pp[k].x : pp[k].y;
+    half[(g * hw + c) * TG + ll] = v;
   }
   __syncthreads();
   // entries (bucket c, table l0 + ll), summed over the query heads in order;
-  // to HBM (bucket-major) and to LDS as tl[c*8 + ((ll + c) & 7)] (rotated so
+  // to HBM (bucket-major) and to LDS as tl[c*TG + ((ll + c) % TG)] (rotated so
   // lanes with different buckets use different banks)
   float* Tg = a.tables + static_cast<long long>(bh) * nb * L;
   for (int e = t; e < nb * lg; e += NT) {
     const int c = e / lg, ll = e % lg;
     double acc = 0.0;
     for (int g = 0; g < G; ++g)
-      acc += half[(g * hw + (c & (nlo - 1))) * kTabGroup + ll] *
-             half[(g * hw + nlo + (c >> plo)) * kTabGroup + ll];
+      acc += half[(g * hw + (c & (nlo - 1))) * TG + ll] *
+             half[(g * hw + nlo + (c >> plo)) * TG + ll];
     const float v = static_cast<float>(acc);
     Tg[c * L + l0 + ll] = v;
-    tl[c * kTabGroup + ((ll + c) & 7)] = v;
+    tl[c * TG + ((ll + c) & (TG - 1))] = v;
   }
   if (S == 0) return;
   __syncthreads();
@@ -247,18 +251,17 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     const int i = t + u * NT;
     if (i >= S) continue;
     float s2[2] = {0.f, 0.f};
-    if (full8) {
-      const uint32_t w2[2] = {sid[u].x, sid[u].y};
+    if (fullg) {
 #pragma unroll
-      for (int ll = 0; ll < 8; ++ll) {
-        const int c = static_cast<int>((w2[ll >> 2] >> (8 * (ll & 3))) & idm);
-        s2[ll & 1] += tl[c * kTabGroup + ((ll + c) & 7)];
+      for (int ll = 0; ll < TG; ++ll) {
+        const int c = static_cast<int>((sid[u][ll >> 2] >> (8 * (ll & 3))) & idm);
+        s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
       }
     } else {
       const uint8_t* row = ids + (base + sample_pos(i, S, n)) * L + l0;
       for (int ll = 0; ll < lg; ++ll) {
         const int c = static_cast<int>(row[ll] & idm);
-        s2[ll & 1] += tl[c * kTabGroup + ((ll + c) & 7)];
+        s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
       }
     }
     part[i] = s2[0] + s2[1];
@@ -370,7 +373,7 @@ prep_given_kernel(const KT* __restrict__ scores, const int32_t* __restrict__ seq
 // launchers
 
 int prep_parts(int kind, int L) {
-  if (kind == kScanSoftFast || kind == kScanSoftAny) return (L + kTabGroup - 1) / kTabGroup;
+  if (kind == kScanSoftFast || kind == kScanSoftAny) return (L + tab_group(L) - 1) / tab_group(L);
   return kind == kScanHamming ? 8 : 1;
 }
 
@@ -382,22 +385,25 @@ hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* 
   // linear order, so the parts of one head (B*Hkv apart) share an XCD and its
   // L2 whenever B*Hkv is a multiple of 8, and the sampled id rows are fetched
   // from HBM once per head
-  dim3 grid(s.B * s.Hkv, (a.L + kTabGroup - 1) / kTabGroup);
+  const int TG = tab_group(a.L);
+  dim3 grid(s.B * s.Hkv, (a.L + TG - 1) / TG);
+#define HST_PREP(TT, TGV)                                                                      \
+  do {                                                                                         \
+    auto kern = prep_tables_kernel<TT, TGV>;                                                   \
+    const size_t smem = tab_smem(G, s.d, static_cast<int>(sizeof(TT)), a.P, TGV).bytes;        \
+    hipError_t e = set_smem(kern, smem);                                                       \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL(kern, grid, dim3(kPrepNT), smem, st, static_cast<const TT*>(q),         \
+                       static_cast<const TT*>(W), ids, vnorm, norm_f16, s.seq_lens, kps, a);   \
+  } while (0)
   if (s.kv_dtype == HST_F32) {
-    auto kern = prep_tables_kernel<float>;
-    const size_t smem = tab_smem(G, s.d, 4, a.P).bytes;
-    hipError_t e = set_smem(kern, smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(kPrepNT), smem, st, static_cast<const float*>(q),
-                       static_cast<const float*>(W), ids, vnorm, norm_f16, s.seq_lens, kps, a);
+    if (TG == 8) HST_PREP(float, 8);
+    else HST_PREP(float, 4);
   } else {
-    auto kern = prep_tables_kernel<bf16>;
-    const size_t smem = tab_smem(G, s.d, 2, a.P).bytes;
-    hipError_t e = set_smem(kern, smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(kPrepNT), smem, st, static_cast<const bf16*>(q),
-                       static_cast<const bf16*>(W), ids, vnorm, norm_f16, s.seq_lens, kps, a);
+    if (TG == 8) HST_PREP(bf16, 8);
+    else HST_PREP(bf16, 4);
   }
+#undef HST_PREP
   return hipGetLastError();
 }
 

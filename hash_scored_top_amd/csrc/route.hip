@@ -398,15 +398,7 @@ token_route_kernel(const float* __restrict__ scores, int nitems,
 
 template <typename K>
 static hipError_t route_lds_limit(K kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 int route_chunks(int Nmax) { return (Nmax + kChunkTok - 1) / kChunkTok; }

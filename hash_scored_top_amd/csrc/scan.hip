@@ -589,19 +589,10 @@ size_t scan_smem(int region, int chunk) {
   return static_cast<size_t>(region) + static_cast<size_t>(chunk) * 4 + hst_align16(sizeof(ScanTail<kScanNT>));
 }
 
-// Raises a kernel's dynamic LDS limit once per device (the largest size
-// requested so far).
+// Raises a kernel's dynamic LDS limit (kept per kernel and device).
 template <typename K>
 static hipError_t lds_limit(K kern, size_t bytes) {
-  static size_t done[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && done[dev] >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bytes));
-  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev] = bytes;
-  return e;
+  return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
 template <int LANES, bool FILTER, bool F16>
