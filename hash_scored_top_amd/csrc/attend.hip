@@ -183,8 +183,11 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[e];
-        s += __shfl_xor(s, 8, 16);
-        s += __shfl_xor(s, 4, 16);
+        // sum over the 16 lanes of the row group, all in-row DPP (no LDS
+        // crossbar): rotations by 8 and 4, then the quad exchanges; every
+        // lane ends with the same sum
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x128, 0xF, 0xF, false));
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x124, 0xF, 0xF, false));
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, true));
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, true));
         const float mn = fmaxf(m[g], s);
@@ -197,22 +200,33 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
       }
     }
   }
-  // merge the row groups of a wave (lanes xor 16, 32), then the waves
+  // merge the row groups of a wave (lanes 16 apart, then 32 apart), then the
+  // waves.  A lane swap (v_permlane16/32_swap of a value with itself) gives
+  // every lane the pair's two states in the same order, so both lanes of a
+  // pair compute the same merge, without the LDS crossbar.
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     if (g >= G) break;
 #pragma unroll
     for (int x = 16; x <= 32; x <<= 1) {
-      const float m2 = __shfl_xor(m[g], x, 64);
-      const float l2 = __shfl_xor(l[g], x, 64);
-      const float mn = fmaxf(m[g], m2);
-      const float c1 = mn == -INFINITY ? 0.f : exp2f(m[g] - mn);
-      const float c2 = mn == -INFINITY ? 0.f : exp2f(m2 - mn);
-      l[g] = l[g] * c1 + l2 * c2;
+      const auto pair = [x](float v) {
+        const uint32_t u = __float_as_uint(v);
+        if (x == 16) {
+          const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+          return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      };
+      const float2 mp = pair(m[g]), lp = pair(l[g]);
+      const float mn = fmaxf(mp.x, mp.y);
+      const float c1 = mn == -INFINITY ? 0.f : exp2f(mp.x - mn);
+      const float c2 = mn == -INFINITY ? 0.f : exp2f(mp.y - mn);
+      l[g] = lp.x * c1 + lp.y * c2;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        const float o2 = __shfl_xor(o[g][e], x, 64);
-        o[g][e] = o[g][e] * c1 + o2 * c2;
+        const float2 op = pair(o[g][e]);
+        o[g][e] = op.x * c1 + op.y * c2;
       }
       m[g] = mn;
     }
