@@ -28,32 +28,37 @@ struct BlockScratch {
   int found[4];
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP moves (no LDS
+// crossbar): shifts by 1, 2, 4 and 8 inside each row of 16 lanes (lanes
+// shifted in from outside the row add 0), then the last lane of row 0 (2) is
+// added to row 1 (3), and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Exclusive scan of one int per thread, block wide.  All threads must call.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, BlockScratch<NT>& sc, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) sc.wsum[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < NT / 64; ++i) {
-      const int t = sc.wsum[i];
-      sc.wsum[i] = acc;
-      acc += t;
-    }
-    sc.wsum[NT / 64] = acc;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int s = sc.wsum[i];
+    tot += s;
+    if (i < w) before += s;
   }
-  __syncthreads();
-  const int excl = sc.wsum[w] + x - v;
-  total = sc.wsum[NT / 64];
-  __syncthreads();
-  return excl;
+  total = tot;
+  __syncthreads();  // sc.wsum is reused by the next call
+  return before + x - v;
 }
 
 template <int NT>

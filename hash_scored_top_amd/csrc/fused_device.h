@@ -203,12 +203,7 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
       mine += c[i];
     }
     const int lane = t & 63, w = t >> 6;
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(mine);
     if (lane == 63) sc.wsum[w] = incl;
     __syncthreads();
     int above = incl - mine;
@@ -382,12 +377,7 @@ __device__ void select_lds_regs(const uint32_t* candk, const int32_t* candi, int
           c[i] = (i < per && r < nb) ? static_cast<int>(hist[nb - 1 - r]) : 0;
           mine += c[i];
         }
-        int incl = mine;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(mine);
         if (lane == 63) sc.wsum[wave] = incl;
         __syncthreads();
         int above = incl - mine;
@@ -539,10 +529,27 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
   const int nch = (n + a.span - 1) / a.span;  // chunk c: keys [c*span, (c+1)*span), slots at c*chunk
   const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
   const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the first counts, then the first 128 slots of the first eight chunks of
+  // each wave (copied below), all in flight together: the slot addresses do
+  // not depend on the counts (slots past a chunk's count are read, unused),
+  // and the counts, issued first, arrive without waiting for the slots
+  const int cnt0 = static_cast<int>(threadIdx.x) < nch ? static_cast<int>(cnt[threadIdx.x]) : 0;
+  // (chunk indices clamped, so the loads are unconditional and the wait for
+  // the counts counts exactly the slot loads behind them)
+  uint2 pre[8][2];
+  const int clast = nch > 0 ? nch - 1 : 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = min(wave + u * NW, clast);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) pre[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
+  }
   int run = 0;
   for (int c0 = 0; c0 < nch; c0 += NT) {
     const int c = c0 + static_cast<int>(threadIdx.x);
-    const int v = c < nch ? static_cast<int>(cnt[c]) : 0;
+    const int v = c0 == 0 ? cnt0 : (c < nch ? static_cast<int>(cnt[c]) : 0);
     int tot;
     const int x = block_excl_scan<NT>(v, sc, tot);
     if (c < nch) ws.offs[c] = run + x;
@@ -556,9 +563,7 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
   if (k_eff > 0) {
     if (M >= k_eff && M <= kSelCap) {
       // each wave copies whole chunks (coalesced): eight chunks and sixteen
-      // loads per lane in flight
-      constexpr int NW = NT / 64;
-      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      // loads per lane in flight (the first eight already loaded)
       for (int c0 = wave; c0 < nch; c0 += NW * 8) {
         uint2 v[8][2];
         int cnt[8], base[8];
@@ -568,8 +573,10 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
           cnt[u] = c < nch ? ws.offs[c + 1] - ws.offs[c] : 0;
           base[u] = c < nch ? ws.offs[c] : 0;
 #pragma unroll
-          for (int x = 0; x < 2; ++x)
-            if (lane + 64 * x < cnt[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
+          for (int x = 0; x < 2; ++x) {
+            if (c0 == wave) v[u][x] = pre[u][x];
+            else if (lane + 64 * x < cnt[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
+          }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
