@@ -429,7 +429,8 @@ def main():
     # with events on the stream it is launched on
     if w.scheme == "softlsh":
         f16 = "true" if w.norm_dtype == "f16" else "false"
-        kname = f"scan_softlsh_kernel<{w.L // 16}, 2, false, {f16}>"  # scores only, no candidate filter
+        # scores only (no candidate filter), default chunk length
+        kname = f"scan_softlsh_kernel<{w.L // 16}, 2, false, {f16}, false>"
         ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
         tables = hst.hst_query_tables_softlsh(q, Wp, w.L, w.P, w.tau, K, seq_lens=sl)
         sc = torch.empty((w.B, w.Hkv, w.N), dtype=torch.float32, device=dev)
