@@ -321,9 +321,11 @@ __device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, i
 // how many keys equal to it are taken, without further passes.  The result
 // is the masked-prefix rule of radix_select_regs.  Writes the selected
 // indices at output positions [r0, r1).  hist: 2048 words of LDS.
+// candi: the entries' key indices, anything indexable by position (an LDS
+// array, or a map from positions to indices).
 constexpr int kRankBin = 64;
-template <int NT, int PERW>
-__device__ void select_lds_regs(const uint32_t* candk, const int32_t* candi, int M, int k, int r0, int r1,
+template <int NT, int PERW, class Idx>
+__device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
                                 int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
   constexpr int NW = NT / 64;
   constexpr int MAXPER = (2048 + NT - 1) / NT;
@@ -487,7 +489,7 @@ __device__ void select_lds_regs(const uint32_t* candk, const int32_t* candi, int
     const unsigned long long selb = __ballot(sel);
     const int pos = run + lanes_below(selb);
     if (sel && pos >= r0 && pos < r1) {
-      const int32_t v = candi[p];
+      const int32_t v = static_cast<int32_t>(candi[p]);
       if (out_g != nullptr) out_g[pos] = v;
       if (out_l != nullptr) out_l[pos - r0] = v;
     }

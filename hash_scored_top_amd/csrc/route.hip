@@ -27,8 +27,7 @@
 // Both cut by a radix select of count histograms (12, 10, 10 bits; after
 // the first level only the crossing bucket's items are visited); ties go
 // to the lower position, which is the lower index; output ascending.
-#include "hst_common.h"
-#include "hst_fused.h"
+#include "fused_device.h"
 #include "hst_launch.h"
 #include "table_lds.h"
 
@@ -290,10 +289,17 @@ __device__ __forceinline__ uint32_t block_count_nonzero(const uint32_t* key, int
   return s;
 }
 
+// A card's position is its chunk index.
+struct PosIdx {
+  __device__ __forceinline__ int32_t operator[](int r) const { return r; }
+};
+
 // Chunk routing for one (sequence, kv head): the head's table (table-major
 // in LDS) scores every card, and the C best cards (score descending, chunk
-// ascending) are written ascending to chunks[bh][0..C), then -1.
-template <int L>
+// ascending) are written ascending to chunks[bh][0..C), then -1.  REGS: the
+// selection on register-held keys, two cards per lane (Nc <= 2048); else the
+// count-histogram cut (more cards would spill the registers).
+template <int L, bool REGS>
 __global__ void __launch_bounds__(kTopNT)
 card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ cids,
                   const void* __restrict__ cw, int norm_f16, const int32_t* __restrict__ seq_lens,
@@ -302,11 +308,11 @@ card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ 
   const int nb = 1 << P;
   const size_t tbytes = static_cast<size_t>(L) * (nb + 1) * 4;
   const size_t cbytes = static_cast<size_t>(Nc) * 4;
-  float* tl = reinterpret_cast<float*>(sm);                                   // table, then cand
-  uint32_t* cand = reinterpret_cast<uint32_t*>(sm);
+  float* tl = reinterpret_cast<float*>(sm);  // table, then the cut's candidates (count-histogram cut)
   uint32_t* key = reinterpret_cast<uint32_t*>(sm + (tbytes > cbytes ? tbytes : cbytes));
   uint32_t* hist = key + Nc;                                                  // 4096
   __shared__ uint32_t red[kTopNT / 64];
+  __shared__ BlockScratch<kTopNT> tsc;
   __shared__ uint64_t red64[kTopNT / 64];
   __shared__ uint32_t vars[4], total;
   const int bh = blockIdx.x, b = bh / Hkv, t = threadIdx.x;
@@ -340,11 +346,25 @@ card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ 
   }
   __syncthreads();
   const uint32_t valid = block_count_nonzero(key, Nc, red);
-  const Cut cut = block_cut(key, Nc, valid, static_cast<uint32_t>(min(C, nc)),
-                            CutScratch{hist, cand, red, vars});
-  block_cut_compact(key, Nc, cut, chunks + static_cast<long long>(bh) * C, C, red64, &total,
-                    [](int r) { return r; });
+  int32_t* orow = chunks + static_cast<long long>(bh) * C;
+  if constexpr (REGS) {
+    // the C best cards (fewer if fewer chunks exist), ascending, then -1
+    const int ks = min(min(C, nc), static_cast<int>(valid));
+    if (ks > 0) select_lds_regs<kTopNT, 2>(key, PosIdx{}, Nc, ks, 0, ks, orow, nullptr, hist, tsc);
+    for (int p = ks + t; p < C; p += kTopNT) orow[p] = -1;
+  } else {
+    const Cut cut = block_cut(key, Nc, valid, static_cast<uint32_t>(min(C, nc)),
+                              CutScratch{hist, reinterpret_cast<uint32_t*>(sm), red, vars});
+    block_cut_compact(key, Nc, cut, orow, C, red64, &total, [](int r) { return r; });
+  }
 }
+
+// Position r of the scored keys of the kept chunks (slot r / 64, token r % 64)
+// as a key index.
+struct ChunkIdx {
+  const int32_t* cl;  // kept chunks, ascending (LDS)
+  __device__ __forceinline__ int32_t operator[](int r) const { return cl[r / kChunkTok] * kChunkTok + (r % kChunkTok); }
+};
 
 // Token routing: the k (or k_per_seq[b]) best of the scored keys of the kept
 // chunks, as key indices, ascending.
@@ -352,14 +372,12 @@ __global__ void __launch_bounds__(kTopNT)
 token_route_kernel(const float* __restrict__ scores, int nitems,
                    const int32_t* __restrict__ chunks, int C, int k,
                    const int32_t* __restrict__ k_per_seq, int Hkv, int32_t* __restrict__ out) {
-  extern __shared__ __align__(16) uint32_t keybuf[];  // [nitems] keys, [nitems] cand, [4096] hist
+  extern __shared__ __align__(16) uint32_t keybuf[];  // [nitems] keys, [2048] hist
   __shared__ uint32_t red[kTopNT / 64];
-  __shared__ uint64_t red64[kTopNT / 64];
-  __shared__ uint32_t vars[4], total;
+  __shared__ BlockScratch<kTopNT> tsc;
   const int bh = blockIdx.x, b = bh / Hkv, t = threadIdx.x;
   uint32_t* key = keybuf;
-  uint32_t* cand = keybuf + nitems;
-  uint32_t* hist = cand + nitems;
+  uint32_t* hist = keybuf + nitems;  // 2048 words of radix histogram
   __shared__ int32_t cl[kRouteMaxChunks];
   const float* sr = scores + static_cast<long long>(bh) * nitems;
   const int32_t* crow = chunks + static_cast<long long>(bh) * C;
@@ -390,10 +408,15 @@ token_route_kernel(const float* __restrict__ scores, int nitems,
   const uint32_t valid = block_count_nonzero(key, nitems, red);
   int kb = k_per_seq != nullptr ? k_per_seq[b] : k;
   kb = max(0, min(kb, k));
-  const Cut cut = block_cut(key, nitems, valid, static_cast<uint32_t>(kb),
-                            CutScratch{hist, cand, red, vars});
-  block_cut_compact(key, nitems, cut, out + static_cast<long long>(bh) * k, k, red64, &total,
-                    [clp = &cl[0]](int r) { return clp[r / kChunkTok] * kChunkTok + (r % kChunkTok); });
+  // the kb best (fewer if fewer keys exist: a missing key's order key 0 is
+  // below every real one, so it is never among them), by the selection on
+  // register-held keys; positions map to key indices through the kept chunks
+  const int ks = min(kb, static_cast<int>(valid));
+  int32_t* orow = out + static_cast<long long>(bh) * k;
+  if (ks > 0)
+    select_lds_regs<kTopNT, kRouteMaxChunks * kChunkTok / kTopNT>(key, ChunkIdx{cl}, nitems, ks, 0, ks, orow,
+                                                                   nullptr, hist, tsc);
+  for (int p = ks + t; p < k; p += kTopNT) orow[p] = -1;
 }
 
 template <typename K>
@@ -446,7 +469,7 @@ hipError_t launch_route_scan(const hst_shape& s, const float* tables, const int3
 
 size_t card_route_smem(int L, int P, int Nc) {
   const size_t tb = static_cast<size_t>(L) * ((1u << P) + 1) * 4, cb = static_cast<size_t>(Nc) * 4;
-  return (tb > cb ? tb : cb) + static_cast<size_t>(Nc) * 4 + 4096 * 4;
+  return (tb > cb ? tb : cb) + static_cast<size_t>(Nc) * 4 + 4096 * 4;  // table, keys, histogram
 }
 
 hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint8_t* cids,
@@ -455,12 +478,18 @@ hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint
   const int Nc = route_chunks(s.Nmax);
   const size_t smem = card_route_smem(L, P, Nc);
   hipError_t e;
-#define HST_CARD_L(LL)                                                                           \
-  case LL:                                                                                       \
-    e = route_lds_limit(card_route_kernel<LL>, smem);                                            \
-    if (e != hipSuccess) return e;                                                               \
-    hipLaunchKernelGGL(card_route_kernel<LL>, dim3(s.B * s.Hkv), dim3(kTopNT), smem, st, tables, \
-                       cids, cw, norm_f16, s.seq_lens, s.Hkv, s.Nmax, Nc, P, C, chunks);         \
+  const bool regs = Nc <= 2 * kTopNT;
+#define HST_CARD_LP(LL, RG)                                                                    \
+  do {                                                                                         \
+    e = route_lds_limit(card_route_kernel<LL, RG>, smem);                                      \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((card_route_kernel<LL, RG>), dim3(s.B * s.Hkv), dim3(kTopNT), smem, st,  \
+                       tables, cids, cw, norm_f16, s.seq_lens, s.Hkv, s.Nmax, Nc, P, C, chunks); \
+  } while (0)
+#define HST_CARD_L(LL)                    \
+  case LL:                                \
+    if (regs) HST_CARD_LP(LL, true);      \
+    else HST_CARD_LP(LL, false);          \
     break;
   switch (L) {
     HST_CARD_L(16)
@@ -469,6 +498,7 @@ hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint
     HST_CARD_L(128)
     default: return hipErrorInvalidValue;
   }
+#undef HST_CARD_LP
 #undef HST_CARD_L
   return hipGetLastError();
 }
@@ -476,7 +506,7 @@ hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint
 hipError_t launch_token_route(const hst_shape& s, const float* scores, int nitems,
                               const int32_t* chunks, int C, int k, const int32_t* kps,
                               int32_t* out, hipStream_t st) {
-  const size_t smem = static_cast<size_t>(nitems) * 8 + 4096 * 4;
+  const size_t smem = static_cast<size_t>(nitems) * 4 + 2048 * 4;
   hipError_t e = route_lds_limit(token_route_kernel, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(token_route_kernel, dim3(s.B * s.Hkv), dim3(kTopNT), smem, st, scores, nitems,
