@@ -24,9 +24,12 @@
 //   token_route_kernel one 1024-thread workgroup per (sequence, kv head):
 //                      the exact top k of the scored keys, mapped from
 //                      positions in the kept chunks to key indices.
-// Both cut by a radix select of count histograms (12, 10, 10 bits; after
-// the first level only the crossing bucket's items are visited); ties go
-// to the lower position, which is the lower index; output ascending.
+// Both cut with the selection of the attention kernel (keys held in
+// registers, radix passes, a direct rank of a small boundary bin, ballot
+// compaction); a card cut over more than 2048 cards uses a radix select of
+// count histograms (12, 10, 10 bits; after the first level only the
+// crossing bucket's items are visited) instead.  Ties go to the lower
+// position, which is the lower index; output ascending.
 #include "fused_device.h"
 #include "hst_launch.h"
 #include "table_lds.h"
