@@ -77,7 +77,8 @@ int prep_parts(int kind, int L);  // partial sample scores per head (prep workgr
 int scan_chunk(int L);  // default keys per scan chunk
 int scan_cap(int L);    // candidate slots per chunk: the longest chunk a scan workgroup takes
 // keys per chunk of a filtering scan over s (slot stride cap, default length
-// chunk): lengthened (up to cap) when that fits the grid in one resident round
+// chunk): lengthened (up to cap) when the threshold workgroups would
+// otherwise add a round of resident workgroups
 int scan_span(const hst_shape& s, int chunk, int cap, bool filter);
 // filter != 0: the scan also derives each head's candidate threshold from the
 // partial sample scores (prep with sampling must precede it) and fills the

@@ -566,20 +566,21 @@ static int resident_scan_groups() {
 }
 
 // A filtering scan runs B*Hkv*nch chunk workgroups plus B*Hkv threshold
-// workgroups.  When that just overflows one resident round, the few chunks
-// left over start only once a threshold workgroup finishes, well into the
-// stream, and end the kernel late.  Lengthening the chunks (up to the slot
-// capacity) so that one round holds everything removes that tail.  With
-// several rounds the dispatcher already balances whole chunks, and shorter
-// chunks balance better, so the default length stays.
+// workgroups.  When the threshold workgroups add a round of resident
+// workgroups that the chunks alone would not need, the chunks left over for
+// it start only once earlier workgroups finish and end the kernel late.
+// Lengthening the chunks (up to the slot capacity) so that the chunks and
+// thresholds fit the chunks' own rounds removes that tail.
 int scan_span(const hst_shape& s, int chunk, int cap, bool filter) {
   const long long BH = static_cast<long long>(s.B) * s.Hkv;
   const long long N = s.Nmax;
   if (!filter || BH <= 0 || N <= 0) return chunk;
   const long long R0 = resident_scan_groups();
   const long long nch0 = (N + chunk - 1) / chunk;
-  if (BH * (nch0 + 1) <= R0 || BH * (nch0 + 1) > 2 * R0) return chunk;
-  const long long nch = R0 / BH - 1;
+  const long long r_chunks = (BH * nch0 + R0 - 1) / R0;        // rounds of the chunks alone
+  const long long r_all = (BH * (nch0 + 1) + R0 - 1) / R0;     // with the threshold workgroups
+  if (r_all == r_chunks) return chunk;
+  const long long nch = r_chunks * R0 / BH - 1;
   if (nch < 1) return chunk;
   const long long span = ((N + nch - 1) / nch + 63) / 64 * 64;
   return span <= cap ? static_cast<int>(span) : chunk;
