@@ -234,82 +234,6 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
   }
 }
 
-// Exact selection over M <= NT * PER candidates held in LDS in index order
-// (order keys in candk, key indices in candi).  The radix passes work on the
-// keys held in registers (entry t + e * NT in key[e]); the compaction walks
-// one contiguous range per wave twice: counts first, then the output
-// positions from ballots.  Writes the selected indices at output positions
-// [r0, r1).
-template <int NT, int PER>
-__device__ void select_lds(const uint32_t* candk, const int32_t* candi, int M, int k, int r0, int r1,
-                           int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
-  constexpr int NW = NT / 64;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  uint32_t mask = 0u, prefix = 0u;
-  int krem = k >= M ? M : k;
-  if (k < M) {
-    uint32_t key[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) key[e] = t + e * NT < M ? candk[t + e * NT] : 0u;
-    radix_select_regs<NT, PER>(key, M, k, 32, hist, sc, mask, prefix, krem);
-  }
-  // compaction: wave w owns entries [lo, hi) in index order
-  const int span = (M + NW - 1) / NW;
-  const int lo = min(M, wave * span), hi = min(M, lo + span);
-  int gtc = 0, eqc = 0;
-  for (int i0 = lo; i0 < hi; i0 += 256) {  // four reads per lane in flight
-    uint32_t m[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      m[u] = i < hi ? (candk[i] & mask) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      gtc += __popcll(__ballot(i < hi && m[u] > prefix));
-      eqc += __popcll(__ballot(i < hi && m[u] == prefix));
-    }
-  }
-  if (lane == 0) {
-    sc.red[0][wave] = static_cast<uint32_t>(gtc);
-    sc.red[1][wave] = static_cast<uint32_t>(eqc);
-  }
-  __syncthreads();
-  int gt_before = 0, eq_run = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += static_cast<int>(sc.red[0][w]);
-    eq_run += static_cast<int>(sc.red[1][w]);
-  }
-  __syncthreads();  // sc.red is reused by the caller
-  int sel_run = gt_before + min(eq_run, krem);
-  for (int i0 = lo; i0 < hi && sel_run < r1; i0 += 256) {  // wave-uniform loop
-    uint32_t m[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      m[u] = i < hi ? (candk[i] & mask) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      const bool gt = i < hi && m[u] > prefix;
-      const bool eq = i < hi && m[u] == prefix;
-      const unsigned long long eqb = __ballot(eq);
-      const bool sel = gt || (eq && eq_run + lanes_below(eqb) < krem);
-      const unsigned long long selb = __ballot(sel);
-      const int pos = sel_run + lanes_below(selb);
-      if (sel && pos >= r0 && pos < r1) {
-        const int32_t v = candi[i];
-        if (out_g != nullptr) out_g[pos] = v;
-        if (out_l != nullptr) out_l[pos - r0] = v;
-      }
-      sel_run += __popcll(selb);
-      eq_run += __popcll(eqb);
-    }
-  }
-}
-
 // Exact selection over M <= NT * PERW candidates held in LDS in index order,
 // on keys held in registers: wave w holds the entries at positions
 // [lo_w, hi_w) (lane l's entry u at lo_w + 64u + l), the order in which the
