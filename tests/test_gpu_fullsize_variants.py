@@ -6,7 +6,8 @@
   attention over it matches the oracle;
 * routed step at the 128K workload (252 chunks kept): cards bit-exact on
   sampled slabs; kept chunks and selected keys equal the oracle's up to
-  float32 near-ties; attention within the bf16 tolerance;
+  float32 near-ties; attention within the bf16 tolerance; and past 2048
+  cards per head (140000 keys), where the card cut changes method;
 * shared-prefix step on a batch of 8 sharing a 32768-key prefix with ragged
   suffixes: sampled slabs against the oracle over the concatenated context;
 * 64- and 256-bit codes at the binary-code workload's shape (B16, 64K):
@@ -121,6 +122,47 @@ def test_routed_step_at_128k(longctx):
         if np.array_equal(got, r["idx"]):
             assert np.abs(out[0, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, h
             np.testing.assert_allclose(lse[0, h * G:(h + 1) * G], r["lse"], rtol=1e-4, atol=1e-4)
+
+
+def test_routed_step_past_2048_cards():
+    # 140000 keys: 2188 cards per head, so the card cut takes the
+    # count-histogram path (the register-held selection takes up to 2048)
+    import dataclasses
+    import hash_scored_top_amd as hst
+    base = WL.WORKLOADS["longctx_softlsh_b1_n128k"]
+    w = dataclasses.replace(base, name="route_many_cards", N=140000)
+    x = WL.make_full(w)
+    kmax = int(x["k_per_seq"].max())
+    C = min(256, 4 * math.ceil(kmax / 64))
+    print(f"[fullsize-variants] routed step N={w.N} C={C}", flush=True)
+    K, V, q, Wp = (to_dev(x[n], w.kv_dtype, DEV) for n in ("K", "V", "q", "W"))
+    nd = norm_torch_dtype(w.norm_dtype)
+    ids, vn = hst.hst_hash_keys_softlsh(K, V, Wp, w.L, w.P, nd)
+    _, cids, cw, clens = hst.hst_build_cards_softlsh(K, vn, Wp, w.L, w.P)
+    assert cids.shape[2] > 2048
+    step = hst.DecodeSoftLSHRouted(K, w.Hq, w.L, w.P, w.tau, kmax, C, nd)
+    idx, out, lse = step(q, K, V, Wp, ids, vn, cids, cw)
+    torch.cuda.synchronize()
+    idx, out = idx.cpu().numpy(), out.cpu().numpy()
+    f64 = lambda a: WL.storage_to_f64(a, w.kv_dtype)
+    G = w.G
+    for h in (0, w.Hkv - 1):
+        qg = f64(x["q"][0, h * G:(h + 1) * G])
+        K64, V64 = f64(x["K"][0, h]), f64(x["V"][0, h])
+        r = O.route_slab_softlsh(qg, K64, V64, f64(x["W"][h]), w.L, w.P, w.tau, kmax, C,
+                                 w.norm_dtype, w.kv_dtype)
+        got = idx[0, h, :kmax]
+        assert (np.diff(got) > 0).all() and (idx[0, h, kmax:] == -1).all()
+        # every selected key in one of the oracle's kept chunks, up to near-ties
+        # of the C-th card score
+        outside = set((got // 64).tolist()) - set(np.asarray(r["chunks"]).tolist())
+        kth = np.sort(r["chunk_scores"])[::-1][C - 1]
+        for c in outside:
+            assert abs(r["chunk_scores"][c] - kth) <= 2e-5 * kth, (h, c)
+        if not outside:
+            pos = lambda a: np.searchsorted(r["keys"], a)
+            if _band(r["scores"], pos(got), pos(r["idx"]), kmax) == 0:
+                assert np.abs(out[0, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, h
 
 
 def test_shared_prefix_step_at_bench_size():
