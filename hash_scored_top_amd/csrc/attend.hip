@@ -25,6 +25,7 @@ template <>
 struct RowLd<bf16, 8> {
   typedef u32x4 raw;
   static __device__ __forceinline__ raw load(const bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+  static __device__ __forceinline__ uint32_t word(const raw& v, int i) { return v[i]; }
   static __device__ __forceinline__ void cvt(const raw& v, float (&x)[8]) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
     x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
@@ -34,6 +35,7 @@ template <>
 struct RowLd<bf16, 4> {
   typedef uint2 raw;
   static __device__ __forceinline__ raw load(const bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+  static __device__ __forceinline__ uint32_t word(const raw& v, int i) { return i == 0 ? v.x : v.y; }
   static __device__ __forceinline__ void cvt(const raw& v, float (&x)[4]) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
   }
@@ -64,6 +66,14 @@ struct RowLd<float, 4> {
   }
 };
 
+// Dot product of two packed bf16 pairs added to c: both products are exact in
+// fp32, the sum is taken in fp32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), c,
+                                         false);
+}
+
 // LDS of the attend kernel: [64 KB: candidate keys and indices, later the
 // wave partials][hist 8 KB][chunk offsets][rows of this split]
 static_assert(8 * kSelCap <= 65536, "candidate region");
@@ -74,8 +84,11 @@ size_t attend_smem(int nchunks, int rps) {
 // grid (nsplit, B*Hkv).  SELECT: rows come from the head's selection (and
 // the split's part of the index row is written to idx); otherwise rows are
 // read from idx.  Rows outside [0, N_b) are skipped.
+// bf16 rows with up to four query heads per kv head fit 128 VGPRs, so that two
+// workgroups share a CU.
 template <typename T, int D, int GMAX, bool SELECT>
 __global__ void __launch_bounds__(kAttNT)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && GMAX <= 4 ? 4 : 1)))
 attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
               int32_t* __restrict__ idx, const void* __restrict__ scores, int scores_int, int chunk,
               const int32_t* __restrict__ seq_lens, float scale_log2, FusedArgs a) {
@@ -84,6 +97,9 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   constexpr int NW = NT / 64;
   constexpr int NG = NT / 16;
   constexpr int U = 4;
+  // bf16 rows: q stays in packed bf16 pairs and each lane's part of a score is
+  // a chain of pair dot products, scaled once after the row-group sum
+  constexpr bool PK = sizeof(T) == 2;
   extern __shared__ __align__(16) unsigned char sm[];
   __shared__ BlockScratch<NT> sc;
   __shared__ float red_ml[NW][GMAX][2];
@@ -119,6 +135,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   __syncthreads();
 
   float qv[GMAX][EPL];
+  uint32_t qp[GMAX][EPL / 2];
   {
     typename RowLd<T, EPL>::raw qr[GMAX];
 #pragma unroll
@@ -126,7 +143,10 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
       if (g < G) qr[g] = RowLd<T, EPL>::load(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL);
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      if (g < G) {
+      if constexpr (PK) {
+#pragma unroll
+        for (int w = 0; w < EPL / 2; ++w) qp[g][w] = g < G ? RowLd<T, EPL>::word(qr[g], w) : 0u;
+      } else if (g < G) {
         RowLd<T, EPL>::cvt(qr[g], qv[g]);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
@@ -171,33 +191,67 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
       kr[u] = RowLd<T, EPL>::load(kp[u]);
       vr[u] = RowLd<T, EPL>::load(vp[u]);
     }
+    // scores of the batch's rows for every query head slot (slots past G
+    // hold a zero query and are never written out); an absent row scores -inf
+    float sc[U][GMAX];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (!ok[u]) continue;  // uniform over the 16 lanes of a row group
-      float kx[EPL], vx[EPL];
-      RowLd<T, EPL>::cvt(kr[u], kx);
-      RowLd<T, EPL>::cvt(vr[u], vx);
+      float kx[EPL];
+      if constexpr (!PK) RowLd<T, EPL>::cvt(kr[u], kx);
 #pragma unroll
       for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) break;
         float s = 0.f;
+        if constexpr (PK) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[e];
+          for (int w = 0; w < EPL / 2; ++w) s = dot2_bf16(qp[g][w], RowLd<T, EPL>::word(kr[u], w), s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s += qv[g][e] * kx[e];
+        }
         // sum over the 16 lanes of the row group, all in-row DPP (no LDS
         // crossbar): rotations by 8 and 4, then the quad exchanges; every
-        // lane ends with the same sum
-        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x128, 0xF, 0xF, false));
-        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x124, 0xF, 0xF, false));
+        // lane ends with the same sum.  Every lane of a row rotation reads a
+        // lane of its own row, so bound_ctrl changes nothing there; set, it
+        // lets the move fold into the add.
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x128, 0xF, 0xF, true));
+        s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x124, 0xF, 0xF, true));
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, true));
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, true));
-        const float mn = fmaxf(m[g], s);
-        const float c = exp2f(m[g] - mn);
-        const float p = exp2f(s - mn);
-        l[g] = l[g] * c + p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * c + p * vx[e];
-        m[g] = mn;
+        if constexpr (PK) s *= scale_log2;
+        sc[u][g] = ok[u] ? s : -INFINITY;
       }
+    }
+    // one online-softmax step per batch: the running state of each head is
+    // rescaled once to the batch's new maximum, then the rows are added.
+    // While a head has seen no row its maximum stays -inf and the exponents
+    // are taken against 0, so that every weight is exactly 0 (never NaN).
+    float pw[U][GMAX];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+      float mx = m[g];
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+      const float ms = mx == -INFINITY ? 0.f : mx;
+      const float c = __builtin_amdgcn_exp2f(m[g] - ms);
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pw[u][g] = __builtin_amdgcn_exp2f(sc[u][g] - ms);
+        ps += pw[u][g];
+      }
+      l[g] = l[g] * c + ps;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] *= c;
+      m[g] = mx;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vx[EPL];
+      RowLd<T, EPL>::cvt(vr[u], vx);
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] += pw[u][g] * vx[e];
     }
   }
   // merge the row groups of a wave (lanes 16 apart, then 32 apart), then the
