@@ -37,6 +37,11 @@ MED_HAM = dataclasses.replace(
     WL.WORKLOADS["hata_hamming_b16_n64k"], name="med_ham", B=3, Hq=8, Hkv=2, N=9000,
     needles=8, ragged=(4000, 9000), seed=98)
 TINY = WL.WORKLOADS["tiny_softlsh_fp32"]
+# query heads per kv head below the attention kernel's head-slot count (3 of
+# 4 and 5 of 8): the spare slots carry a zero query and are never written
+MED_G3 = dataclasses.replace(MED_SOFT, name="med_g3", Hq=6, Hkv=2, seed=97)
+MED_G5 = dataclasses.replace(MED_SOFT, name="med_g5", Hq=10, Hkv=2, N=5000, ragged=(2000, 5000),
+                             seed=96)
 
 _CACHE = {}
 
@@ -296,8 +301,10 @@ def _attn_case(w, ks):
 
 
 @pytest.mark.parametrize("w,ks", [(TINY, [128]), (TINY, [4096]), (TINY, [1]),
-                                  (MED_SOFT, [182, 1, 999]), (MED_HAM, [3000, 17])],
-                         ids=["tiny_k128", "tiny_dense", "tiny_k1", "med_soft", "med_ham"])
+                                  (MED_SOFT, [182, 1, 999]), (MED_HAM, [3000, 17]),
+                                  (MED_G3, [700, 5]), (MED_G5, [1500, 33])],
+                         ids=["tiny_k128", "tiny_dense", "tiny_k1", "med_soft", "med_ham",
+                              "med_g3", "med_g5"])
 def test_attention_parity(w, ks):
     out, lse, refs = _attn_case(w, ks)
     G = w.G
@@ -330,7 +337,7 @@ def test_attention_padding_and_empty():
 
 # ---------------------------------------------------------------- end to end
 
-@pytest.mark.parametrize("w", [TINY, MED_SOFT], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, MED_SOFT, MED_G3], ids=lambda w: w.name)
 def test_decode_softlsh_end_to_end(w):
     hst = _hst()
     from tests.gpu_helpers import norm_torch_dtype
