@@ -34,6 +34,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every csrc/*.hip to an object, then link libhst.so."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    # objects of sources that no longer exist would otherwise linger in the
+    # build folder (they are never linked, but they are shipped with the tree)
+    live = {os.path.basename(s) + ".o" for s in srcs}
+    for stale in glob.glob(os.path.join(BUILD, "*.o")):
+        if os.path.basename(stale) not in live:
+            os.remove(stale)
     objs = []
     procs = []
     for src in srcs:

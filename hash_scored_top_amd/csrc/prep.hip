@@ -1,7 +1,8 @@
 // Per-step query preprocessing, X workgroups per (sequence, kv head).
 //
 //  * Soft-LSH (SOCKET overview page, "Core mechanism: soft LSH", item 2):
-//    workgroup j builds the query tables of hash tables [8j, 8j + 8).  The
+//    workgroup j builds the query tables of hash tables [TG*j, TG*j + TG)
+//    (TG = 4, or 8 from 128 tables on; see tab_group).  The
 //    normalised query of each of the G query heads is projected on the
 //    hyperplanes of those tables (float64: z = W q_hat), and a table's bucket
 //    probabilities are the temperature softmax over all 2^P buckets of
@@ -15,7 +16,7 @@
 //    [16j, 16j + 16) of the G query codes, each the exact sign of a projection.
 //
 // When a top-k follows, each workgroup also scores the key sample on its own
-// part of the hash (its 8 tables, its 16 code bits), reading only that slice
+// part of the hash (its TG tables, its 16 code bits), reading only that slice
 // of each sampled key's metadata; the scan adds the parts up and derives the
 // candidate threshold theta from them (scan.hip).  theta only bounds the work
 // of the selection: the selected set never depends on it.

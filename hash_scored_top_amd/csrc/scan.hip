@@ -19,6 +19,8 @@
 // no other memory needs ordering.  Every wait is bounded: past the bound it
 // falls back to threshold 0 (every key a candidate), which leaves the
 // selection exact, so no dispatch order can stall the kernel.
+#include <atomic>
+
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -551,18 +553,21 @@ int scan_cap(int L) {
 }
 
 // Scan workgroups resident at once on the current device: two 1024-thread
-// workgroups per CU (cached per device).
+// workgroups per CU.  The count is cached per device in an atomic: threads
+// that race on the first call all store the same value.
 static int resident_scan_groups() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached[dev] = 2 * cus;
+    v = 2 * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 // A filtering scan runs B*Hkv*nch chunk workgroups plus B*Hkv threshold

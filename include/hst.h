@@ -48,8 +48,11 @@
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *     null stream) and never synchronizes.  Arguments are validated on the
  *     host before anything is enqueued; on error nothing is launched.
- *   - Calls are reentrant; the library holds no mutable global state except
- *     the thread-local last HIP error.
+ *   - Calls are reentrant and may be made from several host threads at once.
+ *     The only process-wide state is host-side and set once per device: the
+ *     raised dynamic-LDS limit of each kernel (a table under a mutex) and the
+ *     device's compute-unit count (an atomic cache); plus the thread-local
+ *     last HIP error.
  */
 #ifndef HST_H_
 #define HST_H_
@@ -132,7 +135,8 @@ hst_status hst_hash_keys_softlsh(const hst_shape* shape, const void* K,
  * Prefill binary codes of keys [HATA, section 3; random-projection stand-in
  * for the learned hash]:
  *   bit i of codes[b][h][j] = [ R[h][i] . K[b][h][j] >= 0 ]  (exact sign)
- * code_bits must be 128.  No workspace.
+ * code_bits is 64, 128 or 256 (R holds that many rows per kv head).  No
+ * workspace.  Errors: HST_ERR_UNSUPPORTED for any other code_bits.
  */
 hst_status hst_hash_keys_binary(const hst_shape* shape, const void* K,
                                 const void* R, int code_bits, uint32_t* codes,

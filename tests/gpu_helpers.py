@@ -31,3 +31,26 @@ def cancel_case(rng, d, nplanes, n):
     pert = kind == 4                         # antisymmetric but one channel nudged by an ulp
     K[pert, d - 1] = bf(K[pert, d - 1] * (1.0 + 2.0 ** -7))
     return W.astype(np.float32), K.astype(np.float32)
+
+
+def check_attention(out_g, lse_g, qg, K64, V64, sel, kv_dtype, scale=None, where=""):
+    """The GPU's attention rows (out_g [G, d], lse_g [G] or None) against the
+    oracle's exact attention over the GPU's own selected set `sel` (context
+    indices of K64/V64): 1e-5 of the output scale for fp32 K/V, 2e-2 absolute
+    for bf16; the log-sum-exp within 1e-4.  Used on every checked slab, so a
+    selection that differs from the oracle's at a near-tie still has its
+    attention checked."""
+    import math
+    import oracle as O
+    if scale is None:
+        scale = 1.0 / math.sqrt(K64.shape[1])
+    ro, rl = O.attend(qg, K64, V64, np.asarray(sel, dtype=np.int64), scale)
+    if kv_dtype == "f32":
+        tol = 1e-5 * max(np.abs(ro).max(), 1e-30)
+    else:
+        tol = 2e-2
+    err = np.abs(np.asarray(out_g, dtype=np.float64) - ro).max()
+    assert err <= tol, (where, "out", err, tol)
+    if lse_g is not None:
+        np.testing.assert_allclose(np.asarray(lse_g, dtype=np.float64), rl, rtol=1e-4, atol=1e-4,
+                                   err_msg=f"{where} lse")

@@ -206,3 +206,42 @@ def test_shared_prefix_entry_points_validate_before_launch():
     assert call(4096, 100) == -3                           # workspace too small
     assert call(1 << 30, 1 << 40) == -2                    # context too long
     assert C.hst_last_hip_error() == 0
+
+
+def test_sizing_and_validation_from_many_threads():
+    """The host-side calls are reentrant: workspace sizing (which reads the
+    device's compute-unit count through its atomic cache on a GPU host) and
+    argument validation give the same answers from several threads at once."""
+    import threading
+    L = _lib()
+    C = L._C
+    shapes = [_shape(L, B=b, Nmax=n) for b in (1, 3, 8) for n in (1000, 40000, 131072)]
+    want = [L.workspace_size(L.HST_OP_DECODE_SOFTLSH, sh, 64, 8, k=100) for sh in shapes]
+    errors = []
+
+    def worker(tid):
+        try:
+            for rep in range(200):
+                i = (tid + rep) % len(shapes)
+                out = ctypes.c_size_t(0)
+                st = C.hst_workspace_size(L.HST_OP_DECODE_SOFTLSH, ctypes.byref(shapes[i]), 64, 8,
+                                          128, 100, ctypes.byref(out))
+                assert st == 0 and out.value == want[i]
+                bad = _shape(L, d=96)
+                st = C.hst_workspace_size(L.HST_OP_DECODE_SOFTLSH, ctypes.byref(bad), 64, 8, 128,
+                                          100, ctypes.byref(out))
+                assert st == -2
+                # validation before launch: a null query is rejected, nothing enqueued
+                st = C.hst_decode_step_softlsh(ctypes.byref(shapes[i]), None, None, None, None, 64,
+                                               8, 0.3, None, None, L.HST_F16, 100, None, 0.1, None,
+                                               None, None, None, 0, None)
+                assert st == -1
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]

@@ -172,7 +172,9 @@ def test_append_then_decode(scheme):
                 kth = np.sort(r["scores"])[::-1][k - 1]
                 for j in diff:
                     assert abs(r["scores"][j] - kth) <= 2e-5 * kth, (b, h, j)
-                continue
-            assert np.abs(out[b, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, (b, h)
-            np.testing.assert_allclose(lse[b, h * G:(h + 1) * G], r["lse"], rtol=1e-4,
-                                       atol=1e-4)
+            # attention over the GPU's own selection, on every slab
+            from tests.gpu_helpers import check_attention
+            check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], qg,
+                            Kf[b, h, :n], Vf[b, h, :n], got, dt, where=(b, h))
+            if not diff:
+                assert np.abs(out[b, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, (b, h)

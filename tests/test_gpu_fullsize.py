@@ -9,7 +9,8 @@ hold at any size:
 * sampled slabs: bucket ids, value norms and binary codes bit-exact; soft
   scores within 1e-5 relative, Hamming scores exact; the selected set equal
   to the oracle's (soft-LSH: keys outside the intersection must sit within
-  the float32 rounding band of the k-th score); attention within 2e-2 absolute
+  the float32 rounding band of the k-th score); attention over the GPU's own
+  selected set within 2e-2 absolute of the oracle's attention over that set,
   and the log-sum-exp within 1e-4;
 * every slab: indices ascending, in [0, N_b), exactly k_b of them, -1 after;
   and the set is exactly the first k_b keys in the order (score descending,
@@ -116,7 +117,7 @@ def test_fullsize_decode_step(name):
         sample = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     print(f"[fullsize] {name}: oracle on slabs {sample}", flush=True)
     G = w.G
-    same_sets = 0
+    from tests.gpu_helpers import check_attention
     for (b, h) in sample:
         n, kb = int(lens[b]), int(ks[b])
         q64 = f64(x["q"][b, h * G:(h + 1) * G])
@@ -140,8 +141,8 @@ def test_fullsize_decode_step(name):
             kth = np.sort(r["scores"])[::-1][kb - 1]
             for j in diff:
                 assert abs(r["scores"][j] - kth) <= 2e-5 * kth, (b, h, j)
-            continue
-        same_sets += 1
-        assert np.abs(out[b, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, (b, h)
-        np.testing.assert_allclose(lse[b, h * G:(h + 1) * G], r["lse"], rtol=1e-4, atol=1e-4)
-    assert same_sets >= len(sample) // 2
+        # attention over the GPU's own selection, on every sampled slab
+        check_attention(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], q64, K64, V64,
+                        got, w.kv_dtype, where=(b, h))
+        if not diff:
+            assert np.abs(out[b, h * G:(h + 1) * G] - r["out"]).max() <= 2e-2, (b, h)

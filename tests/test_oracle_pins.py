@@ -634,3 +634,60 @@ def test_decode_slab_with_all_keys_is_dense_attention():
     assert r["idx"].tolist() == list(range(n))
     dense, _ = O.attend(qg, K, V, np.arange(n), 1 / math.sqrt(d))
     np.testing.assert_allclose(r["out"], dense, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- binary-code decode slab
+
+_AX_KEYS = np.array([[-1, -1, 1, 1], [1, 1, 1, 1], [1, -1, 1, 1], [1, 1, -1, 1],
+                     [-1, -1, -1, -1], [-1, 1, 1, 1]], dtype=np.float64)
+_AX_Q = np.array([[1, 1, 1, 1], [-1, 1, 1, 1]], dtype=np.float64)
+_AX_R = np.array([np.eye(4)[i % 4] for i in range(128)])
+
+
+def test_decode_slab_hamming_hand_derived_selection(golden_dir):
+    rows = _read_golden(golden_dir, "hamming_step_axes.txt")
+    assert len(rows) == 6
+    V = np.arange(24, dtype=np.float64).reshape(6, 4)
+    for kk, sel in rows:
+        r = O.decode_slab_hamming(_AX_Q, _AX_KEYS, V, _AX_R, int(kk))
+        assert r["idx"].tolist() == [int(x) for x in sel.split()]
+    r = O.decode_slab_hamming(_AX_Q, _AX_KEYS, V, _AX_R, 3)
+    assert r["scores"].tolist() == [160, 224, 160, 160, 32, 224]
+    assert r["kcodes"][1].tolist() == [0xFFFFFFFF] * 4
+    assert r["kcodes"][4].tolist() == [0] * 4
+
+
+def test_decode_slab_hamming_hand_derived_attention():
+    # k = 3 keeps keys 0, 1, 5 (golden file above).  With scale 1/sqrt(4) the
+    # logits are q1: (0, 2, 1) and q2: (1, 1, 2); one-hot values make the
+    # output the softmax weights themselves.
+    V = np.zeros((6, 4))
+    V[0, 0] = V[1, 1] = V[5, 3] = 1.0
+    V[2] = V[3] = V[4] = 7.0  # never selected
+    r = O.decode_slab_hamming(_AX_Q, _AX_KEYS, V, _AX_R, 3)
+    e = math.e
+    z1, z2 = 1 + e * e + e, 2 * e + e * e
+    want = np.array([[1 / z1, e * e / z1, 0, e / z1], [e / z2, e / z2, 0, e * e / z2]])
+    np.testing.assert_allclose(r["out"], want, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(r["lse"], [math.log(z1), math.log(z2)], rtol=1e-14)
+    # an explicit scale replaces 1/sqrt(d)
+    r2 = O.decode_slab_hamming(_AX_Q, _AX_KEYS, V, _AX_R, 3, scale=1.0)
+    z1b = 1 + e ** 4 + e ** 2
+    np.testing.assert_allclose(r2["out"][0], [1 / z1b, e ** 4 / z1b, 0, e ** 2 / z1b], rtol=1e-14)
+
+
+def test_decode_slab_hamming_all_keys_is_dense_attention():
+    rng = np.random.default_rng(15)
+    n, d, G = 48, 32, 3
+    K = rng.standard_normal((n, d)); V = rng.standard_normal((n, d))
+    R = rng.standard_normal((64, d)); qg = rng.standard_normal((G, d))
+    r = O.decode_slab_hamming(qg, K, V, R, n)
+    assert r["idx"].tolist() == list(range(n))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qg)[None, :, None, :], torch.from_numpy(K)[None, None].expand(1, G, n, d),
+        torch.from_numpy(V)[None, None].expand(1, G, n, d))[0, :, 0].numpy()
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-13)
+    # and for soft-LSH, the same library reference
+    W = rng.standard_normal((4 * 3, d))
+    rs = O.decode_slab_softlsh(qg, K, V, W, 4, 3, 0.5, n, "f32")
+    np.testing.assert_allclose(rs["out"], ref, rtol=1e-12, atol=1e-13)
