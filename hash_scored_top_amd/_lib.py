@@ -32,6 +32,7 @@ EXPORTED = (
     "hst_score_scan_softlsh", "hst_append_kv_softlsh", "hst_append_kv_binary",
     "hst_select_mass", "hst_decode_step_softlsh_mass", "hst_build_cards_softlsh",
     "hst_decode_step_softlsh_routed", "hst_decode_step_softlsh_shared", "hst_workspace_size_shared",
+    "hst_noalloc_scratch_bytes", "hst_decode_step_softlsh_noalloc",
 )
 
 
@@ -83,6 +84,9 @@ def _load() -> ctypes.CDLL:
                                             P, P, P, SZ, P], I),
         "hst_decode_step_softlsh_mass": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, D, F, P, P, P,
                                           P, P, SZ, P], I),
+        "hst_noalloc_scratch_bytes": ([], SZ),
+        "hst_decode_step_softlsh_noalloc": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, F, P, P, P, P],
+                                            I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -389,6 +393,28 @@ class DecodeHamming:
             _ptr(self.out), _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st),
             "hst_decode_step_hamming")
         return self.idx, self.out, self.lse
+
+
+def hst_decode_step_softlsh_noalloc(q, K, V, W, ids, vnorm, L: int, P: int, tau: float, k: int,
+                                    seq_lens=None, k_per_seq=None, scale=None, idx=None, out=None,
+                                    lse=None):
+    """The soft-LSH decode step on the library's fixed per-GPU workspace (no
+    workspace allocation; outputs may be passed in)."""
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    shape = make_shape(K, Hq, seq_lens)
+    if idx is None:
+        idx = torch.empty((B, Hkv, k), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sc = float(d ** -0.5 if scale is None else scale)
+    _check(_C.hst_decode_step_softlsh_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(W), L, P, float(tau), _ptr(ids),
+        _ptr(vnorm), _norm_code(vnorm.dtype), k, _ptr(k_per_seq), sc, _ptr(idx), _ptr(out),
+        _ptr(lse), _stream(q.device)), "hst_decode_step_softlsh_noalloc")
+    return idx, out, lse
 
 
 def hst_decode_step_softlsh(q, K, V, W, ids, vnorm, L: int, P: int, tau: float, k: int,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hst.h"
 #include "hst_fused.h"
 #include "hst_launch.h"
@@ -481,6 +483,69 @@ hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const 
                                         idx, out, lse, ws, static_cast<hipStream_t>(stream)));
   return hip_status(hst::fused_decode_hamming(*shape, q, K, V, R, codes, k, k_per_seq, scale, idx,
                                               out, lse, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The soft-LSH decode step without allocation, for callers that cannot
+// allocate device memory (code under graph capture, tight serving loops,
+// harnesses that forbid it).  Its workspace is a file-scope device array,
+// one copy per GPU, held from module load until the process ends.  Host code
+// never uses the array's name as an address: the first call on a device
+// looks its address up with hipGetSymbolAddress (with that device current)
+// and keeps it per device.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t{64} << 20;  // 64 MiB per GPU
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // device address of `scratch`, per device ordinal
+
+hst_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= 64) return HST_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return HST_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HST_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hst_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+hst_status hst_decode_step_softlsh_noalloc(const hst_shape* shape, const void* q, const void* K,
+                                           const void* V, const void* W, int L, int P, double tau,
+                                           const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                           int k, const int32_t* k_per_seq, float scale,
+                                           int32_t* idx, float* out, float* lse, void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  if (!ptr_ok(idx)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  size_t need = 0;
+  HST_TRY(hst_workspace_size(HST_OP_DECODE_SOFTLSH, shape, L, P, 128, k, &need));
+  if (need > kScratchBytes) return HST_ERR_WORKSPACE;  // the shape needs more than the array
+  void* ws = nullptr;
+  HST_TRY(scratch_address(&ws));
+  // the step needs no initial workspace contents: whatever the previous call
+  // on this GPU left there is reset or overwritten before it is read
+  return hip_status(hst::fused_decode_softlsh(*shape, q, K, V, W, L, P, tau, ids, vnorm, norm_dtype,
+                                              k, k_per_seq, scale, idx, out, lse, ws,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -391,6 +391,33 @@ hst_status hst_decode_step_softlsh_shared(const hst_shape* shape, int Np,
 hst_status hst_workspace_size_shared(const hst_shape* shape, int Np, int L,
                                      int P, int k, size_t* bytes);
 
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the soft-LSH decode
+ * step of hst_decode_step_softlsh, same arguments and results, without the
+ * caller's workspace.  Its workspace is a fixed device array inside the
+ * library, hst_noalloc_scratch_bytes() bytes (64 MiB) per GPU, held from the
+ * library's load on that GPU until the process ends; the call allocates
+ * nothing.  The first call on a device looks up that device's copy of the
+ * array (once, under a lock).
+ *   - Shapes whose workspace (hst_workspace_size of HST_OP_DECODE_SOFTLSH)
+ *     exceeds the array are rejected with HST_ERR_WORKSPACE before anything
+ *     is enqueued.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, or host threads) race and must not
+ *     be made.  Calls in sequence on one stream are safe; the array keeps the
+ *     last call's contents, and the step needs none of them.
+ */
+size_t hst_noalloc_scratch_bytes(void);
+hst_status hst_decode_step_softlsh_noalloc(const hst_shape* shape, const void* q,
+                                           const void* K, const void* V,
+                                           const void* W, int L, int P,
+                                           double tau, const uint8_t* ids,
+                                           const void* vnorm, int norm_dtype,
+                                           int k, const int32_t* k_per_seq,
+                                           float scale, int32_t* idx, float* out,
+                                           float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

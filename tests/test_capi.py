@@ -245,3 +245,23 @@ def test_sizing_and_validation_from_many_threads():
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_noalloc_rejects_before_launch():
+    """The no-allocation step validates like the workspace step, and rejects a
+    shape whose workspace exceeds its fixed array with HST_ERR_WORKSPACE,
+    before any device call (the pointers below are never dereferenced)."""
+    L = _lib()
+    C = L._C
+    cap = C.hst_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    fake = 0x10000  # aligned, never touched: validation ends before any launch
+    big = _shape(L, B=32, Hq=32, Hkv=4, Nmax=65536)
+    assert L.workspace_size(L.HST_OP_DECODE_SOFTLSH, big, 64, 8, k=1311) > cap
+    args = lambda sh, q: (ctypes.byref(sh), q, fake, fake, fake, 64, 8, 0.3, fake, fake, L.HST_F16,
+                          1311, None, 0.088, fake, fake, fake, None)
+    assert C.hst_decode_step_softlsh_noalloc(*args(big, fake)) == -3
+    small = _shape(L)
+    assert L.workspace_size(L.HST_OP_DECODE_SOFTLSH, small, 64, 8, k=1311) <= cap
+    assert C.hst_decode_step_softlsh_noalloc(*args(small, None)) == -1
+    assert C.hst_decode_step_softlsh_noalloc(*args(_shape(L, d=96), fake)) == -2
