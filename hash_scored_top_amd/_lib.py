@@ -33,6 +33,9 @@ EXPORTED = (
     "hst_select_mass", "hst_decode_step_softlsh_mass", "hst_build_cards_softlsh",
     "hst_decode_step_softlsh_routed", "hst_decode_step_softlsh_shared", "hst_workspace_size_shared",
     "hst_noalloc_scratch_bytes", "hst_decode_step_softlsh_noalloc",
+    "hst_decode_prepare_softlsh", "hst_decode_filter_softlsh", "hst_decode_finish_softlsh",
+    "hst_decode_prepare_hamming", "hst_decode_filter_hamming", "hst_decode_finish_hamming",
+    "hst_decode_candidates",
 )
 
 
@@ -85,6 +88,13 @@ def _load() -> ctypes.CDLL:
         "hst_decode_step_softlsh_mass": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, D, F, P, P, P,
                                           P, P, SZ, P], I),
         "hst_noalloc_scratch_bytes": ([], SZ),
+        "hst_decode_prepare_softlsh": ([SH, P, P, I, I, D, P, P, I, I, P, P, SZ, P], I),
+        "hst_decode_filter_softlsh": ([SH, I, I, P, P, I, I, P, P, SZ, P], I),
+        "hst_decode_finish_softlsh": ([SH, P, P, P, I, I, P, P, I, I, F, P, P, P, P, SZ, P], I),
+        "hst_decode_prepare_hamming": ([SH, P, P, P, I, P, P, SZ, P], I),
+        "hst_decode_filter_hamming": ([SH, P, I, P, P, SZ, P], I),
+        "hst_decode_finish_hamming": ([SH, P, P, P, P, I, F, P, P, P, P, SZ, P], I),
+        "hst_decode_candidates": ([SH, I, I, I, I, P, SZ, I, P, P, P, P, P], I),
         "hst_decode_step_softlsh_noalloc": ([SH, P, P, P, P, I, I, D, P, P, I, I, P, F, P, P, P, P],
                                             I),
     }
@@ -366,6 +376,47 @@ class DecodeSoftLSH:
             self.ws.numel(), st), "hst_decode_step_softlsh")
         return self.idx, self.out, self.lse
 
+    # the step's three stages (the call above runs them in order)
+    def prepare(self, q, W, ids, vnorm, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_prepare_softlsh(
+            ctypes.byref(self.shape), _ptr(q), _ptr(W), self.L, self.P, self.tau, _ptr(ids),
+            _ptr(vnorm), self.norm_code, self.k, _ptr(self.k_per_seq), _ptr(self.ws),
+            self.ws.numel(), st), "hst_decode_prepare_softlsh")
+
+    def filter(self, ids, vnorm, stream: Optional[int] = None):
+        st = _stream(ids.device) if stream is None else stream
+        _check(_C.hst_decode_filter_softlsh(
+            ctypes.byref(self.shape), self.L, self.P, _ptr(ids), _ptr(vnorm), self.norm_code,
+            self.k, _ptr(self.k_per_seq), _ptr(self.ws), self.ws.numel(), st),
+            "hst_decode_filter_softlsh")
+
+    def finish(self, q, K, V, ids, vnorm, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_finish_softlsh(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), self.L, self.P, _ptr(ids),
+            _ptr(vnorm), self.norm_code, self.k, self.scale, _ptr(self.idx), _ptr(self.out),
+            _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st), "hst_decode_finish_softlsh")
+        return self.idx, self.out, self.lse
+
+    def candidates(self, cap: int):
+        return _candidates(self.shape, HST_OP_DECODE_SOFTLSH, self.L, self.P, self.k, self.ws, cap)
+
+
+def _candidates(shape, op, L, P, k, ws, cap):
+    """The filter stage's candidates per (sequence, kv head): order keys
+    [B,Hkv,cap] (int32 bit patterns of the uint32 keys), indices [B,Hkv,cap],
+    counts [B,Hkv] and thresholds [B,Hkv] (order keys as int32 bits)."""
+    B, Hkv, dev = shape.B, shape.Hkv, ws.device
+    keys = torch.zeros((B, Hkv, cap), dtype=torch.int32, device=dev)
+    index = torch.full((B, Hkv, cap), -1, dtype=torch.int32, device=dev)
+    count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    theta = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+    _check(_C.hst_decode_candidates(ctypes.byref(shape), op, L, P, k, _ptr(ws), ws.numel(), cap,
+                                    _ptr(keys), _ptr(index), _ptr(count), _ptr(theta),
+                                    _stream(dev)), "hst_decode_candidates")
+    return keys, index, count, theta
+
 
 class DecodeHamming:
     """Pre-sized binary-code decode step."""
@@ -393,6 +444,30 @@ class DecodeHamming:
             _ptr(self.out), _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st),
             "hst_decode_step_hamming")
         return self.idx, self.out, self.lse
+
+    # the step's three stages (128-bit codes; the call above runs them in order)
+    def prepare(self, q, R, codes, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_prepare_hamming(
+            ctypes.byref(self.shape), _ptr(q), _ptr(R), _ptr(codes), self.k, _ptr(self.k_per_seq),
+            _ptr(self.ws), self.ws.numel(), st), "hst_decode_prepare_hamming")
+
+    def filter(self, codes, stream: Optional[int] = None):
+        st = _stream(codes.device) if stream is None else stream
+        _check(_C.hst_decode_filter_hamming(
+            ctypes.byref(self.shape), _ptr(codes), self.k, _ptr(self.k_per_seq), _ptr(self.ws),
+            self.ws.numel(), st), "hst_decode_filter_hamming")
+
+    def finish(self, q, K, V, codes, stream: Optional[int] = None):
+        st = _stream(q.device) if stream is None else stream
+        _check(_C.hst_decode_finish_hamming(
+            ctypes.byref(self.shape), _ptr(q), _ptr(K), _ptr(V), _ptr(codes), self.k, self.scale,
+            _ptr(self.idx), _ptr(self.out), _ptr(self.lse), _ptr(self.ws), self.ws.numel(), st),
+            "hst_decode_finish_hamming")
+        return self.idx, self.out, self.lse
+
+    def candidates(self, cap: int):
+        return _candidates(self.shape, HST_OP_DECODE_HAMMING, 0, 0, self.k, self.ws, cap)
 
 
 def hst_decode_step_softlsh_noalloc(q, K, V, W, ids, vnorm, L: int, P: int, tau: float, k: int,

@@ -120,7 +120,8 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
                      reinterpret_cast<uint32_t*>(sm + 65536), offs};
     int M = 0;
-    const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
+    const void* srow =
+        scores != nullptr ? static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4 : nullptr;
     const int path = select_range<NT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, r0, r1, irow,
                                       rows, sc, &M);
     nrows = max(0, min(k_eff, r1) - r0);
@@ -417,13 +418,59 @@ select_kernel(int32_t* __restrict__ idx, const void* __restrict__ scores, int sc
   SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
                    reinterpret_cast<uint32_t*>(sm + 65536), reinterpret_cast<int*>(sm + 65536 + 8192)};
   int M = 0;
-  const void* srow = static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4;
+  const void* srow =
+      scores != nullptr ? static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4 : nullptr;
   const int path = select_range<kSelNT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, 0, a.kcap,
                                         idx + static_cast<long long>(bh) * a.kcap, nullptr, sc, &M);
   if (threadIdx.x == 0) {
     a.heads[bh].path = static_cast<uint32_t>(path);
     a.heads[bh].cand_total = static_cast<uint32_t>(M);
   }
+}
+
+// The candidates the filtering scan left for each head, in index order: the
+// (order key, index) pairs of its chunk slots, up to cap of them, their count
+// and the head's threshold.  One workgroup per (sequence, kv head).
+__global__ void __launch_bounds__(256)
+candidates_kernel(FusedArgs a, int chunk, const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ keys,
+                  int32_t* __restrict__ index, int32_t* __restrict__ count, uint32_t* __restrict__ theta,
+                  int cap) {
+  __shared__ int offs[kMaxChunks + 1];
+  const int bh = blockIdx.x, b = bh / a.Hkv;
+  const int n = seq_len(seq_lens, b, a.Nmax);
+  const int nch = (n + a.span - 1) / a.span;
+  const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
+  const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int c = 0; c < nch; ++c) {
+      offs[c] = run;
+      run += static_cast<int>(cnt[c]);
+    }
+    offs[nch] = run;
+    count[bh] = run;
+    theta[bh] = a.heads[bh].theta;
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int m = offs[c + 1] - offs[c];
+    for (int i = threadIdx.x; i < m; i += blockDim.x) {
+      const int p = offs[c] + i;
+      if (p < cap) {
+        const uint2 v = slots[static_cast<long long>(c) * chunk + i];
+        keys[static_cast<long long>(bh) * cap + p] = v.x;
+        index[static_cast<long long>(bh) * cap + p] = static_cast<int32_t>(v.y);
+      }
+    }
+  }
+}
+
+hipError_t launch_candidates(const hst_shape& s, const FusedArgs& a, int chunk, uint32_t* keys, int32_t* index,
+                             int32_t* count, uint32_t* theta, int cap, hipStream_t st) {
+  if (a.nchunks > kMaxChunks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(candidates_kernel, dim3(s.B * s.Hkv), dim3(256), 0, st, a, chunk, s.seq_lens, keys, index,
+                     count, theta, cap);
+  return hipGetLastError();
 }
 
 // Raises a kernel's dynamic LDS limit (kept per kernel and device).

@@ -488,6 +488,105 @@ hst_status hst_decode_step_hamming(const hst_shape* shape, const void* q, const 
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// The decode step in three stages over one workspace.
+
+extern "C" {
+
+hst_status hst_decode_prepare_softlsh(const hst_shape* shape, const void* q, const void* W, int L,
+                                      int P, double tau, const uint8_t* ids, const void* vnorm,
+                                      int norm_dtype, int k, const int32_t* k_per_seq, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  HST_TRY(score_softlsh_checks(shape, q, W, L, P, tau, ids, vnorm, norm_dtype));
+  if (k < 1) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::decode_prepare_softlsh(*shape, q, W, L, P, tau, ids, vnorm, norm_dtype, k,
+                                                k_per_seq, ws, static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_filter_softlsh(const hst_shape* shape, int L, int P, const uint8_t* ids,
+                                     const void* vnorm, int norm_dtype, int k,
+                                     const int32_t* k_per_seq, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  HST_TRY(check_shape(shape));
+  HST_TRY(check_lp(L, P));
+  HST_TRY(check_norm_dtype(norm_dtype));
+  HST_TRY(check_soft_prep(shape, L, P));
+  if (k < 1) return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(ids) || !ptr_ok(vnorm)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::decode_filter_softlsh(*shape, L, P, ids, vnorm, norm_dtype, k, k_per_seq,
+                                               ws, static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_finish_softlsh(const hst_shape* shape, const void* q, const void* K,
+                                     const void* V, int L, int P, const uint8_t* ids,
+                                     const void* vnorm, int norm_dtype, int k, float scale,
+                                     int32_t* idx, float* out, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  HST_TRY(check_lp(L, P));
+  HST_TRY(check_norm_dtype(norm_dtype));
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  HST_TRY(check_soft_prep(shape, L, P));
+  if (!ptr_ok(idx) || !ptr_ok(ids) || !ptr_ok(vnorm)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_SOFTLSH, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::decode_finish_softlsh(*shape, q, K, V, L, P, ids, vnorm, norm_dtype, k,
+                                               scale, idx, out, lse, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_prepare_hamming(const hst_shape* shape, const void* q, const void* R,
+                                      const uint32_t* codes, int k, const int32_t* k_per_seq,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  HST_TRY(score_hamming_checks(shape, q, R, 128, codes));
+  if (k < 1) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::decode_prepare_hamming(*shape, q, R, codes, k, k_per_seq, ws,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_filter_hamming(const hst_shape* shape, const uint32_t* codes, int k,
+                                     const int32_t* k_per_seq, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  HST_TRY(check_shape(shape));
+  if (group(shape) > 64) return HST_ERR_UNSUPPORTED;
+  if (k < 1) return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(codes)) return HST_ERR_INVALID_ARG;
+  if (k_per_seq != nullptr && !aligned16(k_per_seq)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::decode_filter_hamming(*shape, codes, k, k_per_seq, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_finish_hamming(const hst_shape* shape, const void* q, const void* K,
+                                     const void* V, const uint32_t* codes, int k, float scale,
+                                     int32_t* idx, float* out, float* lse, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  HST_TRY(attention_checks(shape, q, K, V, k, scale, out, lse));
+  if (!ptr_ok(idx) || !ptr_ok(codes)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(HST_OP_DECODE_HAMMING, shape, 0, 0, k, ws, ws_bytes));
+  return hip_status(hst::decode_finish_hamming(*shape, q, K, V, codes, k, scale, idx, out, lse, ws,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+hst_status hst_decode_candidates(const hst_shape* shape, int op, int L, int P, int k,
+                                 void* ws, size_t ws_bytes, int cap, uint32_t* keys,
+                                 int32_t* index, int32_t* count, uint32_t* theta, void* stream) {
+  HST_TRY(check_shape(shape));
+  if (op != HST_OP_DECODE_SOFTLSH && op != HST_OP_DECODE_HAMMING) return HST_ERR_INVALID_ARG;
+  if (op == HST_OP_DECODE_SOFTLSH) HST_TRY(check_lp(L, P));
+  if (k < 1 || cap < 1) return HST_ERR_INVALID_ARG;
+  if (!ptr_ok(keys) || !ptr_ok(index) || !ptr_ok(count) || !ptr_ok(theta)) return HST_ERR_INVALID_ARG;
+  HST_TRY(workspace_check(op, shape, L, P, k, ws, ws_bytes));
+  return hip_status(hst::decode_candidates(*shape, op, L, P, k, ws, keys, index, count, theta, cap,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // The soft-LSH decode step without allocation, for callers that cannot
 // allocate device memory (code under graph capture, tight serving loops,
 // harnesses that forbid it).  Its workspace is a file-scope device array,

@@ -234,23 +234,184 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
   }
 }
 
+// The head's histogram of candidate keys, built by the filtering scan: key c
+// (always >= theta) is counted in bin min(kHistBins - 1, (c - theta) >> shift).
+struct HistInfo {
+  uint32_t theta;
+  int shift;
+  bool ok;  // every chunk counted its candidates under the published threshold
+};
+
+// Bin of the k-th largest candidate from the histogram, counted from the top
+// bin down.  hb: this thread's bins, kHistBins / NT of them, in descending
+// bin order starting at bin kHistBins - 1 - threadIdx.x * (kHistBins / NT).
+// Returns false when the bins do not add up to M (the histogram is not
+// usable); otherwise bstar is the bin holding rank k, krem how many of its
+// entries complete the k largest, cnt its size.  All threads call.
+template <int NT>
+__device__ bool hist_boundary(const uint32_t (&hb)[kHistBins / NT], int M, int k, BlockScratch<NT>& sc,
+                              int& bstar, int& krem, int& cnt) {
+  constexpr int BPT = kHistBins / NT;
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) mine += static_cast<int>(hb[i]);
+  const int incl = wave_incl_scan(mine);
+  if (lane == 63) sc.wsum[wave] = incl;
+  __syncthreads();
+  int above = incl - mine, total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    total += sc.wsum[w];
+    if (w < wave) above += sc.wsum[w];
+  }
+  if (total != M) {  // uniform: every thread read the same sums
+    __syncthreads();
+    return false;
+  }
+  if (above < k && k <= above + mine) {
+    int cum = above;
+    bool hit = false;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int c = static_cast<int>(hb[i]);
+      if (!hit && cum + c >= k) {
+        sc.found[0] = kHistBins - 1 - (t * BPT + i);
+        sc.found[1] = k - cum;
+        sc.found[2] = c;
+        hit = true;
+      }
+      if (!hit) cum += c;
+    }
+  }
+  __syncthreads();
+  bstar = sc.found[0];
+  krem = sc.found[1];
+  cnt = sc.found[2];
+  __syncthreads();  // sc.found is rewritten by the caller
+  return true;
+}
+
+// Ranks the entries of the wave-held keys that satisfy `in` (at most
+// kRankBin of them; cnt in total) by (key descending, position ascending) and
+// returns the key of the krem-th and how many entries equal to it are taken
+// (rank krem - 1 among the bin's entries).  bl: LDS, >= kRankBin uint2.
+constexpr int kRankBin = 256;
+template <int NT, int PERW, class In>
+__device__ void rank_entries(const uint32_t (&key)[PERW], int lo, int hi, const In& in, int cnt, int krem,
+                             uint2* bl, BlockScratch<NT>& sc, uint32_t& kstar, int& eq_taken) {
+  const int t = threadIdx.x, lane = t & 63;
+  if (t == 0) sc.found[3] = 0;
+  __syncthreads();
+  {
+    // this wave's entries, then one slot reservation per wave
+    int nw = 0;
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) nw += __popcll(__ballot(lo + 64 * u + lane < hi && in(key[u])));
+    int base = 0;
+    if (lane == 0 && nw > 0) base = atomicAdd(&sc.found[3], nw);
+    base = __shfl(base, 0, 64);
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) {
+      const int p = lo + 64 * u + lane;
+      const bool ok = p < hi && in(key[u]);
+      const unsigned long long b = __ballot(ok);
+      const int slot = base + lanes_below(b);
+      if (ok && slot < kRankBin) bl[slot] = make_uint2(key[u], static_cast<uint32_t>(p));
+      base += __popcll(b);
+    }
+  }
+  __syncthreads();
+  const int nb = cnt < kRankBin ? cnt : kRankBin;
+  if (t < nb) {
+    const uint2 me = bl[t];
+    int gt = 0, eq = 0;
+    for (int j = 0; j < nb; ++j) {
+      const uint2 o = bl[j];
+      gt += o.x > me.x ? 1 : 0;
+      eq += (o.x == me.x && o.y < me.y) ? 1 : 0;
+    }
+    if (gt + eq == krem - 1) {
+      sc.found[0] = static_cast<int>(me.x);
+      sc.found[1] = eq + 1;
+    }
+  }
+  __syncthreads();
+  kstar = static_cast<uint32_t>(sc.found[0]);
+  eq_taken = sc.found[1];
+  __syncthreads();
+}
+
+// Counts and stable compaction under the masked-prefix rule (selected iff
+// (key & mask) > prefix, or == prefix among the first krem such entries in
+// position order), from ballots over the wave-held keys: writes the
+// selected indices at output positions [r0, r1).
+template <int NT, int PERW, class Idx>
+__device__ void compact_regs(const uint32_t (&key)[PERW], int lo, int hi, const Idx& candi, uint32_t mask,
+                             uint32_t prefix, int krem, int r0, int r1, int32_t* out_g, int32_t* out_l,
+                             BlockScratch<NT>& sc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int gtc = 0, eqc = 0;
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const bool ok = lo + 64 * u + lane < hi;
+    const uint32_t m = key[u] & mask;
+    gtc += __popcll(__ballot(ok && m > prefix));
+    eqc += __popcll(__ballot(ok && m == prefix));
+  }
+  if (lane == 0) {
+    sc.red[0][wave] = static_cast<uint32_t>(gtc);
+    sc.red[1][wave] = static_cast<uint32_t>(eqc);
+  }
+  __syncthreads();
+  int gt_before = 0, eq_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += static_cast<int>(sc.red[0][w]);
+    eq_run += static_cast<int>(sc.red[1][w]);
+  }
+  __syncthreads();  // sc is reused by the caller
+  int run = gt_before + min(eq_run, krem);
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) {
+    const int p = lo + 64 * u + lane;
+    const bool ok = p < hi;
+    const uint32_t m = key[u] & mask;
+    const bool top = ok && m > prefix;
+    const bool eq = ok && m == prefix;
+    const unsigned long long eqb = __ballot(eq);
+    const bool sel = top || (eq && eq_run + lanes_below(eqb) < krem);
+    const unsigned long long selb = __ballot(sel);
+    const int pos = run + lanes_below(selb);
+    if (sel && pos >= r0 && pos < r1) {
+      const int32_t v = static_cast<int32_t>(candi[p]);
+      if (out_g != nullptr) out_g[pos] = v;
+      if (out_l != nullptr) out_l[pos - r0] = v;
+    }
+    run += __popcll(selb);
+    eq_run += __popcll(eqb);
+  }
+}
+
 // Exact selection over M <= NT * PERW candidates held in LDS in index order,
 // on keys held in registers: wave w holds the entries at positions
 // [lo_w, hi_w) (lane l's entry u at lo_w + 64u + l), the order in which the
 // compaction walks them, so the counts and the compaction come from ballots
-// over registers instead of a second pass over LDS.  Radix passes of up to
-// 11 bits below the keys' common prefix narrow the bin of the k-th largest
-// key; once that bin holds at most kRankBin entries they are ranked directly
-// by (key descending, position ascending), which resolves the k-th key and
-// how many keys equal to it are taken, without further passes.  The result
-// is the masked-prefix rule of radix_select_regs.  Writes the selected
-// indices at output positions [r0, r1).  hist: 2048 words of LDS.
-// candi: the entries' key indices, anything indexable by position (an LDS
-// array, or a map from positions to indices).
-constexpr int kRankBin = 64;
-template <int NT, int PERW, class Idx>
-__device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
-                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+// over registers instead of a second pass over LDS.
+//  * With the head's candidate histogram (HIST): one block scan over the bins
+//    finds the bin of the k-th largest key.  If that bin is taken whole, or
+//    holds a single key value (shift 0), the rule follows at once; otherwise
+//    its entries (at most kRankBin) are ranked directly.
+//  * Otherwise, or when the bin is too full: radix passes of up to 11 bits
+//    below the keys' common prefix narrow the bin of the k-th largest key
+//    until it holds at most kRankBin entries, which are then ranked.
+// Writes the selected indices at output positions [r0, r1).  hist: 2048
+// words of LDS.  candi: the entries' key indices, anything indexable by
+// position (an LDS array, or a map from positions to indices).
+template <int NT, int PERW, class Idx, bool HIST>
+__device__ void select_lds_core(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
+                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc,
+                                const uint32_t (&hb)[kHistBins / NT], const HistInfo& hi_info) {
   constexpr int NW = NT / 64;
   constexpr int MAXPER = (2048 + NT - 1) / NT;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -266,7 +427,42 @@ __device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, 
   // the first krem such entries in index order
   uint32_t mask = 0u, prefix = 0u;
   int krem = k < M ? k : M;
-  if (k < M) {
+  bool done = k >= M;
+  if (HIST && !done && hi_info.ok) {
+    int bstar, kb, cnt;
+    if (hist_boundary<NT>(hb, M, k, sc, bstar, kb, cnt)) {
+      const uint32_t th = hi_info.theta;
+      const int sh = hi_info.shift;
+      const unsigned long long klo = static_cast<unsigned long long>(th) +
+                                     (static_cast<unsigned long long>(bstar) << sh);
+      if (kb == cnt && klo >= 1ull && klo <= 0xffffffffull) {
+        // the whole bin is taken: every key >= its lower edge
+        mask = 0xffffffffu;
+        prefix = static_cast<uint32_t>(klo - 1ull);
+        krem = 0;
+        done = true;
+      } else if (sh == 0 && bstar < kHistBins - 1) {
+        // the bin is one key value: its first kb entries in index order
+        mask = 0xffffffffu;
+        prefix = static_cast<uint32_t>(klo);
+        krem = kb;
+        done = true;
+      } else if (cnt <= kRankBin) {
+        const auto in_bin = [th, sh, bstar](uint32_t c) {
+          const uint32_t b = (c - th) >> sh;
+          return static_cast<int>(b < static_cast<uint32_t>(kHistBins - 1) ? b : kHistBins - 1) == bstar;
+        };
+        uint32_t kstar;
+        int eqt;
+        rank_entries<NT, PERW>(key, lo, hi, in_bin, cnt, kb, reinterpret_cast<uint2*>(hist), sc, kstar, eqt);
+        mask = 0xffffffffu;
+        prefix = kstar;
+        krem = eqt;
+        done = true;
+      }
+    }
+  }
+  if (!done) {
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int u = 0; u < PERW; ++u)
@@ -276,17 +472,16 @@ __device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, 
       }
     block_minmax<NT>(mn, mx, sc);
     if (mn != mx) {
-      const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
-      mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
+      const int hb_ = 31 - __clz(static_cast<int>(mn ^ mx));
+      mask = hb_ == 31 ? 0u : ~((1u << (hb_ + 1)) - 1u);
       prefix = mn & mask;
-      int lob = hb + 1;
+      int lob = hb_ + 1;
       while (lob > 0) {
         const int width = lob < 11 ? lob : 11;
         const int sh = lob - width;
         const int nb = 1 << width;
         const uint32_t dm = static_cast<uint32_t>(nb - 1);
         for (int i = t; i < nb; i += NT) hist[i] = 0u;
-        if (t == 0) sc.found[3] = 0;
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < PERW; ++u)
@@ -330,96 +525,34 @@ __device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, 
         prefix |= static_cast<uint32_t>(digit) << sh;
         mask |= dm << sh;
         lob = sh;
+        __syncthreads();  // every thread has read sc.found and its bins
         if (cnt == krem || lob == 0) break;  // the whole bin is taken, or every bit is resolved
         if (cnt <= kRankBin) {
-          // the bin's entries (key, position), in any order, over the histogram
-          uint2* bl = reinterpret_cast<uint2*>(hist);
-          __syncthreads();  // every thread has read its bins
-          {
-            // this wave's entries of the bin, then one slot reservation per wave
-            int nw = 0;
-#pragma unroll
-            for (int u = 0; u < PERW; ++u) nw += __popcll(__ballot(lo + 64 * u + lane < hi && (key[u] & mask) == prefix));
-            int base = 0;
-            if (lane == 0 && nw > 0) base = atomicAdd(&sc.found[3], nw);
-            base = __shfl(base, 0, 64);
-#pragma unroll
-            for (int u = 0; u < PERW; ++u) {
-              const int p = lo + 64 * u + lane;
-              const bool in = p < hi && (key[u] & mask) == prefix;
-              const unsigned long long b = __ballot(in);
-              if (in) bl[base + lanes_below(b)] = make_uint2(key[u], static_cast<uint32_t>(p));
-              base += __popcll(b);
-            }
-          }
-          __syncthreads();
-          if (t < cnt) {
-            // rank of this entry by (key descending, position ascending): the
-            // bin's entries with a larger key, then its equal keys earlier
-            const uint2 me = bl[t];
-            int gt = 0, eq = 0;
-            for (int j = 0; j < cnt; ++j) {
-              const uint2 o = bl[j];
-              gt += o.x > me.x ? 1 : 0;
-              eq += (o.x == me.x && o.y < me.y) ? 1 : 0;
-            }
-            if (gt + eq == krem - 1) {  // the k-th entry: its key, and how many
-              sc.found[0] = static_cast<int>(me.x);  // entries equal to it are taken
-              sc.found[1] = eq + 1;
-            }
-          }
-          __syncthreads();
+          const uint32_t pm = mask, pp = prefix;
+          uint32_t kstar;
+          int eqt;
+          rank_entries<NT, PERW>(key, lo, hi, [pm, pp](uint32_t c) { return (c & pm) == pp; }, cnt, krem,
+                                 reinterpret_cast<uint2*>(hist), sc, kstar, eqt);
           // the k-th key is now fully resolved: take the keys above it and the
-          // first krem keys equal to it (index order)
-          prefix = static_cast<uint32_t>(sc.found[0]);
+          // first eqt keys equal to it (index order)
+          prefix = kstar;
           mask = 0xffffffffu;
-          krem = sc.found[1];
+          krem = eqt;
           break;
         }
       }
     }
   }
   __syncthreads();  // sc.found is read above; sc.red is written below
-  // counts per wave (strictly above, tied at the prefix), then the waves before
-  int gtc = 0, eqc = 0;
-#pragma unroll
-  for (int u = 0; u < PERW; ++u) {
-    const bool ok = lo + 64 * u + lane < hi;
-    const uint32_t m = key[u] & mask;
-    gtc += __popcll(__ballot(ok && m > prefix));
-    eqc += __popcll(__ballot(ok && m == prefix));
-  }
-  if (lane == 0) {
-    sc.red[0][wave] = static_cast<uint32_t>(gtc);
-    sc.red[1][wave] = static_cast<uint32_t>(eqc);
-  }
-  __syncthreads();
-  int gt_before = 0, eq_run = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += static_cast<int>(sc.red[0][w]);
-    eq_run += static_cast<int>(sc.red[1][w]);
-  }
-  __syncthreads();  // sc is reused by the caller
-  int run = gt_before + min(eq_run, krem);
-#pragma unroll
-  for (int u = 0; u < PERW; ++u) {
-    const int p = lo + 64 * u + lane;
-    const bool ok = p < hi;
-    const uint32_t m = key[u] & mask;
-    const bool top = ok && m > prefix;
-    const bool eq = ok && m == prefix;
-    const unsigned long long eqb = __ballot(eq);
-    const bool sel = top || (eq && eq_run + lanes_below(eqb) < krem);
-    const unsigned long long selb = __ballot(sel);
-    const int pos = run + lanes_below(selb);
-    if (sel && pos >= r0 && pos < r1) {
-      const int32_t v = static_cast<int32_t>(candi[p]);
-      if (out_g != nullptr) out_g[pos] = v;
-      if (out_l != nullptr) out_l[pos - r0] = v;
-    }
-    run += __popcll(selb);
-    eq_run += __popcll(eqb);
-  }
+  compact_regs<NT, PERW>(key, lo, hi, candi, mask, prefix, krem, r0, r1, out_g, out_l, sc);
+}
+
+template <int NT, int PERW, class Idx>
+__device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
+                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+  const uint32_t hb[kHistBins / NT] = {};
+  select_lds_core<NT, PERW, Idx, false>(candk, candi, M, k, r0, r1, out_g, out_l, hist, sc, hb,
+                                        HistInfo{0u, 0, false});
 }
 
 // Lower bound of the r-th largest (1 <= r <= count) of the keys held PER per
@@ -441,12 +574,58 @@ struct SelectScratch {
   int* offs;        // LDS, nchunks + 1
 };
 
+// Keys rescored from the metadata, for the rare selection over every key
+// (fewer than k keys passed the threshold): the soft-collision score of key
+// i from the query tables in the workspace, or its code similarity.  These
+// scores may differ from the scan's in the last bit (the lookups are summed
+// in table order); the selection is exact for them.
+struct SoftRescoreSrc {
+  const uint8_t* ids;  // the head's rows [n][L]
+  const void* vn;      // the head's value norms
+  const float* tbl;    // the head's table, bucket-major [2^P][L]
+  int L;
+  uint32_t idmask;
+  bool f16;
+  __device__ __forceinline__ uint32_t key(int i) const {
+    const uint8_t* r = ids + static_cast<long long>(i) * L;
+    float acc = 0.f;
+    for (int l = 0; l < L; ++l) acc += tbl[(r[l] & idmask) * L + l];
+    const float v = f16 ? f16_bits_to_f32(static_cast<const uint16_t*>(vn)[i]) : static_cast<const float*>(vn)[i];
+    return order_key_f32(acc * v);
+  }
+  __device__ __forceinline__ int32_t idx(int i) const { return i; }
+};
+struct HamRescoreSrc {
+  const uint32_t* codes;  // the head's codes [n][4]
+  const uint32_t* qc;     // the head's G query codes [G][4]
+  int G;
+  __device__ __forceinline__ uint32_t key(int i) const {
+    const uint32_t* c = codes + static_cast<long long>(i) * 4;
+    int ham = 0;
+    for (int g = 0; g < G; ++g)
+      ham += __popc(c[0] ^ qc[4 * g]) + __popc(c[1] ^ qc[4 * g + 1]) + __popc(c[2] ^ qc[4 * g + 2]) +
+             __popc(c[3] ^ qc[4 * g + 3]);
+    return order_key_i32(128 * G - ham);
+  }
+  __device__ __forceinline__ int32_t idx(int i) const { return i; }
+};
+
+template <int NT, class Src>
+__device__ void select_all_keys(const Src& src, int n, int k_eff, int r0, int r1, int32_t* out_g,
+                                int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
+  const SelRule rule = block_select_rule<NT>(src, n, k_eff, hist, sc);
+  block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
+}
+
 // The head's exact top-k (k_eff keys, ties to the lower index) from the
-// candidate slots the scan wrote (or, when fewer than k_eff keys passed the
-// threshold, from the whole score row).  Writes the selected indices at
-// output positions [r0, r1) (see block_compact_range) and -1 at positions
-// in [max(r0, k_eff), r1) of out_g.  Returns the selection path taken
-// (0: candidates in LDS, 1: candidates read from HBM, 2: whole score row).
+// candidate slots the scan wrote.  Writes the selected indices at output
+// positions [r0, r1) and -1 at positions in [max(r0, k_eff), r1) of out_g.
+// Returns the selection path taken:
+//   0: candidates in LDS (the head's candidate histogram gives the bin of the
+//      k-th key; radix passes only when it cannot);
+//   1: more candidates than LDS holds: selected from the slots in HBM;
+//   2: fewer than k_eff keys passed the threshold: every key, from the given
+//      score row (scores_row) or rescored from the metadata (a.meta).
 template <int NT>
 __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int chunk,
                             const void* scores_row, bool scores_int, const SelectScratch& ws,
@@ -456,14 +635,23 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
   const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
   const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
   constexpr int NW = NT / 64;
+  constexpr int BPT = kHistBins / NT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the first counts, then the first 128 slots of the first eight chunks of
-  // each wave (copied below), all in flight together: the slot addresses do
-  // not depend on the counts (slots past a chunk's count are read, unused),
-  // and the counts, issued first, arrive without waiting for the slots
+  // the first counts, then the histogram bins and the head's threshold, then
+  // the first 128 slots of the first eight chunks of each wave (copied
+  // below), all in flight together: the slot addresses do not depend on the
+  // counts (slots past a chunk's count are read, unused), and the counts,
+  // issued first, arrive without waiting for the rest
   const int cnt0 = static_cast<int>(threadIdx.x) < nch ? static_cast<int>(cnt[threadIdx.x]) : 0;
-  // (chunk indices clamped, so the loads are unconditional and the wait for
-  // the counts counts exactly the slot loads behind them)
+  uint32_t hb[BPT];
+  const bool have_hist = a.hist != nullptr;
+  const uint32_t* hrow = have_hist ? a.hist + static_cast<long long>(bh) * kHistBins : nullptr;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i)
+    hb[i] = have_hist ? hrow[kHistBins - 1 - (static_cast<int>(threadIdx.x) * BPT + i)] : 0u;
+  const HeadState& hs = a.heads[bh];
+  const uint32_t h_theta = hs.theta, h_shift = hs.shift, h_bad = have_hist ? hs.hist_bad : 1u;
+  // (chunk indices clamped, so the loads are unconditional)
   uint2 pre[8][2];
   const int clast = nch > 0 ? nch - 1 : 0;
 #pragma unroll
@@ -521,22 +709,35 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
         }
       }
       __syncthreads();
-      select_lds_regs<NT, kSelCap / NT>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
+      const HistInfo hi{h_theta, static_cast<int>(h_shift), h_bad == 0u && h_shift < 32u};
+      select_lds_core<NT, kSelCap / NT, const int32_t*, true>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g,
+                                                              out_l, ws.hist, sc, hb, hi);
     } else if (M >= k_eff) {
       path = 1;
       const SlotSrc src{slots, ws.offs, nch, chunk};
       const SelRule rule = block_select_rule<NT>(src, M, k_eff, ws.hist, sc);
       block_compact_range<NT>(src, M, rule, r0, r1, out_g, out_l, sc);
     } else {
-      path = 2;  // the sample overestimated the threshold: use every score
-      if (scores_int) {
-        const I32RowSrc src{static_cast<const int32_t*>(scores_row)};
-        const SelRule rule = block_select_rule<NT>(src, n, k_eff, ws.hist, sc);
-        block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
+      path = 2;  // the sample overestimated the threshold: use every key
+      const long long base = static_cast<long long>(bh) * a.Nmax;
+      if (scores_row != nullptr && scores_int) {
+        select_all_keys<NT>(I32RowSrc{static_cast<const int32_t*>(scores_row)}, n, k_eff, r0, r1, out_g, out_l,
+                            ws.hist, sc);
+      } else if (scores_row != nullptr) {
+        select_all_keys<NT>(F32RowSrc{static_cast<const float*>(scores_row)}, n, k_eff, r0, r1, out_g, out_l,
+                            ws.hist, sc);
+      } else if (a.meta_kind == kScanHamming) {
+        const int G = a.Hq / a.Hkv;
+        const HamRescoreSrc src{static_cast<const uint32_t*>(a.meta) + base * 4,
+                                a.qcodes + static_cast<long long>(bh) * G * 4, G};
+        select_all_keys<NT>(src, n, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
       } else {
-        const F32RowSrc src{static_cast<const float*>(scores_row)};
-        const SelRule rule = block_select_rule<NT>(src, n, k_eff, ws.hist, sc);
-        block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
+        const bool f16 = a.meta_f16 != 0;
+        const char* vnb = static_cast<const char*>(a.meta_vn) + base * (f16 ? 2 : 4);
+        const SoftRescoreSrc src{static_cast<const uint8_t*>(a.meta) + base * a.L, vnb,
+                                 a.tables + static_cast<long long>(bh) * (static_cast<long long>(a.L) << a.P),
+                                 a.L, (1u << a.P) - 1u, f16};
+        select_all_keys<NT>(src, n, k_eff, r0, r1, out_g, out_l, ws.hist, sc);
       }
     }
   }

@@ -10,6 +10,7 @@
 namespace hst {
 
 constexpr int kSample = 2048;      // keys sampled per head for the candidate threshold
+constexpr int kHistBins = 2048;    // bins of the per-head histogram of candidate keys
 constexpr int kRunLen = 8;         // the sample is kSample / kRunLen runs of consecutive keys
 constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
 constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
@@ -23,16 +24,18 @@ struct HeadState {
   int32_t k_eff;        // keys to select
   int32_t n;            // context length
   uint32_t cand_total;  // candidates the scan found (diagnostic)
-  uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every score (diagnostic)
-  uint32_t pad0;
-  uint64_t thr_word;    // (1 << 32) | theta once the scan has published it, else 0
-  uint32_t pad[8];
+  uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every key rescored or read (diagnostic)
+  uint32_t shift;       // histogram bin width: candidate key c is counted in bin
+                        //   min(kHistBins - 1, (c - theta) >> shift)
+  uint64_t thr_word;    // ((0x100 | shift) << 32) | theta once the scan has published it, else 0
+  uint32_t hist_bad;    // nonzero when a chunk filtered without the published threshold
+  uint32_t pad[7];
 };
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_scores, off_counts,
-      off_slots, off_part_o, off_part_ml, bytes;
+  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_hist, off_counts, off_slots,
+      off_part_o, off_part_ml, bytes;
   int chunk;    // candidate slots per scan chunk (the stride of the slot array)
   int nchunks;  // scan chunks per head at the default chunk length (the most there can be)
   int sample, xparts, rps, nsplit, kind;
@@ -50,10 +53,17 @@ struct FusedArgs {
                      //   (soft-LSH: tables of the workgroup; binary codes: its 16 code bits;
                      //   given scores: part 0 holds the order keys' bits)
   float* svn;        // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
+  uint32_t* hist;    // [B*Hkv][kHistBins]: candidate keys per bin (see HeadState::shift)
   uint32_t* counts;  // [B*Hkv][nchunks]
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index), chunk c holding keys [c*span, (c+1)*span)
   float* part_o;     // [B*Hq][nsplit][d]
   float* part_ml;    // [B*Hq][nsplit][2]
+  // the key metadata, for rescoring every key when fewer than k keys passed
+  // the threshold (meta_kind: kScanSoftFast / kScanSoftAny: ids [.][Nmax][L]
+  // with value norms meta_vn; kScanHamming: 128-bit codes; -1: none)
+  const void* meta;
+  const void* meta_vn;
+  int meta_f16, meta_kind;
   // shared prefix (attention over given rows only): rows j < np come from
   // pk / pv [Hkv][np][d], rows np + j from K / V row j of the sequence
   const void* pk;
@@ -91,6 +101,8 @@ hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, 
                          int chunk, float scale, float* out, float* lse, hipStream_t st);
 hipError_t launch_select_only(const hst_shape& s, const FusedArgs& a, int32_t* idx, const void* scores,
                               int scores_int, int chunk, hipStream_t st);
+hipError_t launch_candidates(const hst_shape& s, const FusedArgs& a, int chunk, uint32_t* keys, int32_t* index,
+                             int32_t* count, uint32_t* theta, int cap, hipStream_t st);
 
 // cumulative-mass selection (mass.hip): float64 logits of the candidates in
 // `logits` ([B*Hq][kcap] doubles), then the cut and the compaction
@@ -166,6 +178,33 @@ hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K
                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,
                                 hipStream_t st);
+// The decode step's three stages over one workspace (the full step runs
+// them in this order): query tables or codes with the key sample; the
+// filtering scan (scores, threshold, candidates and their histogram); the
+// selection and the attention.
+hipError_t decode_prepare_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                                  double tau, const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                  int kcap, const int32_t* kps, void* ws, hipStream_t st);
+hipError_t decode_filter_softlsh(const hst_shape& s, int L, int P, const uint8_t* ids,
+                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
+                                 void* ws, hipStream_t st);
+hipError_t decode_finish_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
+                                 int L, int P, const uint8_t* ids, const void* vnorm,
+                                 int norm_dtype, int kcap, float scale, int32_t* idx, float* out,
+                                 float* lse, void* ws, hipStream_t st);
+hipError_t decode_prepare_hamming(const hst_shape& s, const void* q, const void* R,
+                                  const uint32_t* codes, int kcap, const int32_t* kps, void* ws,
+                                  hipStream_t st);
+hipError_t decode_filter_hamming(const hst_shape& s, const uint32_t* codes, int kcap,
+                                 const int32_t* kps, void* ws, hipStream_t st);
+hipError_t decode_finish_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
+                                 const uint32_t* codes, int kcap, float scale, int32_t* idx,
+                                 float* out, float* lse, void* ws, hipStream_t st);
+// candidates of every head after the filtering scan, in index order:
+// (order key, index) pairs, up to cap per head, their count and threshold
+hipError_t decode_candidates(const hst_shape& s, int op, int L, int P, int kcap, void* ws,
+                             uint32_t* keys, int32_t* index, int32_t* count, uint32_t* theta,
+                             int cap, hipStream_t st);
 hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,

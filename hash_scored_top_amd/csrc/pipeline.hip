@@ -43,8 +43,8 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
     f.off_spart = take(BH * static_cast<size_t>(f.xparts) * kSample * 4);
     if (soft) f.off_svn = take(BH * static_cast<size_t>(kSample) * 4);
   }
-  if (decode) f.off_scores = take(BH * static_cast<size_t>(s.Nmax) * 4);
   if (select) {
+    f.off_hist = take(BH * static_cast<size_t>(kHistBins) * 4);
     f.off_counts = take(BH * f.nchunks * 4);
     f.off_slots = take(BH * f.nchunks * static_cast<size_t>(f.chunk) * 8);
   }
@@ -82,6 +82,7 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   a.nsplit = f.nsplit;
   a.xparts = f.xparts;
   a.region_bytes = 65536;
+  a.meta_kind = -1;
   const int dchunk = f.kind == kScanSoftFast ? scan_chunk(L) : scan_chunk(0);
   a.span = f.nchunks > 0 ? scan_span(s, dchunk, f.chunk, true) : dchunk;
   char* p = static_cast<char*>(ws);
@@ -91,6 +92,7 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
     a.spart = reinterpret_cast<float*>(p + f.off_spart);
     a.svn = reinterpret_cast<float*>(p + f.off_svn);
+    a.hist = f.off_hist != 0 ? reinterpret_cast<uint32_t*>(p + f.off_hist) : nullptr;
     a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
     a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
     a.part_o = reinterpret_cast<float*>(p + f.off_part_o);
@@ -110,13 +112,46 @@ hipError_t fused_decode_softlsh(const hst_shape& s, const void* q, const void* K
                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,
                                 hipStream_t st) {
+  HST_CHECK(decode_prepare_softlsh(s, q, W, L, P, tau, ids, vnorm, norm_dtype, kcap, kps, ws, st));
+  HST_CHECK(decode_filter_softlsh(s, L, P, ids, vnorm, norm_dtype, kcap, kps, ws, st));
+  return decode_finish_softlsh(s, q, K, V, L, P, ids, vnorm, norm_dtype, kcap, scale, idx, out, lse, ws, st);
+}
+
+// The three stages of the soft-LSH decode step over one workspace.
+static FusedArgs soft_args(const hst_shape& s, void* ws, int L, int P, double tau, int kcap,
+                           const uint8_t* ids, const void* vnorm, int norm_dtype, FusedLayout* fo) {
   const FusedLayout f = fused_layout(s, HST_OP_DECODE_SOFTLSH, L, P, kcap);
-  const FusedArgs a = make_args(s, f, ws, L, P, tau, kcap);
-  const int f16 = norm_dtype == HST_F16;
-  float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + f.off_scores);
-  HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
-  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, kps, st));
-  return launch_attend(s, a, q, K, V, idx, true, scores, 0, f.chunk, scale, out, lse, st);
+  FusedArgs a = make_args(s, f, ws, L, P, tau, kcap);
+  a.meta = ids;
+  a.meta_vn = vnorm;
+  a.meta_f16 = norm_dtype == HST_F16;
+  a.meta_kind = f.kind;
+  if (fo != nullptr) *fo = f;
+  return a;
+}
+
+hipError_t decode_prepare_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,
+                                  double tau, const uint8_t* ids, const void* vnorm, int norm_dtype,
+                                  int kcap, const int32_t* kps, void* ws, hipStream_t st) {
+  const FusedArgs a = soft_args(s, ws, L, P, tau, kcap, ids, vnorm, norm_dtype, nullptr);
+  return launch_prep_soft(s, a, q, W, ids, vnorm, norm_dtype == HST_F16, kps, st);
+}
+
+hipError_t decode_filter_softlsh(const hst_shape& s, int L, int P, const uint8_t* ids,
+                                 const void* vnorm, int norm_dtype, int kcap, const int32_t* kps,
+                                 void* ws, hipStream_t st) {
+  FusedLayout f;
+  const FusedArgs a = soft_args(s, ws, L, P, 0.0, kcap, ids, vnorm, norm_dtype, &f);
+  return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, nullptr, 1, kps, st);
+}
+
+hipError_t decode_finish_softlsh(const hst_shape& s, const void* q, const void* K, const void* V,
+                                 int L, int P, const uint8_t* ids, const void* vnorm,
+                                 int norm_dtype, int kcap, float scale, int32_t* idx, float* out,
+                                 float* lse, void* ws, hipStream_t st) {
+  FusedLayout f;
+  const FusedArgs a = soft_args(s, ws, L, P, 0.0, kcap, ids, vnorm, norm_dtype, &f);
+  return launch_attend(s, a, q, K, V, idx, true, nullptr, 0, f.chunk, scale, out, lse, st);
 }
 
 // Workspace of the mass decode step: the decode layout, then the candidate
@@ -135,17 +170,16 @@ hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const vo
                                      int kcap, const int32_t* kps, double p, float scale,
                                      int32_t* idx, int32_t* counts, float* out, float* lse,
                                      void* ws, hipStream_t st) {
-  const FusedLayout f = fused_layout(s, HST_OP_DECODE_SOFTLSH, L, P, kcap);
-  const FusedArgs a = make_args(s, f, ws, L, P, tau, kcap);
+  FusedLayout f;
+  const FusedArgs a = soft_args(s, ws, L, P, tau, kcap, ids, vnorm, norm_dtype, &f);
   const int f16 = norm_dtype == HST_F16;
   char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base + f.off_scores);
   int32_t* cand = reinterpret_cast<int32_t*>(base + align256(f.bytes));
   const size_t ncand = static_cast<size_t>(s.B) * s.Hkv * static_cast<size_t>(kcap) * 4;
   double* logits = reinterpret_cast<double*>(base + align256(f.bytes) + align256(ncand));
   HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
-  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, scores, 1, kps, st));
-  HST_CHECK(launch_select_only(s, a, cand, scores, 0, f.chunk, st));
+  HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, nullptr, 1, kps, st));
+  HST_CHECK(launch_select_only(s, a, cand, nullptr, 0, f.chunk, st));
   HST_CHECK(launch_select_mass(s, q, K, cand, kcap, p, scale, idx, counts, logits, st));
   return launch_attend(s, a, q, K, V, idx, false, nullptr, 0, f.chunk, scale, out, lse, st);
 }
@@ -340,12 +374,49 @@ hipError_t fused_decode_hamming(const hst_shape& s, const void* q, const void* K
                                 const void* R, const uint32_t* codes, int kcap, const int32_t* kps,
                                 float scale, int32_t* idx, float* out, float* lse, void* ws,
                                 hipStream_t st) {
+  HST_CHECK(decode_prepare_hamming(s, q, R, codes, kcap, kps, ws, st));
+  HST_CHECK(decode_filter_hamming(s, codes, kcap, kps, ws, st));
+  return decode_finish_hamming(s, q, K, V, codes, kcap, scale, idx, out, lse, ws, st);
+}
+
+static FusedArgs ham_args(const hst_shape& s, void* ws, int kcap, const uint32_t* codes, FusedLayout* fo) {
   const FusedLayout f = fused_layout(s, HST_OP_DECODE_HAMMING, 0, 0, kcap);
-  const FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
-  int32_t* scores = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + f.off_scores);
-  HST_CHECK(launch_prep_hamming(s, a, q, R, codes, kps, st));
-  HST_CHECK(launch_scan(s, a, kScanHamming, codes, nullptr, 0, scores, 1, kps, st));
-  return launch_attend(s, a, q, K, V, idx, true, scores, 1, f.chunk, scale, out, lse, st);
+  FusedArgs a = make_args(s, f, ws, 0, 0, 0.0, kcap);
+  a.meta = codes;
+  a.meta_kind = kScanHamming;
+  if (fo != nullptr) *fo = f;
+  return a;
+}
+
+hipError_t decode_prepare_hamming(const hst_shape& s, const void* q, const void* R,
+                                  const uint32_t* codes, int kcap, const int32_t* kps, void* ws,
+                                  hipStream_t st) {
+  const FusedArgs a = ham_args(s, ws, kcap, codes, nullptr);
+  return launch_prep_hamming(s, a, q, R, codes, kps, st);
+}
+
+hipError_t decode_filter_hamming(const hst_shape& s, const uint32_t* codes, int kcap,
+                                 const int32_t* kps, void* ws, hipStream_t st) {
+  const FusedArgs a = ham_args(s, ws, kcap, codes, nullptr);
+  return launch_scan(s, a, kScanHamming, codes, nullptr, 0, nullptr, 1, kps, st);
+}
+
+hipError_t decode_finish_hamming(const hst_shape& s, const void* q, const void* K, const void* V,
+                                 const uint32_t* codes, int kcap, float scale, int32_t* idx,
+                                 float* out, float* lse, void* ws, hipStream_t st) {
+  FusedLayout f;
+  const FusedArgs a = ham_args(s, ws, kcap, codes, &f);
+  return launch_attend(s, a, q, K, V, idx, true, nullptr, 1, f.chunk, scale, out, lse, st);
+}
+
+hipError_t decode_candidates(const hst_shape& s, int op, int L, int P, int kcap, void* ws,
+                             uint32_t* keys, int32_t* index, int32_t* count, uint32_t* theta,
+                             int cap, hipStream_t st) {
+  const bool soft = op == HST_OP_DECODE_SOFTLSH;
+  const FusedLayout f = fused_layout(s, soft ? HST_OP_DECODE_SOFTLSH : HST_OP_DECODE_HAMMING,
+                                     soft ? L : 0, soft ? P : 0, kcap);
+  const FusedArgs a = make_args(s, f, ws, soft ? L : 0, soft ? P : 0, 0.0, kcap);
+  return launch_candidates(s, a, f.chunk, keys, index, count, theta, cap, st);
 }
 
 hipError_t fused_score_softlsh(const hst_shape& s, const void* q, const void* W, int L, int P,

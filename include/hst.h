@@ -269,10 +269,12 @@ hst_status hst_select_mass(const hst_shape* shape, const void* q, const void* K,
                            size_t ws_bytes, void* stream);
 
 /*
- * One soft-LSH decode step: hst_score_keys_softlsh, hst_select_topk and
- * hst_sparse_decode_attention in sequence on the same stream, with the
- * scores kept in the workspace.  idx (the selection, as hst_select_topk
- * writes it) is an output.  lse nullable.
+ * One soft-LSH decode step: the scores of hst_score_keys_softlsh, the
+ * selection of hst_select_topk over them and hst_sparse_decode_attention
+ * over that selection, on the same stream (the three stage calls below).
+ * Only the candidate keys' scores are kept (in the workspace), not the
+ * whole score row.  idx (the selection, as hst_select_topk writes it) is an
+ * output.  lse nullable.
  */
 hst_status hst_decode_step_softlsh(const hst_shape* shape, const void* q,
                                    const void* K, const void* V,
@@ -390,6 +392,76 @@ hst_status hst_decode_step_softlsh_shared(const hst_shape* shape, int Np,
 /* Workspace bytes of hst_decode_step_softlsh_shared. */
 hst_status hst_workspace_size_shared(const hst_shape* shape, int Np, int L,
                                      int P, int k, size_t* bytes);
+
+/*
+ * The decode step in three stages over one workspace (the same workspace
+ * hst_workspace_size reports for HST_OP_DECODE_SOFTLSH / _HAMMING).  Run in
+ * this order on one stream, they compute exactly what hst_decode_step_softlsh
+ * (hst_decode_step_hamming, 128-bit codes) computes; the step itself is
+ * these three calls.  Each stage reads what the previous one left in the
+ * workspace, so a caller may put other work between them but must not reuse
+ * the workspace in between.
+ *   prepare: the query tables [SOCKET, core mechanism item 2] (or the query
+ *            codes [HATA, section 3]) and the scores of a fixed sample of
+ *            2048 keys per (sequence, kv head), which bound the top-k
+ *            threshold from below;
+ *   filter:  every key scored once [SOCKET, item 3; HATA, section 3]; the
+ *            keys scoring at or above the threshold are kept as candidates,
+ *            in index order, with a histogram of their scores (the exactness
+ *            of the selection never depends on the threshold);
+ *   finish:  the exact top-k of the candidates (or of every key, rescored,
+ *            when fewer than k_b keys passed the threshold) and exact
+ *            attention over them [SOCKET, item 4]; idx, out, lse as for the
+ *            full step.
+ * k_per_seq (optional) is read by prepare and filter; finish uses what
+ * filter recorded.  Arguments are those of the full step.
+ */
+hst_status hst_decode_prepare_softlsh(const hst_shape* shape, const void* q,
+                                      const void* W, int L, int P, double tau,
+                                      const uint8_t* ids, const void* vnorm,
+                                      int norm_dtype, int k,
+                                      const int32_t* k_per_seq, void* ws,
+                                      size_t ws_bytes, void* stream);
+hst_status hst_decode_filter_softlsh(const hst_shape* shape, int L, int P,
+                                     const uint8_t* ids, const void* vnorm,
+                                     int norm_dtype, int k,
+                                     const int32_t* k_per_seq, void* ws,
+                                     size_t ws_bytes, void* stream);
+hst_status hst_decode_finish_softlsh(const hst_shape* shape, const void* q,
+                                     const void* K, const void* V, int L, int P,
+                                     const uint8_t* ids, const void* vnorm,
+                                     int norm_dtype, int k, float scale,
+                                     int32_t* idx, float* out, float* lse,
+                                     void* ws, size_t ws_bytes, void* stream);
+hst_status hst_decode_prepare_hamming(const hst_shape* shape, const void* q,
+                                      const void* R, const uint32_t* codes,
+                                      int k, const int32_t* k_per_seq, void* ws,
+                                      size_t ws_bytes, void* stream);
+hst_status hst_decode_filter_hamming(const hst_shape* shape,
+                                     const uint32_t* codes, int k,
+                                     const int32_t* k_per_seq, void* ws,
+                                     size_t ws_bytes, void* stream);
+hst_status hst_decode_finish_hamming(const hst_shape* shape, const void* q,
+                                     const void* K, const void* V,
+                                     const uint32_t* codes, int k, float scale,
+                                     int32_t* idx, float* out, float* lse,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Inspection of the filter stage: for every (sequence b, kv head h), row
+ * bh = b*Hkv + h of the outputs receives the candidates the filter stage
+ * left in the workspace, in index order, as (order key, index) pairs in
+ * keys[bh][0..cap) / index[bh][0..cap) (at most cap of them), their number
+ * in count[bh] (which may exceed cap) and the threshold in theta[bh].  The
+ * order key of a float32 score s >= 0 is bits(s) | 0x80000000 (of an int32
+ * score v: v ^ 0x80000000).  op is HST_OP_DECODE_SOFTLSH (L, P as for the
+ * step) or HST_OP_DECODE_HAMMING; ws must come from a filter stage of the
+ * same shape and k.
+ */
+hst_status hst_decode_candidates(const hst_shape* shape, int op, int L, int P,
+                                 int k, void* ws, size_t ws_bytes, int cap,
+                                 uint32_t* keys, int32_t* index, int32_t* count,
+                                 uint32_t* theta, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under graph capture,

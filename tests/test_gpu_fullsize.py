@@ -12,6 +12,10 @@ hold at any size:
   the float32 rounding band of the k-th score); attention over the GPU's own
   selected set within 2e-2 absolute of the oracle's attention over that set,
   and the log-sum-exp within 1e-4;
+* sampled slabs: the candidates the step's own filtering scan kept, read back
+  from its workspace, carry their oracle scores (soft-LSH within 1e-5
+  relative, binary codes exactly) and include every key clearly above the
+  head's threshold;
 * every slab: indices ascending, in [0, N_b), exactly k_b of them, -1 after;
   and the set is exactly the first k_b keys in the order (score descending,
   index ascending) of the scores the GPU scorer produces.
@@ -53,6 +57,38 @@ def _topk_of(scores, k):
     return np.sort(order[:k])
 
 
+CAND_CAP = 16384  # candidates read back per head (the step's own filtering-scan scores)
+
+
+def _check_candidates(scheme, s, keys, index, count, theta, kk, where):
+    """The candidates the step's filtering scan kept for one head, against the
+    oracle's scores s: in index order, each with its own score (soft-LSH:
+    within 1e-5 relative; binary codes: exact), and every key clearly above
+    the threshold among them (binary codes: exactly the keys >= it)."""
+    c = min(count, CAND_CAP)
+    assert count >= kk, where
+    ix = index[:c]
+    assert (np.diff(ix) > 0).all() and ix[0] >= 0 and ix[-1] < s.shape[0], where
+    u = keys[:c].astype(np.uint32)
+    th = np.uint32(theta & 0xFFFFFFFF)
+    if scheme == "softlsh":
+        assert (u & np.uint32(0x80000000)).all(), where
+        got = (u & np.uint32(0x7FFFFFFF)).view(np.float32).astype(np.float64)
+        rel = np.abs(got - s[ix]) / s[ix]
+        assert rel.max() <= 1e-5, (where, rel.max())
+        thf = float(np.array([th & np.uint32(0x7FFFFFFF)], np.uint32).view(np.float32)[0]) \
+            if th & np.uint32(0x80000000) else 0.0
+        must = np.nonzero(s >= thf * (1 + 2e-5))[0]
+        must = must[must <= ix[-1]] if count > c else must
+        assert np.isin(must, ix).all(), where
+    else:
+        got = (u ^ np.uint32(0x80000000)).view(np.int32)
+        np.testing.assert_array_equal(got, s[ix], err_msg=str(where))
+        thi = int(np.array([th ^ np.uint32(0x80000000)], np.uint32).view(np.int32)[0])
+        want = np.nonzero(s >= thi)[0]
+        np.testing.assert_array_equal(ix, want[:c], err_msg=str(where))
+
+
 @pytest.mark.parametrize("name", LARGE)
 def test_fullsize_decode_step(name):
     import hash_scored_top_amd as hst
@@ -78,6 +114,7 @@ def test_fullsize_decode_step(name):
         step = hst.DecodeSoftLSH(K, w.Hq, w.L, w.P, w.tau, kmax, vn.dtype, seq_lens=sl,
                                  k_per_seq=kp)
         idx, out, lse = step(q, K, V, Wd, ids, vn)
+        cand = step.candidates(CAND_CAP)
         scores = hst.hst_score_keys_softlsh(q, Wd, w.L, w.P, w.tau, ids, vn, K, seq_lens=sl)
         meta = (ids.cpu().numpy(), vn.cpu().numpy().astype(np.float64))
     else:
@@ -85,11 +122,13 @@ def test_fullsize_decode_step(name):
         codes = hst.hst_hash_keys_binary(K, Rd, seq_lens=sl)
         step = hst.DecodeHamming(K, w.Hq, kmax, seq_lens=sl, k_per_seq=kp)
         idx, out, lse = step(q, K, V, Rd, codes)
+        cand = step.candidates(CAND_CAP)
         scores = hst.hst_score_keys_hamming(q, Rd, codes, K, seq_lens=sl)
         meta = (codes.cpu().numpy().view(np.uint32),)
     torch.cuda.synchronize()
     idx, out, lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
     scores = scores.cpu().numpy()
+    ckeys, cidx, ccount, ctheta = (t.cpu().numpy() for t in cand)
     paths = np.frombuffer(step.ws[:64 * w.B * w.Hkv].cpu().numpy().tobytes(),
                           dtype=np.uint32).reshape(-1, 16)[:, 4]
     print(f"[fullsize] {name}: selection paths {np.bincount(paths, minlength=3).tolist()}",
@@ -133,6 +172,8 @@ def test_fullsize_decode_step(name):
             r = O.decode_slab_hamming(q64, K64, V64, f64(x["R"][h]), kb)
             np.testing.assert_array_equal(meta[0][b, h, :n], r["kcodes"])
             np.testing.assert_array_equal(scores[b, h, :n], r["scores"])
+        _check_candidates(w.scheme, r["scores"], ckeys[b, h], cidx[b, h], int(ccount[b, h]),
+                          int(ctheta[b, h]), min(kb, n), (b, h))
         got = idx[b, h, :min(kb, n)]
         diff = set(got.tolist()) ^ set(r["idx"].tolist())
         if w.scheme == "hamming":
