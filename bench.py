@@ -9,12 +9,18 @@ rows.  The prefill hashing is timed separately.
 Inputs are resident in HBM before timing.  Each timed step reads a different
 copy of the key metadata and K/V (``--rotate`` copies, enough to exceed twice
 the 256 MB Infinity Cache), so repeated steps cannot be served from cache.
-The timed steps are replays of one captured graph holding one step per input
-copy (``--no-graph`` times eager launches instead).
+Exactly ``--steps`` steps are timed back to back: replays of captured graphs
+of up to 1024 consecutive steps between two events (``--no-graph`` times
+eager launches instead).  The per-step latency percentiles come from a
+separate pass that launches each step alone (one-step graph replays with an
+event between steps).
 
 Prints one JSON line: decode tokens/s (= batch / step time), the roofline of
-the dominant kernel (HBM bytes per launch / event-timed duration), the whole
-step's fraction of the HBM roofline, and the CPU oracle's rate on the host.
+the dominant kernel (the step's own filtering scan: the metadata bytes of
+every key / its event-timed duration in the step's filter stage), the whole
+step's fraction of the HBM roofline, and the CPU oracle's rate on the host
+(the whole step over every slab, in single-threaded processes over the
+host's CPUs).
 Beside them: the prefill hashing, the decode-time append, the step with a
 cumulative-mass budget instead of a fixed k, the step with two-level chunk
 routing, and dense attention over every cached key (for the sparse/dense
@@ -54,7 +60,6 @@ def parse():
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix leg")
     ap.add_argument("--core-only", action="store_true",
                     help="time the step and the roofline kernel only (no variant legs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of a captured graph")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -79,6 +84,38 @@ def capture(fn):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def spin_cycles_per_ms(stream):
+    """Cycles of torch's spin kernel per millisecond on this GPU."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 2_000_000
+    torch.cuda._sleep(1000)
+    e0.record(stream)
+    torch.cuda._sleep(cyc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return cyc / max(e0.elapsed_time(e1), 1e-3)
+
+
+def scan_span_of(w, dev):
+    """Keys per chunk of the step's filtering scan (as the library picks it:
+    chunks are lengthened when the threshold workgroups would add a round of
+    resident workgroups, two per compute unit)."""
+    import torch
+    chunk, cap = 2048, 2560
+    BH, N = w.B * w.Hkv, w.N
+    R0 = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    nch0 = -(-N // chunk)
+    r_chunks, r_all = -(-BH * nch0 // R0), -(-BH * (nch0 + 1) // R0)
+    if r_all == r_chunks:
+        return chunk
+    nch = r_chunks * R0 // BH - 1
+    if nch < 1:
+        return chunk
+    span = (-(-N // nch) + 63) // 64 * 64
+    return span if span <= cap else chunk
 
 
 def alg_bytes(w, lens, ks):
@@ -117,58 +154,124 @@ def traffic_record(kernel: str, workload: str, src: str):
         return None
 
 
-def cpu_baseline(w, x, seconds):
-    """The float64 oracle's decode step on a sample of (b, kv head) slabs."""
+CPU_WORKERS_MAX = 16  # the host share one GPU machine gives a run
+
+
+def _cpu_worker(wname, slabs, conn):
+    """One process of the CPU baseline: the float64 oracle's decode step on
+    its (b, kv head) slabs, one BLAS thread.  Started before the parent
+    touches the GPU; it generates its slabs and their prefill metadata when
+    told to (untimed), then times its share of each step on request."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    sys.path.insert(0, ROOT)
     import numpy as np
     import oracle as O
     import workloads as WL
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    lens, ks = x["seq_lens"], x["k_per_seq"]
-    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)][:2]
+    w = WL.WORKLOADS[wname]
+    lens, ks = w.seq_lens(), w.k_per_seq()
     prepared = []
-    for (b, h) in slabs:
-        n = int(lens[b])
-        q64 = WL.storage_to_f64(x["q"][b, h * w.G:(h + 1) * w.G], w.kv_dtype)
-        K64 = WL.storage_to_f64(x["K"][b, h, :n], w.kv_dtype)
-        V64 = WL.storage_to_f64(x["V"][b, h, :n], w.kv_dtype)
-        if w.scheme == "softlsh":
-            W64 = WL.storage_to_f64(x["W"][h], w.kv_dtype)
-            meta = (O.hash_keys_softlsh(K64, W64, w.L, w.P), O.value_norms(V64, w.norm_dtype), W64)
-        else:
-            R64 = WL.storage_to_f64(x["R"][h], w.kv_dtype)
-            meta = (O.binary_codes(K64, R64), None, R64)
-        prepared.append((b, h, q64, K64, V64, meta))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx is not None:
-        ctx.__enter__()
-    try:
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            for (b, h, q64, K64, V64, meta) in prepared:
-                kb = int(ks[b])
+    while True:
+        msg = conn.recv()
+        if msg == "prepare":
+            for (b, h) in slabs:
+                n = int(lens[b])
+                sl = WL.make_slab(w, b, h, n)
+                q64 = WL.storage_to_f64(sl["q"], w.kv_dtype)
+                K64 = WL.storage_to_f64(sl["K"], w.kv_dtype)
+                V64 = WL.storage_to_f64(sl["V"], w.kv_dtype)
+                if w.scheme == "softlsh":
+                    W64 = WL.storage_to_f64(WL.make_planes(w, h), w.kv_dtype)
+                    meta = (O.hash_keys_softlsh(K64, W64, w.L, w.P),
+                            O.value_norms(V64, w.norm_dtype), W64)
+                else:
+                    R64 = WL.storage_to_f64(WL.make_projection(w, h), w.kv_dtype)
+                    meta = (O.binary_codes(K64, R64), None, R64)
+                prepared.append((int(ks[b]), q64, K64, V64, meta))
+            conn.send("ready")
+        elif msg == "go":
+            t0 = time.perf_counter()
+            for (kb, q64, K64, V64, meta) in prepared:
                 if w.scheme == "softlsh":
                     O.decode_slab_softlsh(q64, K64, V64, meta[2], w.L, w.P, w.tau, kb,
                                           w.norm_dtype, ids=meta[0], vnorm=meta[1])
                 else:
                     O.decode_slab_hamming(q64, K64, V64, meta[2], kb, kcodes=meta[0])
-            reps += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    per_slab = dt / (reps * len(prepared))
-    t_step = per_slab * w.B * w.Hkv
-    return {"value": w.B / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{len(prepared)} of {w.B * w.Hkv} (batch, kv head) slabs, decode step "
-                       f"(tables/codes, scores, top-k, attention) x{reps}, float64 numpy, one "
-                       f"thread; step time = mean slab time x {w.B * w.Hkv}"),
-            "seconds": round(dt, 2), "step_s": t_step}
+            conn.send(time.perf_counter() - t0)
+        else:
+            conn.close()
+            return
+
+
+class CpuBaseline:
+    """The oracle's whole decode step (every (b, kv head) slab of the
+    workload) on the host, in a pool of single-threaded processes over the
+    CPUs this process may run on (at most CPU_WORKERS_MAX).  The processes
+    are spawned before the GPU is initialised; the step time is the wall
+    time of one step with every worker running its slabs at once (the
+    slowest worker), median of `reps` steps."""
+
+    def __init__(self, w):
+        import multiprocessing as mp
+        self.w = w
+        self.affinity = len(os.sched_getaffinity(0))
+        slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+        nw = max(1, min(self.affinity, CPU_WORKERS_MAX, len(slabs)))
+        # longest slabs first, dealt round robin
+        lens = w.seq_lens()
+        slabs.sort(key=lambda bh: -int(lens[bh[0]]))
+        parts = [slabs[i::nw] for i in range(nw)]
+        ctx = mp.get_context("spawn")
+        self.conns, self.procs = [], []
+        for part in parts:
+            a, b = ctx.Pipe()
+            p = ctx.Process(target=_cpu_worker, args=(w.name, part, b), daemon=True)
+            p.start()
+            self.conns.append(a)
+            self.procs.append(p)
+        self.nslabs = len(slabs)
+
+    def run(self, reps=3):
+        t0 = time.perf_counter()
+        for c in self.conns:
+            c.send("prepare")
+        for c in self.conns:
+            assert c.recv() == "ready"
+        prep_s = time.perf_counter() - t0
+        steps = []
+        for _ in range(reps):
+            for c in self.conns:
+                c.send("go")
+            steps.append(max(c.recv() for c in self.conns))
+        self.close()
+        steps.sort()
+        t_step = steps[len(steps) // 2]
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+        return {"value": self.w.B / t_step, "unit": "tokens/s", "cores": len(self.procs),
+                "kind": "oracle",
+                "sample": (f"the whole decode step (query tables or codes, scores, top-k, "
+                           f"attention) over all {self.nslabs} (batch, kv head) slabs, float64 "
+                           f"numpy oracle, {len(self.procs)} single-threaded processes; median "
+                           f"of {reps} steps"),
+                "step_s": t_step, "steps_s": steps, "affinity_cpus": self.affinity,
+                "cpu_model": model, "prepare_s": round(prep_s, 1)}
+
+    def close(self):
+        for c in self.conns:
+            try:
+                c.send("stop")
+            except (BrokenPipeError, OSError):
+                pass
+        for p in self.procs:
+            p.join(timeout=10)
 
 
 SHARED_B, SHARED_NP, SHARED_NS = 8, 32768, 2048
@@ -248,16 +351,20 @@ def main():
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
+    w = None
+    import workloads as WL
+    w = WL.WORKLOADS[args.workload]
+    # the CPU baseline's processes start before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else CpuBaseline(w)
+
     import numpy as np
     import torch
 
     import hash_scored_top_amd as hst
-    import workloads as WL
     from workloads.device import norm_torch_dtype, to_dev
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = WL.WORKLOADS[args.workload]
     log(f"workload {w.name}: generating inputs")
     t0 = time.time()
     x = WL.make_full(w)
@@ -378,87 +485,99 @@ def main():
         run = lambda i: step(q, sets[i % R][0], sets[i % R][1], Rp, sets[i % R][2])
     torch.cuda.synchronize()
 
+    # exactly args.steps steps (input copy t % R) back to back: replays of
+    # captured graphs of up to 1024 consecutive steps (--no-graph: eager
+    # launches), between two events.  A spin kernel first keeps the GPU busy
+    # while the host enqueues, so no step waits for the host.
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
-    per = []
+    spin = spin_cycles_per_ms(stream)
+    GSTEPS = 1024
+    spans = [(s0, min(s0 + GSTEPS, args.steps)) for s0 in range(0, args.steps, GSTEPS)]
+    graphs = [] if args.no_graph else [capture(lambda s0=s0, s1=s1: [run(t) for t in range(s0, s1)])
+                                       for s0, s1 in spans]
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    log(f"warmup {args.warmup} done; timing {args.steps} steps "
+        f"({'eager' if args.no_graph else f'{len(graphs)} graph replay(s)'}, {R} input copies)")
+    torch.cuda._sleep(int(spin * min(500.0, 5.0 + 0.2 * args.steps)))
+    ev[0].record(stream)
     if args.no_graph:
-        log(f"warmup {args.warmup} done; timing {args.steps} eager steps")
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        t_begin = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_begin.record(stream)
-        for i in range(args.steps):
-            starts[i].record(stream)
-            run(i)
-            ends[i].record(stream)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_begin.elapsed_time(t_end)
-        timed = args.steps
-        per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
+        for t in range(args.steps):
+            run(t)
     else:
-        # one captured graph runs the R rotated steps back to back; the launch
-        # cost of the host stays out of the timed region
-        graph = capture(lambda: [run(i) for i in range(R)])
-        graph.replay()
-        torch.cuda.synchronize()
-        reps = max(1, math.ceil(args.steps / R))
-        timed = reps * R
-        log(f"warmup {args.warmup} done; timing {timed} steps ({reps} replays of a {R}-step graph)")
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-        t_begin = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_begin.record(stream)
-        for i in range(reps):
-            starts[i].record(stream)
-            graph.replay()
-            ends[i].record(stream)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_begin.elapsed_time(t_end)
-        per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3 / R  # us per step
+        for g in graphs:
+            g.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    timed = args.steps
+    total_ms = ev[0].elapsed_time(ev[1])
     ms_per_step = total_ms / timed
-    log(f"step {ms_per_step * 1e3:.2f} us (p50 {np.percentile(per, 50):.2f} us)")
+    del graphs
+    # per-step latency: each step launched alone (one replay of a captured
+    # one-step graph), an event between consecutive steps
+    g1 = [capture(lambda i=i: run(i)) for i in range(R)]
+    nlat = min(args.steps, 200)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nlat + 1)]
+    torch.cuda._sleep(int(spin * min(500.0, 5.0 + 0.2 * nlat)))
+    evs[0].record(stream)
+    for t in range(nlat):
+        g1[t % R].replay()
+        evs[t + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(nlat)]) * 1e3  # us
+    del g1
+    log(f"step {ms_per_step * 1e3:.2f} us back to back; alone p50 {np.percentile(per, 50):.2f} us")
 
-    # dominant kernel (the score scan: every key's metadata once), timed alone
-    # with events on the stream it is launched on
+    # the step's stages, each between events (the spin kernel first again):
+    # prepare (query tables, key sample), filter (the score scan with the
+    # threshold and the candidates: the dominant kernel), finish (selection,
+    # attention and the split merge)
+    iters = args.kernel_iters
+    if w.scheme == "softlsh":
+        stages = (lambda i: step.prepare(q, Wp, sets[i % R][2], sets[i % R][3]),
+                  lambda i: step.filter(sets[i % R][2], sets[i % R][3]),
+                  lambda i: step.finish(q, sets[i % R][0], sets[i % R][1], sets[i % R][2],
+                                        sets[i % R][3]))
+    else:
+        stages = (lambda i: step.prepare(q, Rp, sets[i % R][2]),
+                  lambda i: step.filter(sets[i % R][2]),
+                  lambda i: step.finish(q, sets[i % R][0], sets[i % R][1], sets[i % R][2]))
+    for i in range(3):
+        for f in stages:
+            f(i)
+    torch.cuda.synchronize()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+    torch.cuda._sleep(int(spin * min(500.0, 5.0 + 0.3 * iters)))
+    for i in range(iters):
+        sev[i][0].record(stream)
+        for j, f in enumerate(stages):
+            f(i)
+            sev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_us = [float(np.median([sev[i][j].elapsed_time(sev[i][j + 1]) * 1e3 for i in range(iters)]))
+                for j in range(3)]
+    scan_mean_us = float(np.mean([sev[i][1].elapsed_time(sev[i][2]) * 1e3 for i in range(iters)]))
+    log("stages (median us): prepare {:.2f}, filter {:.2f}, finish {:.2f}".format(*stage_us))
+
+    # dominant kernel: the step's own filtering scan (the filter stage is that
+    # one launch), with its algorithmic bytes: the metadata of every key
+    # (ids + value norm, or the code), read once
+    kbytes = meta_b
     if w.scheme == "softlsh":
         f16 = "true" if w.norm_dtype == "f16" else "false"
-        # scores only (no candidate filter), default chunk length
-        kname = f"scan_softlsh_kernel<{w.L // 16}, 2, false, {f16}, false>"
-        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
-        tables = hst.hst_query_tables_softlsh(q, Wp, w.L, w.P, w.tau, K, seq_lens=sl)
-        sc = torch.empty((w.B, w.Hkv, w.N), dtype=torch.float32, device=dev)
-        kbytes = meta_b + 4 * tot_keys  # metadata read + one float32 score written per key
-        launch = lambda i: hst.hst_score_scan_softlsh(tables, sets[i % R][2], sets[i % R][3], K,
-                                                      w.Hq, seq_lens=sl, scores=sc)
+        span = scan_span_of(w, dev)
+        kname = (f"scan_softlsh_kernel<{w.L // 16}, 2, true, {f16}, "
+                 f"{'true' if span > 2048 else 'false'}>")
+        ktag = "scan_softlsh_filter"
     else:
-        # no entry point launches the binary-code scan alone: time query codes + scan
-        kname = "prep_hamming+scan_lane_kernel"
-        ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
-        kbytes = meta_b + 4 * tot_keys
-        launch = lambda i: hst.hst_score_keys_hamming(q, Rp, sets[i % R][2], K, seq_lens=sl)
-    for i in range(5):
-        launch(i)
-    torch.cuda.synchronize()
-    # launches back to back (captured), one event pair around the batch
-    kgraph = capture(lambda: [launch(i) for i in range(args.kernel_iters)])
-    kgraph.replay()
-    k0 = torch.cuda.Event(enable_timing=True)
-    k1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    k0.record(stream)
-    kgraph.replay()
-    k1.record(stream)
-    torch.cuda.synchronize()
-    kus = k0.elapsed_time(k1) * 1e3 / args.kernel_iters
+        kname = "scan_lane_kernel<2>"
+        ktag = "scan_hamming_filter"
+    ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
+    kus = scan_mean_us
     achieved = kbytes / (kus * 1e-6) / 1e9
-    traffic = traffic_record(kname.split("<")[0].replace("_kernel", ""), w.name, ksrc)
+    traffic = traffic_record(ktag, w.name, ksrc)
 
     def time_graph(fn, reps=10):
         """Median per-call time (us) of fn over replays of a captured graph of R calls."""
@@ -592,11 +711,18 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "alg_bytes_per_launch": kbytes,
-                     "avg_launch_us": kus},
+                     "avg_launch_us": kus, "launches": iters,
+                     "timing": "HIP events around the step's filter stage (that one kernel), "
+                               "on the stream it is launched on"},
         "step": {"alg_bytes": step_bytes, "meta_bytes": meta_b, "gathered_bytes": gath_b,
                  "hbm_frac": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                 "p10_us": float(np.percentile(per, 10)), "p50_us": float(np.percentile(per, 50)),
-                 "p90_us": float(np.percentile(per, 90)), "rotated_copies": R},
+                 "latency_alone_us": {"p10": float(np.percentile(per, 10)),
+                                      "p50": float(np.percentile(per, 50)),
+                                      "p90": float(np.percentile(per, 90)),
+                                      "p99": float(np.percentile(per, 99)), "steps": int(len(per))},
+                 "rotated_copies": R,
+                 "stages_us": {"prepare": stage_us[0], "filter": stage_us[1],
+                               "finish": stage_us[2]}},
         "prefill": prefill,
         "append": append,
         "mass": mass,
@@ -605,9 +731,9 @@ def main():
         "codes_sweep": codes_sweep,
         "dense": dense,
     }
-    if not args.no_cpu_baseline:
+    if cpu is not None:
         log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu.run()
     print(json.dumps(result), flush=True)
 
 

@@ -3,12 +3,13 @@
 //    top-k keys by soft score, chosen deterministically; ties go to the lower
 //    index): each workgroup derives the head's selection from the candidate
 //    slots itself and keeps the part of the ascending index row that falls in
-//    its split, so no workgroup waits for another.
+//    its split, so no workgroup waits for another before the merge.
 //  * Attention (same item: exact attention on that subset): a split-K flash
 //    decode; each gathered K/V row is read once per kv head and used for all G
 //    query heads of the group (grouped-query attention), with an online
-//    softmax in the base-2 exponent domain.  A second kernel merges the split
-//    states through their log-sum-exp.
+//    softmax in the base-2 exponent domain.  The split states are merged
+//    through their log-sum-exp (by the last split of a head to finish, or by
+//    a second kernel when the rows are given).
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -81,17 +82,114 @@ size_t attend_smem(int nchunks, int rps) {
   return 65536 + 8192 + static_cast<size_t>(nchunks + 1) * 4 + static_cast<size_t>(rps) * 4;
 }
 
-// grid (nsplit, B*Hkv).  SELECT: rows come from the head's selection (and
-// the split's part of the index row is written to idx); otherwise rows are
-// read from idx.  Rows outside [0, N_b) are skipped.
-// bf16 rows with up to four query heads per kv head fit 128 VGPRs, so that two
-// workgroups share a CU.
+// Device-coherent stores and loads of the split states (relaxed atomics at
+// agent scope: they go to and come from the level every XCD shares, so no
+// cache-wide write-back or invalidation is needed around them).
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merge of the splits of one kv head's query heads, done by whichever
+// split of the head finishes last.  Each split stores its state with
+// store_dev, waits until those stores are complete, then adds one to the
+// head's arrival count (an agent-scope atomic); the split that brings the
+// count to nsplit reads the states with load_dev, merges the nsplit states of
+// each query head through their log-sum-exp (weights 2^(m_s - max m); the
+// weighted sum of l is the denominator) and resets the count for the next
+// step.  smem: the workgroup's LDS (>= 16 KB + 64 B, free at this point).
+template <int D, int NT>
+__device__ __forceinline__ void merge_splits(const FusedArgs& a, int bh, long long qh0, int G, int nsplit,
+                                             float* __restrict__ out, float* __restrict__ lse,
+                                             unsigned char* smem, BlockScratch<NT>& sc) {
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's state stores are complete
+  __syncthreads();
+  if (t == 0)
+    sc.found[0] = __hip_atomic_fetch_add(&a.heads[bh].arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          static_cast<uint32_t>(nsplit - 1)
+                      ? 1
+                      : 0;
+  __syncthreads();
+  if (sc.found[0] == 0) return;  // uniform
+  const int GS = G * nsplit;
+  float* wt = reinterpret_cast<float*>(smem);  // [G][nsplit]: the weights
+  float* ls = wt + GS;                         // [G]: sum of weighted l
+  float* mx = ls + 8;                          // [G]: max m
+  // this thread's first output: its partial outputs are in flight while the
+  // weights are formed
+  constexpr int PL = 32;
+  const bool has0 = t < G * D;
+  const int g0 = has0 ? t / D : 0, c0 = t % D;
+  const float* po0 = a.part_o + (qh0 + g0) * nsplit * D + c0;
+  float pv[PL];
+#pragma unroll
+  for (int u = 0; u < PL; ++u) pv[u] = has0 && u < nsplit ? load_dev(po0 + static_cast<long long>(u) * D) : 0.f;
+  // wave g forms the weights of query head g (lanes over the splits)
+  for (int g = wave; g < G; g += NW) {
+    const float* pml = a.part_ml + (qh0 + g) * nsplit * 2;
+    float M = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, load_dev(pml + 2 * s));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = 0.f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float mv = load_dev(pml + 2 * s);
+      const float w = mv == -INFINITY || M == -INFINITY ? 0.f : exp2f(mv - M);
+      wt[g * nsplit + s] = w;
+      L += w * load_dev(pml + 2 * s + 1);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (lane == 0) {
+      mx[g] = M;
+      ls[g] = L;
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < G * D; i += NT) {
+    const int g = i / D, c = i % D;
+    const float* po = a.part_o + (qh0 + g) * nsplit * D + c;
+    const float* wg = wt + g * nsplit;
+    float acc = 0.f;
+    int s = 0;
+    if (i == t) {
+#pragma unroll
+      for (int u = 0; u < PL; ++u)
+        if (u < nsplit) acc += wg[u] * pv[u];
+      s = PL;
+    }
+    for (; s < nsplit; ++s) acc += wg[s] * load_dev(po + static_cast<long long>(s) * D);
+    const float L = ls[g];
+    out[(qh0 + g) * D + c] = acc * (L > 0.f ? 1.f / L : 0.f);
+    if (c == 0) lse[qh0 + g] = L > 0.f ? (mx[g] + log2f(L)) * kLn2F : -INFINITY;
+  }
+  if (t == 0) a.heads[bh].arrive = 0u;
+}
+
+// grid (nsplit, B*Hkv).  Rows outside [0, N_b) are skipped.
+//  * SELECT: every split derives the head's exact selection from the
+//    candidate slots (in LDS when they fit; see select_from_candidates),
+//    keeps the rows of its part [r0, r1) of the ascending index row, attends
+//    over them and writes that part of the row (-1 past k_eff); the split
+//    that finishes last merges the head's split states (merge_splits).
+//  * !SELECT: rows come from idx; a second kernel merges the split states.
+// Rows are gathered in batches of NG*U, the next batch in flight while one
+// is consumed.  Without the selection, bf16 rows with up to four query heads
+// per kv head fit 128 VGPRs, so that two workgroups share a CU.
+template <typename T, int GMAX, bool SELECT>
+constexpr bool kAttOcc2 = !SELECT && sizeof(T) == 2 && GMAX <= 4;  // two workgroups per CU
+
 template <typename T, int D, int GMAX, bool SELECT>
 __global__ void __launch_bounds__(kAttNT)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 && GMAX <= 4 ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu(kAttOcc2<T, GMAX, SELECT> ? 4 : 1)))
 attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
               int32_t* __restrict__ idx, const void* __restrict__ scores, int scores_int, int chunk,
-              const int32_t* __restrict__ seq_lens, float scale_log2, FusedArgs a) {
+              const int32_t* __restrict__ seq_lens, float scale_log2, FusedArgs a, float* __restrict__ out,
+              float* __restrict__ lse) {
   constexpr int NT = kAttNT;
   constexpr int EPL = D / 16;
   constexpr int NW = NT / 64;
@@ -100,6 +198,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   // bf16 rows: q stays in packed bf16 pairs and each lane's part of a score is
   // a chain of pair dot products, scaled once after the row-group sum
   constexpr bool PK = sizeof(T) == 2;
+  typedef typename RowLd<T, EPL>::raw Raw;
   extern __shared__ __align__(16) unsigned char sm[];
   __shared__ BlockScratch<NT> sc;
   __shared__ float red_ml[NW][GMAX][2];
@@ -114,16 +213,25 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   const int r0 = split * a.rps, r1 = min(r0 + a.rps, a.kcap);
   const int t = threadIdx.x, sub = t & 15, grp = t >> 4, lane = t & 63, wave = t >> 6;
   int32_t* irow = idx + static_cast<long long>(bh) * a.kcap;
+  // the query rows, in flight during the selection
+  Raw qr[GMAX];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g)
+    if (g < G) qr[g] = RowLd<T, EPL>::load(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL);
   int nrows;
+  SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
+                   reinterpret_cast<uint32_t*>(sm + 65536), offs};
   if (SELECT) {
-    const int k_eff = a.heads[bh].k_eff;
-    SelectScratch ws{reinterpret_cast<uint32_t*>(sm), reinterpret_cast<int32_t*>(sm + 4 * kSelCap),
-                     reinterpret_cast<uint32_t*>(sm + 65536), offs};
-    int M = 0;
+    // the head's k_eff, threshold and histogram shift, read before anything
+    // else is in flight
+    const HeadState& hs = a.heads[bh];
+    const int k_eff = hs.k_eff;
+    const uint32_t h_theta = hs.theta, h_shift = hs.shift;
+    const int M = candidates_to_lds<NT>(a, bh, n, chunk, k_eff, ws, sc);
     const void* srow =
         scores != nullptr ? static_cast<const char*>(scores) + static_cast<long long>(bh) * a.Nmax * 4 : nullptr;
-    const int path = select_range<NT>(a, bh, n, k_eff, chunk, srow, scores_int != 0, ws, r0, r1, irow,
-                                      rows, sc, &M);
+    const int path = select_from_candidates<NT>(a, bh, n, k_eff, chunk, M, h_theta, h_shift, srow,
+                                                scores_int != 0, ws, r0, r1, nullptr, rows, sc);
     nrows = max(0, min(k_eff, r1) - r0);
     if (split == 0 && t == 0) {
       a.heads[bh].path = static_cast<uint32_t>(path);
@@ -137,24 +245,18 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
 
   float qv[GMAX][EPL];
   uint32_t qp[GMAX][EPL / 2];
-  {
-    typename RowLd<T, EPL>::raw qr[GMAX];
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g)
-      if (g < G) qr[g] = RowLd<T, EPL>::load(q + (static_cast<long long>(b) * Hq + h * G + g) * D + sub * EPL);
+  for (int g = 0; g < GMAX; ++g) {
+    if constexpr (PK) {
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if constexpr (PK) {
+      for (int w = 0; w < EPL / 2; ++w) qp[g][w] = g < G ? RowLd<T, EPL>::word(qr[g], w) : 0u;
+    } else if (g < G) {
+      RowLd<T, EPL>::cvt(qr[g], qv[g]);
 #pragma unroll
-        for (int w = 0; w < EPL / 2; ++w) qp[g][w] = g < G ? RowLd<T, EPL>::word(qr[g], w) : 0u;
-      } else if (g < G) {
-        RowLd<T, EPL>::cvt(qr[g], qv[g]);
+      for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
+    } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[g][e] *= scale_log2;
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
-      }
+      for (int e = 0; e < EPL; ++e) qv[g][e] = 0.f;
     }
   }
   float m[GMAX], l[GMAX], o[GMAX][EPL];
@@ -166,24 +268,23 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
   }
   const long long kvb = static_cast<long long>(bh) * a.Nmax;
-  for (int rb = grp; rb < nrows; rb += NG * U) {
-    // all row loads of the batch issued back to back, without branches: a
-    // row that is absent or out of range reads row 0 of the head (allocated
-    // whenever the head exists) and is skipped below
-    typename RowLd<T, EPL>::raw kr[U], vr[U];
-    bool ok[U];
+  // A batch: rows rb + u*NG (u < U) of this 16-lane group.  All loads of a
+  // batch are issued back to back, without branches: a row that is absent or
+  // out of range reads row 0 of the head (allocated whenever the head
+  // exists) and is masked at use.
+  const auto issue = [&](int rb, Raw (&kr)[U], Raw (&vr)[U], bool (&valid)[U]) {
     const T* kp[U];
     const T* vp[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = rb + u * NG;
       const int j = r < nrows ? rows[r] : -1;
-      ok[u] = j >= 0 && j < n;
-      const int jj = ok[u] ? j : 0;
+      valid[u] = j >= 0 && j < n;
+      const int jj = valid[u] ? j : 0;
       // a shared prefix row, or a row of the sequence's own cache
       const bool pre = !SELECT && jj < a.np;
       const long long off = pre ? (static_cast<long long>(h) * a.np + jj) * D + sub * EPL
-                                : (kvb + (jj - (SELECT ? 0 : (ok[u] ? a.np : 0)))) * D + sub * EPL;
+                                : (kvb + (jj - (SELECT ? 0 : (valid[u] ? a.np : 0)))) * D + sub * EPL;
       kp[u] = (pre ? static_cast<const T*>(a.pk) : K) + off;
       vp[u] = (pre ? static_cast<const T*>(a.pv) : V) + off;
     }
@@ -192,9 +293,15 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
       kr[u] = RowLd<T, EPL>::load(kp[u]);
       vr[u] = RowLd<T, EPL>::load(vp[u]);
     }
-    // scores of the batch's rows for every query head slot (slots past G
-    // hold a zero query and are never written out); an absent row scores -inf
-    float sc[U][GMAX];
+  };
+  // scores of a batch's rows for every query head slot (slots past G hold a
+  // zero query and are never written out; an absent row scores -inf), then
+  // one online-softmax step: the running state of each head is rescaled once
+  // to the batch's new maximum, then the rows are added.  While a head has
+  // seen no row its maximum stays -inf and the exponents are taken against
+  // 0, so that every weight is exactly 0 (never NaN).
+  const auto consume = [&](const Raw (&kr)[U], const Raw (&vr)[U], const bool (&ok)[U]) {
+    float sc2[U][GMAX];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kx[EPL];
@@ -219,25 +326,21 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0x4E, 0xF, 0xF, true));
         s += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), 0xB1, 0xF, 0xF, true));
         if constexpr (PK) s *= scale_log2;
-        sc[u][g] = ok[u] ? s : -INFINITY;
+        sc2[u][g] = ok[u] ? s : -INFINITY;
       }
     }
-    // one online-softmax step per batch: the running state of each head is
-    // rescaled once to the batch's new maximum, then the rows are added.
-    // While a head has seen no row its maximum stays -inf and the exponents
-    // are taken against 0, so that every weight is exactly 0 (never NaN).
     float pw[U][GMAX];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
       float mx = m[g];
 #pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc2[u][g]);
       const float ms = mx == -INFINITY ? 0.f : mx;
       const float c = __builtin_amdgcn_exp2f(m[g] - ms);
       float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        pw[u][g] = __builtin_amdgcn_exp2f(sc[u][g] - ms);
+        pw[u][g] = __builtin_amdgcn_exp2f(sc2[u][g] - ms);
         ps += pw[u][g];
       }
       l[g] = l[g] * c + ps;
@@ -253,6 +356,31 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
       for (int g = 0; g < GMAX; ++g)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[g][e] += pw[u][g] * vx[e];
+    }
+  };
+
+  // Batches of BR rows.  Where the registers hold two batches, the next one
+  // is in flight while one is consumed; where two workgroups share a CU (or
+  // the registers hold one batch), batches go one at a time.
+  constexpr int BR = NG * U;
+  constexpr bool PIPE = !kAttOcc2<T, GMAX, SELECT> &&
+                        (sizeof(T) == 2 ? !(D == 128 && GMAX == 8) : (D == 64 || GMAX <= 2));
+  if constexpr (PIPE) {
+    Raw ka[U], va[U], kb[U], vb[U];
+    bool oka[U], okb[U];
+    if (nrows > 0) issue(grp, ka, va, oka);
+    for (int b0 = 0; b0 < nrows; b0 += 2 * BR) {
+      if (b0 + BR < nrows) issue(b0 + BR + grp, kb, vb, okb);
+      consume(ka, va, oka);
+      if (b0 + 2 * BR < nrows) issue(b0 + 2 * BR + grp, ka, va, oka);
+      if (b0 + BR < nrows) consume(kb, vb, okb);
+    }
+  } else {
+    for (int b0 = 0; b0 < nrows; b0 += BR) {
+      Raw ka[U], va[U];
+      bool oka[U];
+      issue(b0 + grp, ka, va, oka);
+      consume(ka, va, oka);
     }
   }
   // merge the row groups of a wave (lanes 16 apart, then 32 apart), then the
@@ -300,6 +428,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     }
   }
   __syncthreads();
+  const long long qh0 = static_cast<long long>(b) * Hq + h * G;  // the group's first query head
   for (int i = t; i < G * D; i += NT) {
     const int g = i / D, c = i % D;
     float mm = -INFINITY;
@@ -312,13 +441,24 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
         oo += red_o[(w * GMAX + g) * D + c] * wt;
       }
     }
-    const long long pi = (static_cast<long long>(b) * Hq + h * G + g) * nsplit + split;
-    a.part_o[pi * D + c] = oo;
-    if (c == 0) {
-      a.part_ml[pi * 2] = mm;
-      a.part_ml[pi * 2 + 1] = ll;
+    const long long pi = (qh0 + g) * nsplit + split;
+    if (SELECT) {  // read by the merging split of the head (merge_splits)
+      store_dev(a.part_o + pi * D + c, oo);
+      if (c == 0) {
+        store_dev(a.part_ml + pi * 2, mm);
+        store_dev(a.part_ml + pi * 2 + 1, ll);
+      }
+    } else {
+      a.part_o[pi * D + c] = oo;
+      if (c == 0) {
+        a.part_ml[pi * 2] = mm;
+        a.part_ml[pi * 2 + 1] = ll;
+      }
     }
   }
+  if (SELECT)  // the split's part of the ascending index row, -1 past k_eff
+    for (int i = r0 + t; i < r1; i += NT) irow[i] = i - r0 < nrows ? rows[i - r0] : -1;
+  if constexpr (SELECT) merge_splits<D, NT>(a, bh, qh0, G, nsplit, out, lse, sm, sc);
 }
 
 // Merge the split states of one query head.  grid (B*Hq), 256 threads.
@@ -482,7 +622,7 @@ static hipError_t lds_limit(K kern, size_t bytes) {
 template <typename T, int D, bool SELECT>
 static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const void* q, const void* K,
                                   const void* V, int32_t* idx, const void* scores, int scores_int,
-                                  int chunk, float sl2, hipStream_t st) {
+                                  int chunk, float sl2, float* out, float* lse, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
   dim3 grid(a_nsplit(a), s.B * s.Hkv);
   const size_t smem = attend_smem(a.nchunks, a.rps);
@@ -493,7 +633,7 @@ static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const 
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL(kern, grid, dim3(kAttNT), smem, st, static_cast<const T*>(q),            \
                        static_cast<const T*>(K), static_cast<const T*>(V), idx, scores,         \
-                       scores_int, chunk, s.seq_lens, sl2, a);                                  \
+                       scores_int, chunk, s.seq_lens, sl2, a, out, lse);                        \
   } while (0)
   if (G <= 1) HST_ATT(1);
   else if (G <= 2) HST_ATT(2);
@@ -518,20 +658,20 @@ hipError_t launch_attend(const hst_shape& s, const FusedArgs& a, const void* q, 
   hipError_t e;
   if (s.kv_dtype == HST_F32) {
     if (s.d == 64)
-      e = select ? launch_attend_t<float, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
-                 : launch_attend_t<float, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+      e = select ? launch_attend_t<float, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st)
+                 : launch_attend_t<float, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st);
     else
-      e = select ? launch_attend_t<float, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
-                 : launch_attend_t<float, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+      e = select ? launch_attend_t<float, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st)
+                 : launch_attend_t<float, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st);
   } else {
     if (s.d == 64)
-      e = select ? launch_attend_t<bf16, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
-                 : launch_attend_t<bf16, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+      e = select ? launch_attend_t<bf16, 64, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st)
+                 : launch_attend_t<bf16, 64, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st);
     else
-      e = select ? launch_attend_t<bf16, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st)
-                 : launch_attend_t<bf16, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, st);
+      e = select ? launch_attend_t<bf16, 128, true>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st)
+                 : launch_attend_t<bf16, 128, false>(s, a, q, K, V, idx, scores, scores_int, chunk, sl2, out, lse, st);
   }
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || select) return e;
   return s.d == 64 ? launch_combine_t<64>(s, a, out, lse, st) : launch_combine_t<128>(s, a, out, lse, st);
 }
 

@@ -87,7 +87,6 @@ __device__ __forceinline__ void copy_to_lds(u32x4* __restrict__ dst, const u32x4
   }
 }
 
-constexpr int kSelCap = 8192;  // candidates a workgroup selects from in LDS
 
 // Candidate slots of one head seen as one array in index order; entry i lives
 // in the chunk c with offs[c] <= i < offs[c+1].
@@ -159,7 +158,8 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 template <int NT, int PER>
 __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, int max_pass,
                                   uint32_t* hist, BlockScratch<NT>& sc, uint32_t& mask,
-                                  uint32_t& prefix, int& krem, uint32_t* kmin = nullptr) {
+                                  uint32_t& prefix, int& krem, uint32_t* kmin = nullptr,
+                                  uint32_t* kmax = nullptr) {
   const int t = threadIdx.x;
   mask = 0u;
   prefix = 0u;
@@ -173,6 +173,7 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
     }
   block_minmax<NT>(mn, mx, sc);
   if (kmin != nullptr) *kmin = mn;
+  if (kmax != nullptr) *kmax = mx;
   if (mn == mx) return;  // every key equal: mask 0 selects krem of them
   const int hb = 31 - __clz(static_cast<int>(mn ^ mx));
   mask = hb == 31 ? 0u : ~((1u << (hb + 1)) - 1u);
@@ -234,12 +235,18 @@ __device__ void radix_select_regs(const uint32_t (&key)[PER], int count, int k, 
   }
 }
 
-// The head's histogram of candidate keys, built by the filtering scan: key c
-// (always >= theta) is counted in bin min(kHistBins - 1, (c - theta) >> shift).
+// Binning of a selection's candidate histogram: key c falls in bin
+// min(kHistBins - 1, (c - theta) >> shift), and keys below theta (a chunk
+// that filtered with a lower threshold) in bin 0, so bins keep the key order.
 struct HistInfo {
   uint32_t theta;
   int shift;
-  bool ok;  // every chunk counted its candidates under the published threshold
+  bool ok;
+  __device__ __forceinline__ int bin(uint32_t c) const {
+    if (c < theta) return 0;
+    const uint32_t b = (c - theta) >> shift;
+    return b < static_cast<uint32_t>(kHistBins - 1) ? static_cast<int>(b) : kHistBins - 1;
+  }
 };
 
 // Bin of the k-th largest candidate from the histogram, counted from the top
@@ -249,7 +256,7 @@ struct HistInfo {
 // usable); otherwise bstar is the bin holding rank k, krem how many of its
 // entries complete the k largest, cnt its size.  All threads call.
 template <int NT>
-__device__ bool hist_boundary(const uint32_t (&hb)[kHistBins / NT], int M, int k, BlockScratch<NT>& sc,
+__device__ __forceinline__ bool hist_boundary(const uint32_t (&hb)[kHistBins / NT], int M, int k, BlockScratch<NT>& sc,
                               int& bstar, int& krem, int& cnt) {
   constexpr int BPT = kHistBins / NT;
   constexpr int NW = NT / 64;
@@ -293,176 +300,276 @@ __device__ bool hist_boundary(const uint32_t (&hb)[kHistBins / NT], int M, int k
   return true;
 }
 
-// Ranks the entries of the wave-held keys that satisfy `in` (at most
-// kRankBin of them; cnt in total) by (key descending, position ascending) and
-// returns the key of the krem-th and how many entries equal to it are taken
-// (rank krem - 1 among the bin's entries).  bl: LDS, >= kRankBin uint2.
+// Ranks the entries of the wave-held keys that satisfy `in` (cnt of them;
+// at most kRankBin) by (key descending, position ascending) and returns the
+// key and the position of the krem-th (rank krem - 1 among the entries).
+// The entries equal to that key that are taken are exactly those at or
+// before that position.  bl: LDS, >= max(kRankBin, NT) uint2.
+//  * cnt <= 64 (the usual case): one ballot pass writes each wave's entries
+//    to its own 64-entry segment of bl; then lane j of wave 0 takes the j-th
+//    entry over the segments and counts the entries ranked before it, reading
+//    the others from their lanes (no LDS round trip per comparison).
+//  * otherwise: a ballot count per wave, one slot reservation per wave and a
+//    second pass that writes the entries; thread j < cnt compares entry j
+//    with all of them from LDS.
 constexpr int kRankBin = 256;
 template <int NT, int PERW, class In>
-__device__ void rank_entries(const uint32_t (&key)[PERW], int lo, int hi, const In& in, int cnt, int krem,
-                             uint2* bl, BlockScratch<NT>& sc, uint32_t& kstar, int& eq_taken) {
-  const int t = threadIdx.x, lane = t & 63;
-  if (t == 0) sc.found[3] = 0;
-  __syncthreads();
-  {
-    // this wave's entries, then one slot reservation per wave
+__device__ __forceinline__ void rank_entries(const uint32_t (&key)[PERW], int lo, int hi, const In& in, int cnt,
+                                             int krem, uint2* bl, BlockScratch<NT>& sc, uint32_t& kstar,
+                                             int& cut) {
+  constexpr int NW = NT / 64;
+  static_assert(NW * 64 <= 1024, "wave segments fit the histogram region");
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (cnt <= 64) {  // uniform
+    uint2* seg = bl + wave * 64;
     int nw = 0;
-#pragma unroll
-    for (int u = 0; u < PERW; ++u) nw += __popcll(__ballot(lo + 64 * u + lane < hi && in(key[u])));
-    int base = 0;
-    if (lane == 0 && nw > 0) base = atomicAdd(&sc.found[3], nw);
-    base = __shfl(base, 0, 64);
 #pragma unroll
     for (int u = 0; u < PERW; ++u) {
       const int p = lo + 64 * u + lane;
       const bool ok = p < hi && in(key[u]);
       const unsigned long long b = __ballot(ok);
-      const int slot = base + lanes_below(b);
-      if (ok && slot < kRankBin) bl[slot] = make_uint2(key[u], static_cast<uint32_t>(p));
-      base += __popcll(b);
+      if (ok) seg[nw + lanes_below(b)] = make_uint2(key[u], static_cast<uint32_t>(p));
+      nw += __popcll(b);
     }
-  }
-  __syncthreads();
-  const int nb = cnt < kRankBin ? cnt : kRankBin;
-  if (t < nb) {
-    const uint2 me = bl[t];
-    int gt = 0, eq = 0;
-    for (int j = 0; j < nb; ++j) {
-      const uint2 o = bl[j];
-      gt += o.x > me.x ? 1 : 0;
-      eq += (o.x == me.x && o.y < me.y) ? 1 : 0;
+    if (lane == 0) sc.red[1][wave] = static_cast<uint32_t>(nw);
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0, src = -1;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = static_cast<int>(sc.red[1][w]);
+        if (src < 0 && lane < base + c) src = w * 64 + lane - base;
+        base += c;
+      }
+      const uint2 me = src >= 0 ? bl[src] : make_uint2(0u, 0xffffffffu);
+      int before = 0;
+      for (int j = 0; j < cnt; ++j) {
+        const uint32_t ok = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.x), j));
+        const uint32_t op = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.y), j));
+        before += (ok > me.x || (ok == me.x && op < me.y)) ? 1 : 0;
+      }
+      if (src >= 0 && before == krem - 1) {
+        sc.found[0] = static_cast<int>(me.x);
+        sc.found[1] = static_cast<int>(me.y);
+      }
     }
-    if (gt + eq == krem - 1) {
-      sc.found[0] = static_cast<int>(me.x);
-      sc.found[1] = eq + 1;
+  } else {
+    if (t == 0) sc.found[3] = 0;
+    __syncthreads();
+    {
+      // this wave's entries, then one slot reservation per wave
+      int nw = 0;
+#pragma unroll
+      for (int u = 0; u < PERW; ++u) nw += __popcll(__ballot(lo + 64 * u + lane < hi && in(key[u])));
+      int base = 0;
+      if (lane == 0 && nw > 0) base = atomicAdd(&sc.found[3], nw);
+      base = __shfl(base, 0, 64);
+#pragma unroll
+      for (int u = 0; u < PERW; ++u) {
+        const int p = lo + 64 * u + lane;
+        const bool ok = p < hi && in(key[u]);
+        const unsigned long long b = __ballot(ok);
+        const int slot = base + lanes_below(b);
+        if (ok && slot < kRankBin) bl[slot] = make_uint2(key[u], static_cast<uint32_t>(p));
+        base += __popcll(b);
+      }
+    }
+    __syncthreads();
+    const int nb = cnt < kRankBin ? cnt : kRankBin;
+    if (t < nb) {
+      const uint2 me = bl[t];
+      int gt = 0, eq = 0;
+      // four entries per step, their loads issued together (an entry past the
+      // end is read as the last one and not counted)
+      for (int j0 = 0; j0 < nb; j0 += 4) {
+        uint2 o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = bl[j0 + u < nb ? j0 + u : nb - 1];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + u < nb) {
+            gt += o[u].x > me.x ? 1 : 0;
+            eq += (o[u].x == me.x && o[u].y < me.y) ? 1 : 0;
+          }
+      }
+      if (gt + eq == krem - 1) {  // the krem-th entry: its key and position
+        sc.found[0] = static_cast<int>(me.x);
+        sc.found[1] = static_cast<int>(me.y);
+      }
     }
   }
   __syncthreads();
   kstar = static_cast<uint32_t>(sc.found[0]);
-  eq_taken = sc.found[1];
+  cut = sc.found[1];
   __syncthreads();
 }
 
-// Counts and stable compaction under the masked-prefix rule (selected iff
-// (key & mask) > prefix, or == prefix among the first krem such entries in
-// position order), from ballots over the wave-held keys: writes the
+// Stable compaction under the rule (mask, prefix, cut): the entry at
+// position p with masked key m = key & mask is selected iff m > prefix, or
+// m == prefix and p <= cut.  From ballots over the wave-held keys: writes the
 // selected indices at output positions [r0, r1).
 template <int NT, int PERW, class Idx>
-__device__ void compact_regs(const uint32_t (&key)[PERW], int lo, int hi, const Idx& candi, uint32_t mask,
-                             uint32_t prefix, int krem, int r0, int r1, int32_t* out_g, int32_t* out_l,
-                             BlockScratch<NT>& sc) {
+__device__ __forceinline__ void compact_regs(const uint32_t (&key)[PERW], int lo, int hi, const Idx& candi,
+                                             uint32_t mask, uint32_t prefix, int cut, int r0, int r1,
+                                             int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int gtc = 0, eqc = 0;
-#pragma unroll
-  for (int u = 0; u < PERW; ++u) {
-    const bool ok = lo + 64 * u + lane < hi;
+  const auto taken = [&](int u) {
+    const int p = lo + 64 * u + lane;
     const uint32_t m = key[u] & mask;
-    gtc += __popcll(__ballot(ok && m > prefix));
-    eqc += __popcll(__ballot(ok && m == prefix));
-  }
-  if (lane == 0) {
-    sc.red[0][wave] = static_cast<uint32_t>(gtc);
-    sc.red[1][wave] = static_cast<uint32_t>(eqc);
-  }
+    return p < hi && (m > prefix || (m == prefix && p <= cut));
+  };
+  int selc = 0;
+#pragma unroll
+  for (int u = 0; u < PERW; ++u) selc += __popcll(__ballot(taken(u)));
+  if (lane == 0) sc.red[0][wave] = static_cast<uint32_t>(selc);
   __syncthreads();
-  int gt_before = 0, eq_run = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += static_cast<int>(sc.red[0][w]);
-    eq_run += static_cast<int>(sc.red[1][w]);
+  int run = 0;
+  {
+    uint32_t g[NW];  // every wave's count, loads issued together
+#pragma unroll
+    for (int w = 0; w < NW; ++w) g[w] = sc.red[0][w];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) run += static_cast<int>(g[w]);
   }
   __syncthreads();  // sc is reused by the caller
-  int run = gt_before + min(eq_run, krem);
 #pragma unroll
   for (int u = 0; u < PERW; ++u) {
-    const int p = lo + 64 * u + lane;
-    const bool ok = p < hi;
-    const uint32_t m = key[u] & mask;
-    const bool top = ok && m > prefix;
-    const bool eq = ok && m == prefix;
-    const unsigned long long eqb = __ballot(eq);
-    const bool sel = top || (eq && eq_run + lanes_below(eqb) < krem);
+    const bool sel = taken(u);
     const unsigned long long selb = __ballot(sel);
     const int pos = run + lanes_below(selb);
     if (sel && pos >= r0 && pos < r1) {
-      const int32_t v = static_cast<int32_t>(candi[p]);
+      const int32_t v = static_cast<int32_t>(candi[lo + 64 * u + lane]);
       if (out_g != nullptr) out_g[pos] = v;
       if (out_l != nullptr) out_l[pos - r0] = v;
     }
     run += __popcll(selb);
-    eq_run += __popcll(eqb);
   }
 }
 
-// Exact selection over M <= NT * PERW candidates held in LDS in index order,
-// on keys held in registers: wave w holds the entries at positions
-// [lo_w, hi_w) (lane l's entry u at lo_w + 64u + l), the order in which the
-// compaction walks them, so the counts and the compaction come from ballots
-// over registers instead of a second pass over LDS.
-//  * With the head's candidate histogram (HIST): one block scan over the bins
-//    finds the bin of the k-th largest key.  If that bin is taken whole, or
-//    holds a single key value (shift 0), the rule follows at once; otherwise
-//    its entries (at most kRankBin) are ranked directly.
+// Position (in index order) of the krem-th entry among those whose masked
+// key equals prefix (-1 when krem is 0); the wave-held keys as
+// select_rule_core holds them.  All threads call.
+template <int NT, int PERW>
+__device__ __forceinline__ int rule_cut_position(const uint32_t (&key)[PERW], int lo, int hi, uint32_t mask,
+                                                 uint32_t prefix, int krem, BlockScratch<NT>& sc) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (krem <= 0) return -1;  // uniform
+  int eqc = 0;
+#pragma unroll
+  for (int u = 0; u < PERW; ++u)
+    eqc += __popcll(__ballot(lo + 64 * u + lane < hi && (key[u] & mask) == prefix));
+  if (lane == 0) sc.red[1][wave] = static_cast<uint32_t>(eqc);
+  __syncthreads();
+  int before = 0;
+  {
+    uint32_t e[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) e[w] = sc.red[1][w];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) before += static_cast<int>(e[w]);
+  }
+  if (before < krem && krem <= before + eqc) {  // this wave holds the krem-th
+    int run = before;
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) {
+      const int p = lo + 64 * u + lane;
+      const bool eq = p < hi && (key[u] & mask) == prefix;
+      const unsigned long long b = __ballot(eq);
+      const int n = __popcll(b);
+      if (run < krem && krem <= run + n && eq && run + lanes_below(b) == krem - 1) sc.found[0] = p;
+      run += n;
+    }
+  }
+  __syncthreads();
+  const int cut = sc.found[0];
+  __syncthreads();  // sc is reused by the caller
+  return cut;
+}
+
+// The exact top-k rule over M <= NT * PERW candidates held in LDS in index
+// order, as (mask, prefix, cut): the entry at position p with masked key
+// m = key & mask is among the k first in the order (key descending, position
+// ascending) iff m > prefix, or m == prefix and p <= cut.  The keys are left
+// in registers: wave w holds positions [lo, hi) (lane l's entry u at
+// lo + 64u + l), the order a compaction walks them in.
+//  * With a binning from the head's threshold (HIST): the keys go into an LDS
+//    histogram as they are loaded, one block scan over the bins finds the bin
+//    of the k-th key, and the rule follows at once when that bin is taken
+//    whole; otherwise the bin's entries (at most kRankBin) are ranked
+//    directly, which gives the k-th key and its position.  A bin of one key
+//    value (shift 0) needs only the position of its kb-th entry.
 //  * Otherwise, or when the bin is too full: radix passes of up to 11 bits
 //    below the keys' common prefix narrow the bin of the k-th largest key
 //    until it holds at most kRankBin entries, which are then ranked.
-// Writes the selected indices at output positions [r0, r1).  hist: 2048
-// words of LDS.  candi: the entries' key indices, anything indexable by
-// position (an LDS array, or a map from positions to indices).
-template <int NT, int PERW, class Idx, bool HIST>
-__device__ void select_lds_core(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
-                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc,
-                                const uint32_t (&hb)[kHistBins / NT], const HistInfo& hi_info) {
+// hist: 2048 words of LDS.
+template <int NT, int PERW, bool HIST>
+__device__ __forceinline__ void select_rule_core(const uint32_t* candk, int M, int k, uint32_t* hist,
+                                                 BlockScratch<NT>& sc, const HistInfo& hi_info,
+                                                 uint32_t (&key)[PERW], int& lo, int& hi, uint32_t& mask,
+                                                 uint32_t& prefix, int& cut) {
   constexpr int NW = NT / 64;
   constexpr int MAXPER = (2048 + NT - 1) / NT;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int span = ((M + NW - 1) / NW + 63) & ~63;
-  const int lo = min(M, wave * span), hi = min(M, lo + span);
-  uint32_t key[PERW];
-#pragma unroll
-  for (int u = 0; u < PERW; ++u) {
-    const int p = lo + 64 * u + lane;
-    key[u] = p < hi ? candk[p] : 0u;
-  }
-  // rule: selected iff (key & mask) > prefix, or (key & mask) == prefix among
-  // the first krem such entries in index order
-  uint32_t mask = 0u, prefix = 0u;
-  int krem = k < M ? k : M;
-  bool done = k >= M;
+  lo = min(M, wave * span);
+  hi = min(M, lo + span);
+  mask = 0u;
+  prefix = 0u;
+  cut = 0x7fffffff;
+  bool done = k >= M;  // every entry taken
   if (HIST && !done && hi_info.ok) {
+    constexpr int BPT = kHistBins / NT;
+    for (int i = t; i < kHistBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) {
+      const int p = lo + 64 * u + lane;
+      key[u] = p < hi ? candk[p] : 0u;
+      if (p < hi) atomicAdd(&hist[hi_info.bin(key[u])], 1u);
+    }
+    __syncthreads();
+    uint32_t hb[BPT];  // this thread's bins, from the top bin down
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) hb[i] = hist[kHistBins - 1 - (t * BPT + i)];
     int bstar, kb, cnt;
-    if (hist_boundary<NT>(hb, M, k, sc, bstar, kb, cnt)) {
+    if (hist_boundary<NT>(hb, M, k, sc, bstar, kb, cnt) && bstar >= 1) {
       const uint32_t th = hi_info.theta;
       const int sh = hi_info.shift;
       const unsigned long long klo = static_cast<unsigned long long>(th) +
                                      (static_cast<unsigned long long>(bstar) << sh);
-      if (kb == cnt && klo >= 1ull && klo <= 0xffffffffull) {
+      if (kb == cnt && klo <= 0xffffffffull) {
         // the whole bin is taken: every key >= its lower edge
         mask = 0xffffffffu;
         prefix = static_cast<uint32_t>(klo - 1ull);
-        krem = 0;
+        cut = -1;
         done = true;
       } else if (sh == 0 && bstar < kHistBins - 1) {
         // the bin is one key value: its first kb entries in index order
         mask = 0xffffffffu;
         prefix = static_cast<uint32_t>(klo);
-        krem = kb;
+        cut = rule_cut_position<NT, PERW>(key, lo, hi, mask, prefix, kb, sc);
         done = true;
       } else if (cnt <= kRankBin) {
-        const auto in_bin = [th, sh, bstar](uint32_t c) {
-          const uint32_t b = (c - th) >> sh;
-          return static_cast<int>(b < static_cast<uint32_t>(kHistBins - 1) ? b : kHistBins - 1) == bstar;
-        };
-        uint32_t kstar;
-        int eqt;
-        rank_entries<NT, PERW>(key, lo, hi, in_bin, cnt, kb, reinterpret_cast<uint2*>(hist), sc, kstar, eqt);
+        const HistInfo hh = hi_info;
+        const auto in_bin = [hh, bstar](uint32_t c) { return hh.bin(c) == bstar; };
+        rank_entries<NT, PERW>(key, lo, hi, in_bin, cnt, kb, reinterpret_cast<uint2*>(hist), sc, prefix, cut);
         mask = 0xffffffffu;
-        prefix = kstar;
-        krem = eqt;
         done = true;
       }
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) {
+      const int p = lo + 64 * u + lane;
+      key[u] = p < hi ? candk[p] : 0u;
+    }
   }
   if (!done) {
+    int krem = k;
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int u = 0; u < PERW; ++u)
@@ -471,6 +578,7 @@ __device__ void select_lds_core(const uint32_t* candk, const Idx& candi, int M, 
         mx = max(mx, key[u]);
       }
     block_minmax<NT>(mn, mx, sc);
+    bool resolved = false;
     if (mn != mx) {
       const int hb_ = 31 - __clz(static_cast<int>(mn ^ mx));
       mask = hb_ == 31 ? 0u : ~((1u << (hb_ + 1)) - 1u);
@@ -526,44 +634,58 @@ __device__ void select_lds_core(const uint32_t* candk, const Idx& candi, int M, 
         mask |= dm << sh;
         lob = sh;
         __syncthreads();  // every thread has read sc.found and its bins
-        if (cnt == krem || lob == 0) break;  // the whole bin is taken, or every bit is resolved
+        if (cnt == krem) {  // the whole bin is taken
+          cut = 0x7fffffff;
+          resolved = true;
+          break;
+        }
+        if (lob == 0) break;  // every bit is resolved: the first krem equal keys
         if (cnt <= kRankBin) {
           const uint32_t pm = mask, pp = prefix;
-          uint32_t kstar;
-          int eqt;
           rank_entries<NT, PERW>(key, lo, hi, [pm, pp](uint32_t c) { return (c & pm) == pp; }, cnt, krem,
-                                 reinterpret_cast<uint2*>(hist), sc, kstar, eqt);
-          // the k-th key is now fully resolved: take the keys above it and the
-          // first eqt keys equal to it (index order)
-          prefix = kstar;
+                                 reinterpret_cast<uint2*>(hist), sc, prefix, cut);
           mask = 0xffffffffu;
-          krem = eqt;
+          resolved = true;
           break;
         }
       }
     }
+    // all keys equal, or every bit resolved: the first krem equal keys
+    if (!resolved) cut = rule_cut_position<NT, PERW>(key, lo, hi, mask, prefix, krem, sc);
   }
-  __syncthreads();  // sc.found is read above; sc.red is written below
-  compact_regs<NT, PERW>(key, lo, hi, candi, mask, prefix, krem, r0, r1, out_g, out_l, sc);
+  __syncthreads();  // sc.found is read above; sc.red may be written next
+}
+
+// Exact selection over M <= NT * PERW candidates held in LDS in index order:
+// the rule of select_rule_core, then the stable compaction of compact_regs,
+// which writes the selected indices at output positions [r0, r1).
+template <int NT, int PERW, class Idx, bool HIST>
+__device__ void select_lds_core(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
+                                int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc,
+                                const HistInfo& hi_info) {
+  uint32_t key[PERW], mask, prefix;
+  int lo, hi, cut;
+  select_rule_core<NT, PERW, HIST>(candk, M, k, hist, sc, hi_info, key, lo, hi, mask, prefix, cut);
+  compact_regs<NT, PERW>(key, lo, hi, candi, mask, prefix, cut, r0, r1, out_g, out_l, sc);
 }
 
 template <int NT, int PERW, class Idx>
 __device__ void select_lds_regs(const uint32_t* candk, const Idx& candi, int M, int k, int r0, int r1,
                                 int32_t* out_g, int32_t* out_l, uint32_t* hist, BlockScratch<NT>& sc) {
-  const uint32_t hb[kHistBins / NT] = {};
-  select_lds_core<NT, PERW, Idx, false>(candk, candi, M, k, r0, r1, out_g, out_l, hist, sc, hb,
+  select_lds_core<NT, PERW, Idx, false>(candk, candi, M, k, r0, r1, out_g, out_l, hist, sc,
                                         HistInfo{0u, 0, false});
 }
 
 // Lower bound of the r-th largest (1 <= r <= count) of the keys held PER per
 // thread: two 11-bit radix passes below the common prefix of the keys, then
 // the low edge of the bin holding rank r (the common key if all are equal).
+// kmax (optional) receives the largest key.
 template <int NT, int PER>
 __device__ uint32_t rank_lower_bound_regs(const uint32_t (&key)[PER], int count, int r, uint32_t* hist,
-                                          BlockScratch<NT>& sc) {
+                                          BlockScratch<NT>& sc, uint32_t* kmax = nullptr) {
   uint32_t mask, prefix, kmin;
   int krem;
-  radix_select_regs<NT, PER>(key, count, r, 2, hist, sc, mask, prefix, krem, &kmin);
+  radix_select_regs<NT, PER>(key, count, r, 2, hist, sc, mask, prefix, krem, &kmin, kmax);
   return mask == 0u ? kmin : prefix;
 }
 
@@ -617,40 +739,23 @@ __device__ void select_all_keys(const Src& src, int n, int k_eff, int r0, int r1
   block_compact_range<NT>(src, n, rule, r0, r1, out_g, out_l, sc);
 }
 
-// The head's exact top-k (k_eff keys, ties to the lower index) from the
-// candidate slots the scan wrote.  Writes the selected indices at output
-// positions [r0, r1) and -1 at positions in [max(r0, k_eff), r1) of out_g.
-// Returns the selection path taken:
-//   0: candidates in LDS (the head's candidate histogram gives the bin of the
-//      k-th key; radix passes only when it cannot);
-//   1: more candidates than LDS holds: selected from the slots in HBM;
-//   2: fewer than k_eff keys passed the threshold: every key, from the given
-//      score row (scores_row) or rescored from the metadata (a.meta).
+// The head's candidate slots as one array in index order: the chunk offsets
+// go to ws.offs (nch + 1 entries) and, when k_need <= M <= kSelCap (M the
+// candidate count, returned), the candidates to ws.candk / ws.candi.  Ends
+// with a barrier.  All threads call.
 template <int NT>
-__device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int chunk,
-                            const void* scores_row, bool scores_int, const SelectScratch& ws,
-                            int r0, int r1, int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc,
-                            int* cand_total) {
+__device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int n, int chunk, int k_need,
+                                 const SelectScratch& ws, BlockScratch<NT>& sc) {
   const int nch = (n + a.span - 1) / a.span;  // chunk c: keys [c*span, (c+1)*span), slots at c*chunk
   const uint32_t* cnt = a.counts + static_cast<long long>(bh) * a.nchunks;
   const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
   constexpr int NW = NT / 64;
-  constexpr int BPT = kHistBins / NT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the first counts, then the histogram bins and the head's threshold, then
-  // the first 128 slots of the first eight chunks of each wave (copied
-  // below), all in flight together: the slot addresses do not depend on the
-  // counts (slots past a chunk's count are read, unused), and the counts,
-  // issued first, arrive without waiting for the rest
+  // the first counts, then the first 128 slots of the first eight chunks of
+  // each wave (copied below), all in flight together: the slot addresses do
+  // not depend on the counts (slots past a chunk's count are read, unused),
+  // and the counts, issued first, arrive without waiting for the slots
   const int cnt0 = static_cast<int>(threadIdx.x) < nch ? static_cast<int>(cnt[threadIdx.x]) : 0;
-  uint32_t hb[BPT];
-  const bool have_hist = a.hist != nullptr;
-  const uint32_t* hrow = have_hist ? a.hist + static_cast<long long>(bh) * kHistBins : nullptr;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i)
-    hb[i] = have_hist ? hrow[kHistBins - 1 - (static_cast<int>(threadIdx.x) * BPT + i)] : 0u;
-  const HeadState& hs = a.heads[bh];
-  const uint32_t h_theta = hs.theta, h_shift = hs.shift, h_bad = have_hist ? hs.hist_bad : 1u;
   // (chunk indices clamped, so the loads are unconditional)
   uint2 pre[8][2];
   const int clast = nch > 0 ? nch - 1 : 0;
@@ -672,46 +777,69 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
   if (threadIdx.x == 0) ws.offs[nch] = run;
   __syncthreads();
   const int M = run;
-  *cand_total = M;
+  if (M >= k_need && M <= kSelCap) {
+    // each wave copies whole chunks (coalesced): eight chunks and sixteen
+    // loads per lane in flight (the first eight already loaded)
+    for (int c0 = wave; c0 < nch; c0 += NW * 8) {
+      uint2 v[8][2];
+      int cn[8], base[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * NW;
+        cn[u] = c < nch ? ws.offs[c + 1] - ws.offs[c] : 0;
+        base[u] = c < nch ? ws.offs[c] : 0;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          if (c0 == wave) v[u][x] = pre[u][x];
+          else if (lane + 64 * x < cn[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+          if (lane + 64 * x < cn[u]) {
+            ws.candk[base[u] + lane + 64 * x] = v[u][x].x;
+            ws.candi[base[u] + lane + 64 * x] = static_cast<int32_t>(v[u][x].y);
+          }
+        const long long c = c0 + u * NW;
+        for (int i = 128 + lane; i < cn[u]; i += 64) {  // chunks with many candidates
+          const uint2 w = slots[c * chunk + i];
+          ws.candk[base[u] + i] = w.x;
+          ws.candi[base[u] + i] = static_cast<int32_t>(w.y);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return M;
+}
+
+// The head's exact top-k (k_eff keys, ties to the lower index) from the M
+// candidates candidates_to_lds prepared.  Writes the selected indices at
+// output positions [r0, r1) and -1 at positions in [max(r0, k_eff), r1) of
+// out_g.  h_theta and h_shift are the head's threshold and histogram shift
+// (read by the caller ahead of its own loads).  Returns the selection path
+// taken:
+//   0: candidates in LDS (a histogram over a binning from the head's
+//      threshold gives the bin of the k-th key; radix passes only when it
+//      cannot);
+//   1: more candidates than LDS holds: selected from the slots in HBM;
+//   2: fewer than k_eff keys passed the threshold: every key, from the given
+//      score row (scores_row) or rescored from the metadata (a.meta).
+template <int NT>
+__device__ __forceinline__ int select_from_candidates(const FusedArgs& a, int bh, int n, int k_eff, int chunk, int M,
+                                      uint32_t h_theta, uint32_t h_shift, const void* scores_row,
+                                      bool scores_int, const SelectScratch& ws, int r0, int r1,
+                                      int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc) {
+  const int nch = (n + a.span - 1) / a.span;
+  const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
   int path = 0;
   if (k_eff > 0) {
     if (M >= k_eff && M <= kSelCap) {
-      // each wave copies whole chunks (coalesced): eight chunks and sixteen
-      // loads per lane in flight (the first eight already loaded)
-      for (int c0 = wave; c0 < nch; c0 += NW * 8) {
-        uint2 v[8][2];
-        int cnt[8], base[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * NW;
-          cnt[u] = c < nch ? ws.offs[c + 1] - ws.offs[c] : 0;
-          base[u] = c < nch ? ws.offs[c] : 0;
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            if (c0 == wave) v[u][x] = pre[u][x];
-            else if (lane + 64 * x < cnt[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-#pragma unroll
-          for (int x = 0; x < 2; ++x)
-            if (lane + 64 * x < cnt[u]) {
-              ws.candk[base[u] + lane + 64 * x] = v[u][x].x;
-              ws.candi[base[u] + lane + 64 * x] = static_cast<int32_t>(v[u][x].y);
-            }
-          const long long c = c0 + u * NW;
-          for (int i = 128 + lane; i < cnt[u]; i += 64) {  // chunks with many candidates
-            const uint2 w = slots[c * chunk + i];
-            ws.candk[base[u] + i] = w.x;
-            ws.candi[base[u] + i] = static_cast<int32_t>(w.y);
-          }
-        }
-      }
-      __syncthreads();
-      const HistInfo hi{h_theta, static_cast<int>(h_shift), h_bad == 0u && h_shift < 32u};
+      const HistInfo hi{h_theta, static_cast<int>(h_shift), h_shift < 32u};
       select_lds_core<NT, kSelCap / NT, const int32_t*, true>(ws.candk, ws.candi, M, k_eff, r0, r1, out_g,
-                                                              out_l, ws.hist, sc, hb, hi);
+                                                              out_l, ws.hist, sc, hi);
     } else if (M >= k_eff) {
       path = 1;
       const SlotSrc src{slots, ws.offs, nch, chunk};
@@ -745,6 +873,19 @@ __device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int ch
     for (int p = max(r0, k_eff) + static_cast<int>(threadIdx.x); p < r1; p += NT) out_g[p] = -1;
   __syncthreads();
   return path;
+}
+
+template <int NT>
+__device__ int select_range(const FusedArgs& a, int bh, int n, int k_eff, int chunk,
+                            const void* scores_row, bool scores_int, const SelectScratch& ws,
+                            int r0, int r1, int32_t* out_g, int32_t* out_l, BlockScratch<NT>& sc,
+                            int* cand_total) {
+  const HeadState& hs = a.heads[bh];
+  const uint32_t h_theta = hs.theta, h_shift = hs.shift;
+  const int M = candidates_to_lds<NT>(a, bh, n, chunk, k_eff, ws, sc);
+  *cand_total = M;
+  return select_from_candidates<NT>(a, bh, n, k_eff, chunk, M, h_theta, h_shift, scores_row, scores_int, ws,
+                                    r0, r1, out_g, out_l, sc);
 }
 
 }  // namespace hst

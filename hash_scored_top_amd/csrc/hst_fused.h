@@ -10,7 +10,8 @@
 namespace hst {
 
 constexpr int kSample = 2048;      // keys sampled per head for the candidate threshold
-constexpr int kHistBins = 2048;    // bins of the per-head histogram of candidate keys
+constexpr int kSelCap = 8192;      // candidates a workgroup selects from in LDS
+constexpr int kHistBins = 2048;    // bins of a selection's histogram of candidate keys
 constexpr int kRunLen = 8;         // the sample is kSample / kRunLen runs of consecutive keys
 constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
 constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
@@ -25,17 +26,17 @@ struct HeadState {
   int32_t n;            // context length
   uint32_t cand_total;  // candidates the scan found (diagnostic)
   uint32_t path;        // selection path: 0 LDS, 1 HBM, 2 every key rescored or read (diagnostic)
-  uint32_t shift;       // histogram bin width: candidate key c is counted in bin
-                        //   min(kHistBins - 1, (c - theta) >> shift)
-  uint64_t thr_word;    // ((0x100 | shift) << 32) | theta once the scan has published it, else 0
-  uint32_t hist_bad;    // nonzero when a chunk filtered without the published threshold
+  uint32_t shift;       // bin width of the selection's candidate histogram: key c >= theta
+                        //   falls in bin min(kHistBins - 1, (c - theta) >> shift)
+  uint64_t thr_word;    // (1 << 32) | theta once the scan has published it, else 0
+  uint32_t arrive;      // attention splits of the head that have written their state
   uint32_t pad[7];
 };
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_hist, off_counts, off_slots,
-      off_part_o, off_part_ml, bytes;
+  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_counts, off_slots, off_part_o,
+      off_part_ml, bytes;
   int chunk;    // candidate slots per scan chunk (the stride of the slot array)
   int nchunks;  // scan chunks per head at the default chunk length (the most there can be)
   int sample, xparts, rps, nsplit, kind;
@@ -53,7 +54,6 @@ struct FusedArgs {
                      //   (soft-LSH: tables of the workgroup; binary codes: its 16 code bits;
                      //   given scores: part 0 holds the order keys' bits)
   float* svn;        // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
-  uint32_t* hist;    // [B*Hkv][kHistBins]: candidate keys per bin (see HeadState::shift)
   uint32_t* counts;  // [B*Hkv][nchunks]
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index), chunk c holding keys [c*span, (c+1)*span)
   float* part_o;     // [B*Hq][nsplit][d]

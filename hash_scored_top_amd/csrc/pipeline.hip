@@ -44,7 +44,6 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
     if (soft) f.off_svn = take(BH * static_cast<size_t>(kSample) * 4);
   }
   if (select) {
-    f.off_hist = take(BH * static_cast<size_t>(kHistBins) * 4);
     f.off_counts = take(BH * f.nchunks * 4);
     f.off_slots = take(BH * f.nchunks * static_cast<size_t>(f.chunk) * 8);
   }
@@ -92,7 +91,6 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
     a.spart = reinterpret_cast<float*>(p + f.off_spart);
     a.svn = reinterpret_cast<float*>(p + f.off_svn);
-    a.hist = f.off_hist != 0 ? reinterpret_cast<uint32_t*>(p + f.off_hist) : nullptr;
     a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
     a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
     a.part_o = reinterpret_cast<float*>(p + f.off_part_o);

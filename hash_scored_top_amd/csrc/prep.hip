@@ -45,21 +45,11 @@ __device__ __forceinline__ int sample_size(const FusedArgs& a, const int32_t* se
   return a.sample > n ? n : a.sample;
 }
 
-// Zeroes the head's threshold word and histogram flag, which the filtering
-// scan publishes and sets, and the head's candidate histogram, which it
-// fills: the gridDim.y workgroups of the head each zero a slice of the bins.
+// Zeroes the head's threshold word, which the filtering scan publishes.
 __device__ __forceinline__ void reset_scan_state(const FusedArgs& a, int bh) {
-  if (a.sample == 0) return;
-  if (blockIdx.y == 0 && threadIdx.x == 0) {
+  if (a.sample != 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     a.heads[bh].thr_word = 0ull;
-    a.heads[bh].hist_bad = 0u;
-  }
-  if (a.hist != nullptr) {
-    const int per = (kHistBins + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
-    const int b0 = static_cast<int>(blockIdx.y) * per;
-    const int b1 = b0 + per < kHistBins ? b0 + per : kHistBins;
-    uint32_t* row = a.hist + static_cast<long long>(bh) * kHistBins;
-    for (int i = b0 + static_cast<int>(threadIdx.x); i < b1; i += static_cast<int>(blockDim.x)) row[i] = 0u;
+    a.heads[bh].arrive = 0u;
   }
 }
 

@@ -39,8 +39,6 @@ template <int NT>
 struct ScanTail {
   BlockScratch<NT> sc;
   uint32_t theta;
-  int shift;    // histogram bin width of the head (see HeadState)
-  int hist_ok;  // the threshold was published: the chunk's candidates go into the histogram
 };
 constexpr int kScanSoftU = 2;        // key batches per lane group in flight (two workgroups fit a CU)
 constexpr int kThetaSpin = 1 << 16;  // polls of the threshold word before falling back
@@ -207,15 +205,13 @@ __device__ __forceinline__ void soft_score_tiles(const S& sco, long long base, i
 
 // The chunk's scores sit in LDS (tile[0..cnt)): write them out (coalesced)
 // when a score row is asked for, and append the keys scoring >= theta, in
-// index order, to the chunk's candidate slots, counting each in its bin of
-// the head's histogram (hist, when non-null): bin min(kHistBins - 1,
-// (key - theta) >> shift).  Returns the candidate count (every thread).
+// index order, to the chunk's candidate slots.  Returns the candidate count
+// (every thread).
 template <int NT, bool KINT>
 __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt, int j0,
                                                    long long base, uint32_t* scores_out,
                                                    uint32_t theta, bool filter, uint2* slot,
-                                                   BlockScratch<NT>& sc, uint32_t* hist = nullptr,
-                                                   int shift = 0) {
+                                                   BlockScratch<NT>& sc) {
   if (scores_out != nullptr)
     for (int i = threadIdx.x; i < cnt; i += NT) scores_out[base + j0 + i] = tile[i];
   if (!filter) return 0;
@@ -240,10 +236,6 @@ __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt
       if (key >= theta) {
         slot[pos++] = make_uint2(key, static_cast<uint32_t>(j0 + i));
         --nc;
-        if (hist != nullptr) {
-          const uint32_t bin = (key - theta) >> shift;
-          atomicAdd(hist + (bin < static_cast<uint32_t>(kHistBins - 1) ? bin : kHistBins - 1), 1u);
-        }
       }
     }
   }
@@ -267,19 +259,8 @@ __device__ __forceinline__ ScanWork scan_work(bool filt, int BH, int nch) {
   return w;
 }
 
-// Rank in a sample of S_eff keys above which the top-k threshold lies with
-// a wide margin (mean - 4 sd of the binomial count - 8, at least 1): with the
-// threshold rank of sample_rank it brackets where the k-th key falls.
-__device__ __forceinline__ int sample_rank_hi(int k, int n, int S_eff) {
-  if (n <= 0 || k <= 0) return 1;
-  const double f = static_cast<double>(k) / n;
-  const double mu = f * S_eff;
-  const double r = floor(mu - 4.0 * sqrt(mu * (1.0 - f)) - 8.0);
-  return r < 1.0 ? 1 : static_cast<int>(r);
-}
-
-// Histogram bin width for candidates keyed from theta up: the bracket
-// [theta, khi] of the k-th key spans fewer than kHistBins / 2 bins.
+// Histogram bin width for candidates keyed from theta up: [theta, khi] (the
+// sample's largest key) spans fewer than kHistBins / 2 bins.
 __device__ __forceinline__ int hist_shift(uint32_t theta, uint32_t khi) {
   const uint32_t d = khi > theta ? khi - theta : 0u;
   int sh = 0;
@@ -289,9 +270,10 @@ __device__ __forceinline__ int hist_shift(uint32_t theta, uint32_t khi) {
 
 // Candidate threshold of head bh: the sample scores are the sums of the
 // parts prep wrote (times the sampled value norm for soft-LSH), and theta is
-// a lower bound of the sample score at a high-margin rank.  The histogram
-// bin width (shift) comes from the sample score at the opposite margin.
-// Every thread of the workgroup calls; tile: kSample words of LDS scratch.
+// a lower bound of the sample score at a high-margin rank.  The bin width of
+// the selection's candidate histogram (shift) spreads [theta, the sample's
+// largest key] over half the bins.  Every thread of the workgroup calls;
+// tile: kSample words of LDS scratch.
 template <int KIND>
 __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, uint32_t* tile,
                                  BlockScratch<kScanNT>& sc, int& shift) {
@@ -331,9 +313,9 @@ __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, u
                                     : order_key_f32(acc * vn[e]);
     }
   }
-  const uint32_t theta = rank_lower_bound_regs<NT, PER>(key, S, r, tile, sc);
-  const uint32_t khi = rank_lower_bound_regs<NT, PER>(key, S, sample_rank_hi(k_eff, n, S), tile, sc);
-  shift = hist_shift(theta, khi);
+  uint32_t kmax = 0u;
+  const uint32_t theta = rank_lower_bound_regs<NT, PER>(key, S, r, tile, sc, &kmax);
+  shift = hist_shift(theta, kmax);
   return theta;
 }
 
@@ -352,17 +334,14 @@ __device__ void theta_publish(const FusedArgs& a, int bh, const int32_t* seq_len
     hs->k_eff = k_eff;
     hs->n = n;
     hs->shift = static_cast<uint32_t>(shift);
-    const uint64_t word = (static_cast<uint64_t>(0x100u | static_cast<uint32_t>(shift)) << 32) | theta;
-    __hip_atomic_store(&hs->thr_word, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hs->thr_word, (1ull << 32) | theta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Chunk workgroup: the head's threshold and bin width, once published (see
-// above).  Past the bounded wait the chunk filters with threshold 0 (every
-// key a candidate) and marks the head's histogram unusable instead of adding
-// to it; the selection then ranks the candidates by radix passes.
-__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanTail<kScanNT>& tl,
-                                               int& shift, bool& hist_ok) {
+// Chunk workgroup: the head's threshold, once published (see above).  Past
+// the bounded wait the chunk filters with threshold 0 (every key a
+// candidate), which leaves the selection exact.
+__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanTail<kScanNT>& tl) {
   if (threadIdx.x == 0) {
     uint64_t v = 0;
     for (int i = 0; i < kThetaSpin; ++i) {
@@ -370,15 +349,9 @@ __device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanT
       if (v >> 32) break;
       __builtin_amdgcn_s_sleep(4);
     }
-    const bool pub = (v >> 32) != 0;
-    tl.theta = pub ? static_cast<uint32_t>(v) : 0u;
-    tl.shift = pub ? static_cast<int>((v >> 32) & 31u) : 0;
-    tl.hist_ok = pub ? 1 : 0;
-    if (!pub) atomicOr(&a.heads[bh].hist_bad, 1u);
+    tl.theta = (v >> 32) ? static_cast<uint32_t>(v) : 0u;
   }
   __syncthreads();
-  shift = tl.shift;
-  hist_ok = tl.hist_ok != 0;
   return tl.theta;
 }
 
@@ -431,14 +404,11 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   __syncthreads();
   soft_score_tiles<NTILES>(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
-  int shift = 0;
-  bool hist_ok = false;
-  const uint32_t theta = filt ? theta_wait(a, bh, tl, shift, hist_ok) : 0u;
+  const uint32_t theta = filt ? theta_wait(a, bh, tl) : 0u;
   uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kSoftCap;
-  uint32_t* hrow = hist_ok ? a.hist + static_cast<long long>(bh) * kHistBins : nullptr;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
-                                                   slot, sc, hrow, shift);
+                                                   slot, sc);
   if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 
@@ -586,13 +556,10 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
     }
   }
   __syncthreads();
-  int shift = 0;
-  bool hist_ok = false;
-  const uint32_t theta = filt ? theta_wait(a, bh, tl, shift, hist_ok) : 0u;
+  const uint32_t theta = filt ? theta_wait(a, bh, tl) : 0u;
   uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kLaneCap;
-  uint32_t* hrow = hist_ok ? a.hist + static_cast<long long>(bh) * kHistBins : nullptr;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
-                                                  slot, sc, hrow, shift);
+                                                  slot, sc);
   if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 
