@@ -170,7 +170,10 @@ __device__ __forceinline__ void merge_splits(const FusedArgs& a, int bh, long lo
   if (t == 0) a.heads[bh].arrive = 0u;
 }
 
-// grid (nsplit, B*Hkv).  Rows outside [0, N_b) are skipped.
+// 1-D grid of nsplit * B*Hkv workgroups: workgroup i takes split s of head
+// bh with xcd_item(i) = bh * nsplit + s, so that the splits of a head run on
+// one XCD and share its L2 (the head's candidate slots, its partial states).
+// Rows outside [0, N_b) are skipped.
 //  * SELECT: every split derives the head's exact selection from the
 //    candidate slots (in LDS when they fit; see select_from_candidates),
 //    keeps the rows of its part [r0, r1) of the ascending index row, attends
@@ -207,9 +210,10 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
   int* offs = reinterpret_cast<int*>(sm + 65536 + 8192);
   int32_t* rows = reinterpret_cast<int32_t*>(sm + 65536 + 8192 + (nchunks + 1) * 4);
   const int Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+  const int nsplit = a.nsplit;
+  const int item = xcd_item(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+  const int bh = item / nsplit, split = item % nsplit, b = bh / Hkv, h = bh % Hkv;
   const int n = seq_len(seq_lens, b, a.Nmax) + (SELECT ? 0 : a.np);
-  const int split = blockIdx.x, nsplit = gridDim.x;
   const int r0 = split * a.rps, r1 = min(r0 + a.rps, a.kcap);
   const int t = threadIdx.x, sub = t & 15, grp = t >> 4, lane = t & 63, wave = t >> 6;
   int32_t* irow = idx + static_cast<long long>(bh) * a.kcap;
@@ -624,7 +628,7 @@ static hipError_t launch_attend_t(const hst_shape& s, const FusedArgs& a, const 
                                   const void* V, int32_t* idx, const void* scores, int scores_int,
                                   int chunk, float sl2, float* out, float* lse, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
-  dim3 grid(a_nsplit(a), s.B * s.Hkv);
+  const dim3 grid(static_cast<unsigned>(a_nsplit(a) * s.B * s.Hkv));
   const size_t smem = attend_smem(a.nchunks, a.rps);
 #define HST_ATT(GM)                                                                             \
   do {                                                                                          \

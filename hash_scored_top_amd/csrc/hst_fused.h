@@ -44,6 +44,7 @@ struct FusedLayout {
 
 struct FusedArgs {
   int Hq, Hkv, d, Nmax, L, P;
+  int nbh;  // B * Hkv: the (sequence, kv head) pairs
   double inv_tau;
   int kcap, sample, xparts, nchunks, rps, nsplit, region_bytes;
   int span;  // keys per scan chunk (at most the slot stride; see scan_span)
@@ -71,6 +72,21 @@ struct FusedArgs {
   int np;
 };
 __host__ __device__ inline int a_nsplit(const FusedArgs& a) { return a.nsplit; }
+
+// The dispatcher places workgroup i of a 1-D grid on XCD i % kXcds (each XCD
+// has its own L2).  xcd_item maps workgroup lid of a grid of `total` to a
+// work item so that the workgroups of one XCD take consecutive items: XCD x
+// takes [x*q + min(x, r), ... + q + (x < r)), q = total / kXcds,
+// r = total % kXcds (a bijection of [0, total)).  Items laid out head-major
+// then keep one head's workgroups, and the data they share, on one XCD.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_item(int lid, int total) {
+  const int q = total / kXcds, r = total % kXcds, x = lid % kXcds;
+  return x * q + (x < r ? x : r) + lid / kXcds;
+}
+// Threshold workgroups of a filtering scan, padded to whole XCD rounds so
+// that the chunk workgroups after them start on XCD 0.
+__host__ __device__ inline long long theta_groups(long long nbh) { return (nbh + kXcds - 1) / kXcds * kXcds; }
 __host__ __device__ inline size_t hst_align16(size_t x) { return (x + 15) / 16 * 16; }
 
 FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap);

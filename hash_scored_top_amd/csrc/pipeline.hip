@@ -69,6 +69,7 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
   FusedArgs a{};
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
+  a.nbh = s.B * s.Hkv;
   a.d = s.d;
   a.Nmax = s.Nmax;
   a.L = L;

@@ -244,16 +244,20 @@ __device__ __forceinline__ int scan_chunk_epilogue(const uint32_t* tile, int cnt
 
 
 // Work of a scan workgroup: a chunk of one head, or (filtering) the
-// threshold of one head.
+// threshold of one head.  Filtering grids start with theta_groups(BH)
+// threshold workgroups (those past BH have no work); the chunks of one head
+// then run on one XCD (xcd_item), which fetches the head's table once.
 struct ScanWork {
   int bh, chunk;
-  bool theta;
+  bool theta, none;
 };
 __device__ __forceinline__ ScanWork scan_work(bool filt, int BH, int nch) {
   const int lid = blockIdx.x;
+  const int nth = filt ? static_cast<int>(theta_groups(BH)) : 0;
   ScanWork w;
-  w.theta = filt && lid < BH;
-  const int x = w.theta ? 0 : (filt ? lid - BH : lid);
+  w.theta = lid < nth;
+  w.none = w.theta && lid >= BH;
+  const int x = w.theta ? 0 : xcd_item(lid - nth, BH * nch);
   w.bh = w.theta ? lid : x / nch;
   w.chunk = w.theta ? 0 : x % nch;
   return w;
@@ -375,8 +379,8 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   ScanTail<NT>& tl = *reinterpret_cast<ScanTail<NT>*>(smem_raw + a.region_bytes + kSoftCap * 4);
   BlockScratch<NT>& sc = tl.sc;
   constexpr bool filt = FILTER;
-  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
-  const ScanWork wk = scan_work(filt, BH, nch);
+  const ScanWork wk = scan_work(filt, a.nbh, nch);
+  if (wk.none) return;
   if (filt && wk.theta) {
     theta_publish<kScanSoftFast>(a, wk.bh, seq_lens, k_per_seq, reinterpret_cast<uint32_t*>(tile), sc);
     return;
@@ -495,8 +499,8 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   float* tbl = reinterpret_cast<float*>(smem_raw);
   uint32_t* tile = reinterpret_cast<uint32_t*>(smem_raw + a.region_bytes);
   const bool filt = filter != 0;
-  const int BH = static_cast<int>(gridDim.x) / (nch + (filt ? 1 : 0));
-  const ScanWork wk = scan_work(filt, BH, nch);
+  const ScanWork wk = scan_work(filt, a.nbh, nch);
+  if (wk.none) return;
   if (filt && wk.theta) {
     theta_publish<KIND>(a, wk.bh, seq_lens, k_per_seq, tile, sc);
     return;
@@ -602,9 +606,10 @@ int scan_span(const hst_shape& s, int chunk, int cap, bool filter) {
   const long long R0 = resident_scan_groups();
   const long long nch0 = (N + chunk - 1) / chunk;
   const long long r_chunks = (BH * nch0 + R0 - 1) / R0;        // rounds of the chunks alone
-  const long long r_all = (BH * (nch0 + 1) + R0 - 1) / R0;     // with the threshold workgroups
+  const long long TH = theta_groups(BH);
+  const long long r_all = (BH * nch0 + TH + R0 - 1) / R0;      // with the threshold workgroups
   if (r_all == r_chunks) return chunk;
-  const long long nch = r_chunks * R0 / BH - 1;
+  const long long nch = (r_chunks * R0 - TH) / BH;
   if (nch < 1) return chunk;
   const long long span = ((N + nch - 1) / nch + 63) / 64 * 64;
   return span <= cap ? static_cast<int>(span) : chunk;
@@ -670,7 +675,7 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
                        : 0;
   const int nch = static_cast<int>((s.Nmax + chunk - 1) / chunk);
   const long long BH = static_cast<long long>(s.B) * s.Hkv;
-  const long long nblk = BH * nch + (filter ? BH : 0);
+  const long long nblk = BH * nch + (filter ? theta_groups(BH) : 0);
   if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   dim3 grid(static_cast<unsigned>(nblk));
   const uint8_t* ids = static_cast<const uint8_t*>(src);
