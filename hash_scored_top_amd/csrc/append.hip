@@ -20,7 +20,7 @@ namespace hst {
 constexpr int kAppendNT = 256;
 constexpr int kAppendLanes = 4;                         // lanes per plane
 constexpr int kAppendPlanes = kAppendNT / kAppendLanes;  // planes per workgroup
-constexpr int kAppendExp = 16;  // float64 partials of an exact expansion (LDS, per plane)
+constexpr int kAppendExp = kExactLimbs;  // words of an exact fixed-point sum (LDS, per plane)
 
 __device__ __forceinline__ void load8(const float* __restrict__ p, float (&x)[8]) {
   const u32x4 a = *reinterpret_cast<const u32x4*>(p);
@@ -54,7 +54,7 @@ append_rows_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
   constexpr int kPer = D / kAppendLanes;  // elements per lane
   __shared__ uint32_t bits[kAppendPlanes / 32];
   __shared__ double nsum[kAppendNT / 64];
-  __shared__ double hx[kAppendPlanes * kAppendExp];
+  __shared__ uint64_t hx[kAppendPlanes * kAppendExp];
   const int bh = blockIdx.x, b = bh / Hkv, h = bh % Hkv, y = blockIdx.y;
   const int n = lens[b] < 0 ? 0 : lens[b];
   if (n >= Nmax) return;  // full cache: nothing written, the length stays
@@ -100,7 +100,7 @@ append_rows_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
   if (live && part == 0) {
     const bool bit = fabs(s) > 2.0 * D * 0x1p-53 * sa
                          ? s >= 0.0
-                         : expansion_dot_nonneg_in(wr, kn, D, hx + pl * kAppendExp, kAppendExp);
+                         : exact_dot_nonneg_in(wr, kn, D, hx + pl * kAppendExp);
     if (bit) atomicOr(&bits[pl >> 5], 1u << (pl & 31));
   }
 

@@ -95,7 +95,7 @@ binary_codes_generic_kernel(const T* __restrict__ X, const T* __restrict__ R,
 // ---------------------------------------------------------------- matrix-core path
 
 constexpr int kSgnTile = 64;   // keys per tile
-constexpr int kSgnExp = 16;    // float64 partials of an exact expansion (LDS, per lane)
+constexpr int kSgnExp = kExactLimbs;  // words of an exact fixed-point sum (LDS, per lane)
 
 template <int D, int NBG>
 struct SignCfg {
@@ -118,10 +118,10 @@ struct SignCfg {
 
 // Exact sign of W[plane] . K[j] (bf16 rows of D values, 16-byte aligned):
 // both rows are loaded at once, the float64 sum decides unless it lies
-// within its rounding band, where the exact expansion takes over.
+// within its rounding band, where the exact fixed-point sum takes over.
 template <int D>
 __device__ __forceinline__ bool exact_sign_rows(const bf16* __restrict__ wrow,
-                                                const bf16* __restrict__ krow, double* h) {
+                                                const bf16* __restrict__ krow, uint64_t* h) {
   u32x4 wv[D / 8], kv[D / 8];
 #pragma unroll
   for (int i = 0; i < D / 8; ++i) {
@@ -140,7 +140,7 @@ __device__ __forceinline__ bool exact_sign_rows(const bf16* __restrict__ wrow,
       sa += fabs(p0) + fabs(p1);
     }
   if (fabs(s) > 2.0 * D * 0x1p-53 * sa) return s >= 0.0;
-  return expansion_dot_nonneg_in(wrow, krow, D, h, kSgnExp);
+  return exact_dot_nonneg_in(wrow, krow, D, h);
 }
 
 // Workgroup = 8 waves over keys [j0, j0 + kpw) of one (sequence, kv head) and
@@ -351,11 +351,11 @@ hash_signs_mfma_kernel(const bf16* __restrict__ K, const bf16* __restrict__ Wall
   // (free once every wave has left the loop); B: settle the listed pairs one
   // per lane and fix their bits.
   if (nfl == 0) return;
-  // per wave: the lanes' expansion partials, then the listed pairs
+  // per wave: the lanes' fixed-point sums, then the listed pairs
   constexpr int kRegion = static_cast<int>(2 * C::kBuf / C::kWaves) / 8 * 8;
   constexpr int kCap = (kRegion - 64 * kSgnExp * 8) / 8;
   static_assert(kCap >= 64, "room for a wave of pairs");
-  double* hx = reinterpret_cast<double*>(sgn_lds + wave * kRegion) + lane * kSgnExp;
+  uint64_t* hx = reinterpret_cast<uint64_t*>(sgn_lds + wave * kRegion) + lane * kSgnExp;
   uint2* items = reinterpret_cast<uint2*>(sgn_lds + wave * kRegion + 64 * kSgnExp * 8);
   int nit = 0;  // wave-uniform
   // the planes again (L2-resident): the main loop's copy is dead by now,

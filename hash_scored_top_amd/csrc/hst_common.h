@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "exact_dot.h"
 #include "hst.h"
 
 namespace hst {
@@ -53,46 +54,24 @@ __device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int nmax)
   return n < 0 ? 0 : (n > nmax ? nmax : n);
 }
 
-// Sign of a sum of float64 values, exactly: Shewchuk's growing expansion
-// ("Adaptive precision floating-point arithmetic", 1997) keeps the running
-// sum as non-overlapping partials, so the sign of the total is the sign of
-// the largest non-zero partial.  Returns true when the sum is >= 0.  h holds
-// up to hcap partials (products of stored bf16 / float32 values span at most
-// about 600 bits, i.e. a dozen non-overlapping float64 partials).
+// [ a . b >= 0 ] exactly for stored float32/bf16 vectors: the products
+// (exact in float64) summed in the fixed-point accumulator of exact_dot.h.
+// w: kExactLimbs words of scratch (registers, LDS or memory).
 template <typename T>
-__device__ __forceinline__ bool expansion_dot_nonneg_in(const T* __restrict__ a,
-                                                     const T* __restrict__ b, int n,
-                                                     double* h, int hcap) {
-  int nh = 0;
-  for (int c = 0; c < n; ++c) {
-    double x = to_f64(a[c]) * to_f64(b[c]);  // exact: at most 48 significant bits
-    int k = 0;
-    for (int i = 0; i < nh; ++i) {
-      double y = h[i];
-      double hi = x + y;
-      double bv = hi - x;
-      double lo = (x - (hi - bv)) + (y - bv);
-      if (lo != 0.0) h[k++] = lo;
-      x = hi;
-    }
-    if (k < hcap) h[k++] = x;
-    nh = k;
-  }
-  for (int i = nh - 1; i >= 0; --i)
-    if (h[i] != 0.0) return h[i] > 0.0;
-  return true;
+__device__ __forceinline__ bool exact_dot_nonneg_in(const T* __restrict__ a, const T* __restrict__ b, int n,
+                                                    uint64_t* w) {
+  return exact_sum_nonneg([&](int c) { return to_f64(a[c]) * to_f64(b[c]); }, n, w);
 }
 
 template <typename T>
-__device__ __noinline__ bool expansion_dot_nonneg(const T* __restrict__ a,
-                                                  const T* __restrict__ b, int n) {
-  double h[48];
-  return expansion_dot_nonneg_in(a, b, n, h, 48);
+__device__ __noinline__ bool exact_dot_nonneg(const T* __restrict__ a, const T* __restrict__ b, int n) {
+  uint64_t w[kExactLimbs];
+  return exact_dot_nonneg_in(a, b, n, w);
 }
 
 // [ a . b >= 0 ] for the exact real dot product of stored float32/bf16
 // vectors.  The float64 sum has error below n * 2^-53 * sum|a_c b_c| for any
-// order; only inside twice that band is the exact expansion needed.
+// order; only inside twice that band is the exact sum needed.
 template <typename T>
 __device__ __forceinline__ bool dot_nonneg_exact(const T* __restrict__ a,
                                                  const T* __restrict__ b, int n) {
@@ -103,7 +82,7 @@ __device__ __forceinline__ bool dot_nonneg_exact(const T* __restrict__ a,
     sa += fabs(p);
   }
   if (fabs(s) > 2.0 * n * 0x1p-53 * sa) return s >= 0.0;
-  return expansion_dot_nonneg(a, b, n);
+  return exact_dot_nonneg(a, b, n);
 }
 
 // float64 -> IEEE binary16 bits, round to nearest, ties to even, in one

@@ -287,7 +287,7 @@ __device__ __forceinline__ bool lds_dot_nonneg(const float* r, const float* x, i
     sa += fabs(p);
   }
   if (fabs(s) > 2.0 * d * 0x1p-53 * sa) return s >= 0.0;
-  return expansion_dot_nonneg(r, x, d);
+  return exact_dot_nonneg(r, x, d);
 }
 
 // LDS: 16 rows of R [16][d + 1] float, q [G][d + 1] float (rows padded by one
