@@ -751,19 +751,21 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
   const uint2* slots = a.slots + static_cast<long long>(bh) * a.nchunks * chunk;
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // the first counts, then the first 128 slots of the first eight chunks of
-  // each wave (copied below), all in flight together: the slot addresses do
-  // not depend on the counts (slots past a chunk's count are read, unused),
-  // and the counts, issued first, arrive without waiting for the slots
+  // the first counts, then the first 64*PX slots of the first eight chunks
+  // of each wave (copied below), all in flight together: the slot addresses
+  // do not depend on the counts (slots past a chunk's count are read,
+  // unused), and the counts, issued first, arrive without waiting for the
+  // slots
+  constexpr int PX = NT >= 1024 ? 2 : 3;  // (1024-thread workgroups hold 128 VGPRs)
   const int cnt0 = static_cast<int>(threadIdx.x) < nch ? static_cast<int>(cnt[threadIdx.x]) : 0;
   // (chunk indices clamped, so the loads are unconditional)
-  uint2 pre[8][2];
+  uint2 pre[8][PX];
   const int clast = nch > 0 ? nch - 1 : 0;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int c = min(wave + u * NW, clast);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) pre[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
+    for (int x = 0; x < PX; ++x) pre[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
   }
   int run = 0;
   for (int c0 = 0; c0 < nch; c0 += NT) {
@@ -778,18 +780,20 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
   __syncthreads();
   const int M = run;
   if (M >= k_need && M <= kSelCap) {
-    // each wave copies whole chunks (coalesced): eight chunks and sixteen
-    // loads per lane in flight (the first eight already loaded)
+    // each wave copies whole chunks (coalesced): eight chunks and 8*PX
+    // loads per lane in flight (the first eight chunks already loaded)
     for (int c0 = wave; c0 < nch; c0 += NW * 8) {
-      uint2 v[8][2];
+      uint2 v[8][PX];
       int cn[8], base[8];
+      int cmax = 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int c = c0 + u * NW;
         cn[u] = c < nch ? ws.offs[c + 1] - ws.offs[c] : 0;
         base[u] = c < nch ? ws.offs[c] : 0;
+        cmax = max(cmax, cn[u]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
+        for (int x = 0; x < PX; ++x) {
           if (c0 == wave) v[u][x] = pre[u][x];
           else if (lane + 64 * x < cn[u]) v[u][x] = slots[static_cast<long long>(c) * chunk + lane + 64 * x];
         }
@@ -797,16 +801,34 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < PX; ++x)
           if (lane + 64 * x < cn[u]) {
             ws.candk[base[u] + lane + 64 * x] = v[u][x].x;
             ws.candi[base[u] + lane + 64 * x] = static_cast<int32_t>(v[u][x].y);
           }
-        const long long c = c0 + u * NW;
-        for (int i = 128 + lane; i < cn[u]; i += 64) {  // chunks with many candidates
-          const uint2 w = slots[c * chunk + i];
-          ws.candk[base[u] + i] = w.x;
-          ws.candi[base[u] + i] = static_cast<int32_t>(w.y);
+        if constexpr (NT >= 1024) {  // chunks with more candidates, one by one (registers)
+          const long long c = c0 + u * NW;
+          for (int i = 64 * PX + lane; i < cn[u]; i += 64) {
+            const uint2 w = slots[c * chunk + i];
+            ws.candk[base[u] + i] = w.x;
+            ws.candi[base[u] + i] = static_cast<int32_t>(w.y);
+          }
+        }
+      }
+      if constexpr (NT < 1024) {
+        // chunks with more candidates: the next 64 of all eight chunks per
+        // round trip (cmax is the same in every lane of the wave)
+        for (int i0 = 64 * PX; i0 < cmax; i0 += 64) {
+          uint2 w[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + lane < cn[u]) w[u] = slots[static_cast<long long>(c0 + u * NW) * chunk + i0 + lane];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + lane < cn[u]) {
+              ws.candk[base[u] + i0 + lane] = w[u].x;
+              ws.candi[base[u] + i0 + lane] = static_cast<int32_t>(w[u].y);
+            }
         }
       }
     }
