@@ -26,6 +26,7 @@ struct BlockScratch {
   int wsum[NT / 64 + 2];
   uint32_t red[2][NT / 64];
   int found[4];
+  int rank_n;  // entries collected by a rank (zeroed by the selection that uses it)
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave, in DPP moves (no LDS

@@ -304,11 +304,13 @@ __device__ __forceinline__ bool hist_boundary(const uint32_t (&hb)[kHistBins / N
 // at most kRankBin) by (key descending, position ascending) and returns the
 // key and the position of the krem-th (rank krem - 1 among the entries).
 // The entries equal to that key that are taken are exactly those at or
-// before that position.  bl: LDS, >= max(kRankBin, NT) uint2.
-//  * cnt <= 64 (the usual case): one ballot pass writes each wave's entries
-//    to its own 64-entry segment of bl; then lane j of wave 0 takes the j-th
-//    entry over the segments and counts the entries ranked before it, reading
-//    the others from their lanes (no LDS round trip per comparison).
+// before that position.  bl: LDS, >= kRankBin uint2.
+//  * cnt <= 64 (the usual case): the entries go to bl in any order (each
+//    carries its position), at slots taken from the counter sc.rank_n, which
+//    must be 0 on entry; a step of the pass in which no lane of a wave holds
+//    an entry costs that wave one ballot.  Then lane j of wave 0 takes entry
+//    j and counts the entries ranked before it, reading the others from
+//    their lanes (no LDS round trip per comparison).
 //  * otherwise: a ballot count per wave, one slot reservation per wave and a
 //    second pass that writes the entries; thread j < cnt compares entry j
 //    with all of them from LDS.
@@ -317,38 +319,36 @@ template <int NT, int PERW, class In>
 __device__ __forceinline__ void rank_entries(const uint32_t (&key)[PERW], int lo, int hi, const In& in, int cnt,
                                              int krem, uint2* bl, BlockScratch<NT>& sc, uint32_t& kstar,
                                              int& cut) {
-  constexpr int NW = NT / 64;
-  static_assert(NW * 64 <= 1024, "wave segments fit the histogram region");
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (cnt <= 64) {  // uniform
-    uint2* seg = bl + wave * 64;
-    int nw = 0;
 #pragma unroll
     for (int u = 0; u < PERW; ++u) {
       const int p = lo + 64 * u + lane;
       const bool ok = p < hi && in(key[u]);
-      const unsigned long long b = __ballot(ok);
-      if (ok) seg[nw + lanes_below(b)] = make_uint2(key[u], static_cast<uint32_t>(p));
-      nw += __popcll(b);
+      if (__ballot(ok) != 0ull && ok) {
+        const int slot = atomicAdd(&sc.rank_n, 1);
+        bl[slot] = make_uint2(key[u], static_cast<uint32_t>(p));
+      }
     }
-    if (lane == 0) sc.red[1][wave] = static_cast<uint32_t>(nw);
     __syncthreads();
     if (wave == 0) {
-      int base = 0, src = -1;
+      const uint2 me = lane < cnt ? bl[lane] : make_uint2(0u, 0xffffffffu);
+      int bf[4] = {0, 0, 0, 0};  // four independent counts
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int c = static_cast<int>(sc.red[1][w]);
-        if (src < 0 && lane < base + c) src = w * 64 + lane - base;
-        base += c;
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t ok = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.x), j + x));
+          const uint32_t op = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.y), j + x));
+          bf[x] += (ok > me.x || (ok == me.x && op < me.y)) ? 1 : 0;
+        }
       }
-      const uint2 me = src >= 0 ? bl[src] : make_uint2(0u, 0xffffffffu);
-      int before = 0;
-      for (int j = 0; j < cnt; ++j) {
+      for (; j < cnt; ++j) {
         const uint32_t ok = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.x), j));
         const uint32_t op = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(me.y), j));
-        before += (ok > me.x || (ok == me.x && op < me.y)) ? 1 : 0;
+        bf[0] += (ok > me.x || (ok == me.x && op < me.y)) ? 1 : 0;
       }
-      if (src >= 0 && before == krem - 1) {
+      if (lane < cnt && bf[0] + bf[1] + bf[2] + bf[3] == krem - 1) {
         sc.found[0] = static_cast<int>(me.x);
         sc.found[1] = static_cast<int>(me.y);
       }
@@ -434,8 +434,12 @@ __device__ __forceinline__ void compact_regs(const uint32_t (&key)[PERW], int lo
       if (w < wave) run += static_cast<int>(g[w]);
   }
   __syncthreads();  // sc is reused by the caller
+  // this wave's selected entries take positions [run, run + selc): a wave
+  // whose range misses [r0, r1) writes nothing (uniform per wave)
+  if (run >= r1 || run + selc <= r0) return;
 #pragma unroll
   for (int u = 0; u < PERW; ++u) {
+    if (run >= r1) break;  // uniform per wave
     const bool sel = taken(u);
     const unsigned long long selb = __ballot(sel);
     const int pos = run + lanes_below(selb);
@@ -520,6 +524,7 @@ __device__ __forceinline__ void select_rule_core(const uint32_t* candk, int M, i
   mask = 0u;
   prefix = 0u;
   cut = 0x7fffffff;
+  if (t == 0) sc.rank_n = 0;  // read only after the barriers below
   bool done = k >= M;  // every entry taken
   if (HIST && !done && hi_info.ok) {
     constexpr int BPT = kHistBins / NT;
