@@ -49,10 +49,14 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
   }
   if (attn) {
     const long long rows = static_cast<long long>(kcap) * BH;
-    long long r = (rows + 255) / 256;  // about one split per CU
+    // about one split per CU: a selecting split spends a fixed time on the
+    // head's selection before its gather, so a second round of splits would
+    // pay it again on the critical path; up to 4096 rows per split keep one
+    // round (given rows: up to 1024)
+    long long r = (rows + 255) / 256;
     r = (r + 63) / 64 * 64;
     if (r < 64) r = 64;
-    if (r > 1024) r = 1024;
+    if (r > (select ? 4096 : 1024)) r = select ? 4096 : 1024;
     if ((kcap + r - 1) / r > kMaxSplits) r = (kcap + kMaxSplits - 1) / kMaxSplits;
     f.rps = static_cast<int>(r);
     f.nsplit = static_cast<int>((kcap + r - 1) / r);
