@@ -6,7 +6,7 @@ include/hst.h); this package only marshals torch tensors into it.
 from ._lib import (  # noqa: F401
     DecodeHamming, DecodeSoftLSH, DecodeSoftLSHMass, DecodeSoftLSHRouted, DecodeSoftLSHShared,
     EXPORTED, HST_BF16, HST_F16, HST_F32, HST_I32, HstError, HstShape, LIB_PATH,
-    hst_append_kv_binary, hst_append_kv_softlsh, hst_build_cards_softlsh, hst_decode_step_hamming,
+    debug_status, hst_append_kv_binary, hst_append_kv_softlsh, hst_build_cards_softlsh, hst_decode_step_hamming,
     hst_decode_step_softlsh, hst_decode_step_softlsh_noalloc, hst_hash_keys_binary,
     hst_hash_keys_softlsh, hst_query_tables_softlsh,
     hst_score_keys_hamming, hst_score_keys_softlsh, hst_score_scan_softlsh, hst_select_mass,

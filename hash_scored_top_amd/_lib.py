@@ -14,7 +14,8 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhst.so")
+# HST_LIBRARY=debug loads the bounds-checked debug build (libhst_debug.so)
+LIB_PATH = os.path.join(_PKG, "libhst_debug.so" if os.environ.get("HST_LIBRARY") == "debug" else "libhst.so")
 
 HST_OK, HST_ERR_INVALID_ARG, HST_ERR_UNSUPPORTED, HST_ERR_WORKSPACE, HST_ERR_HIP = 0, -1, -2, -3, -4
 HST_F32, HST_BF16, HST_F16, HST_I32 = 0, 1, 2, 3
@@ -25,7 +26,7 @@ HST_F32, HST_BF16, HST_F16, HST_I32 = 0, 1, 2, 3
 CHUNK = 64  # tokens per routing chunk
 
 EXPORTED = (
-    "hst_version", "hst_status_string", "hst_last_hip_error", "hst_workspace_size",
+    "hst_version", "hst_status_string", "hst_last_hip_error", "hst_debug_status", "hst_workspace_size",
     "hst_hash_keys_softlsh", "hst_hash_keys_binary", "hst_score_keys_softlsh",
     "hst_score_keys_hamming", "hst_select_topk", "hst_sparse_decode_attention",
     "hst_decode_step_softlsh", "hst_decode_step_hamming", "hst_query_tables_softlsh",
@@ -65,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "hst_version": ([], I),
         "hst_status_string": ([I], ctypes.c_char_p),
         "hst_last_hip_error": ([], I),
+        "hst_debug_status": ([ctypes.POINTER(ctypes.c_uint32)], I),
         "hst_workspace_size": ([I, SH, I, I, I, I, ctypes.POINTER(SZ)], I),
         "hst_hash_keys_softlsh": ([SH, P, P, P, I, I, I, P, P, P], I),
         "hst_hash_keys_binary": ([SH, P, P, I, P, P], I),
@@ -151,6 +153,15 @@ def make_shape(K: torch.Tensor, Hq: int, seq_lens: Optional[torch.Tensor] = None
 def _check(status: int, where: str) -> None:
     if status != HST_OK:
         raise HstError(status, where)
+
+
+def debug_status() -> int:
+    """The first failed bounds check since the last call (0: none), from the
+    debug build (HST_LIBRARY=debug); synchronises the device.  Raises
+    HstError(HST_ERR_UNSUPPORTED) with the release library."""
+    code = ctypes.c_uint32(0)
+    _check(_C.hst_debug_status(ctypes.byref(code)), "hst_debug_status")
+    return int(code.value)
 
 
 def workspace_size(op: int, shape: HstShape, L: int = 0, P: int = 0, code_bits: int = 128,

@@ -116,6 +116,7 @@ __device__ __forceinline__ void merge_splits(const FusedArgs& a, int bh, long lo
   __syncthreads();
   if (sc.found[0] == 0) return;  // uniform
   const int GS = G * nsplit;
+  HST_DCHECK(GS + 16 <= 16384, kDbgMergeLds);
   float* wt = reinterpret_cast<float*>(smem);  // [G][nsplit]: the weights
   float* ls = wt + GS;                         // [G]: sum of weighted l
   float* mx = ls + 8;                          // [G]: max m
@@ -237,6 +238,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     const int path = select_from_candidates<NT>(a, bh, n, k_eff, chunk, M, h_theta, h_shift, srow,
                                                 scores_int != 0, ws, r0, r1, nullptr, rows, sc);
     nrows = max(0, min(k_eff, r1) - r0);
+    HST_DCHECK(nrows <= a.rps, kDbgRowLds);
     if (split == 0 && t == 0) {
       a.heads[bh].path = static_cast<uint32_t>(path);
       a.heads[bh].cand_total = static_cast<uint32_t>(M);
@@ -283,6 +285,7 @@ attend_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restr
     for (int u = 0; u < U; ++u) {
       const int r = rb + u * NG;
       const int j = r < nrows ? rows[r] : -1;
+      HST_DCHECK(!SELECT || r >= nrows || (j >= 0 && j < n), kDbgGatherRow);
       valid[u] = j >= 0 && j < n;
       const int jj = valid[u] ? j : 0;
       // a shared prefix row, or a row of the sequence's own cache

@@ -10,6 +10,12 @@
 #include "hst_fused.h"
 #include "hst_launch.h"
 
+#ifdef HST_DEBUG
+namespace hst {
+__device__ uint32_t hst_debug_word = 0u;  // first failed check of the debug build (see hst_common.h)
+}
+#endif
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -97,6 +103,27 @@ const char* hst_status_string(int status) {
 }
 
 int hst_last_hip_error(void) { return g_last_hip_error; }
+
+hst_status hst_debug_status(uint32_t* code) {
+  if (code == nullptr) return HST_ERR_INVALID_ARG;
+#ifdef HST_DEBUG
+  uint32_t v = 0u;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(hst::hst_debug_word), sizeof(v), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) {
+    const uint32_t zero = 0u;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(hst::hst_debug_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return HST_ERR_HIP;
+  }
+  *code = v;
+  return HST_OK;
+#else
+  *code = 0u;
+  return HST_ERR_UNSUPPORTED;
+#endif
+}
 
 hst_status hst_workspace_size(int op, const hst_shape* shape, int L, int P, int code_bits, int k,
                               size_t* bytes) {

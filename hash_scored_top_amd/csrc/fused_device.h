@@ -326,7 +326,7 @@ __device__ __forceinline__ void rank_entries(const uint32_t (&key)[PERW], int lo
       const int p = lo + 64 * u + lane;
       const bool ok = p < hi && in(key[u]);
       if (__ballot(ok) != 0ull && ok) {
-        const int slot = atomicAdd(&sc.rank_n, 1);
+        const int slot = HST_DCLAMP(atomicAdd(&sc.rank_n, 1), 0, 63, kDbgRankSlot);
         bl[slot] = make_uint2(key[u], static_cast<uint32_t>(p));
       }
     }
@@ -439,16 +439,17 @@ __device__ __forceinline__ void compact_regs(const uint32_t (&key)[PERW], int lo
   if (run >= r1 || run + selc <= r0) return;
 #pragma unroll
   for (int u = 0; u < PERW; ++u) {
-    if (run >= r1) break;  // uniform per wave
-    const bool sel = taken(u);
-    const unsigned long long selb = __ballot(sel);
-    const int pos = run + lanes_below(selb);
-    if (sel && pos >= r0 && pos < r1) {
-      const int32_t v = static_cast<int32_t>(candi[lo + 64 * u + lane]);
-      if (out_g != nullptr) out_g[pos] = v;
-      if (out_l != nullptr) out_l[pos - r0] = v;
+    if (run < r1) {  // uniform per wave: nothing past r1 is written
+      const bool sel = taken(u);
+      const unsigned long long selb = __ballot(sel);
+      const int pos = run + lanes_below(selb);
+      if (sel && pos >= r0 && pos < r1) {
+        const int32_t v = static_cast<int32_t>(candi[lo + 64 * u + lane]);
+        if (out_g != nullptr) out_g[pos] = v;
+        if (out_l != nullptr) out_l[pos - r0] = v;
+      }
+      run += __popcll(selb);
     }
-    run += __popcll(selb);
   }
 }
 
@@ -776,6 +777,7 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
   for (int c0 = 0; c0 < nch; c0 += NT) {
     const int c = c0 + static_cast<int>(threadIdx.x);
     const int v = c0 == 0 ? cnt0 : (c < nch ? static_cast<int>(cnt[c]) : 0);
+    HST_DCHECK(v <= chunk, kDbgChunkCount);
     int tot;
     const int x = block_excl_scan<NT>(v, sc, tot);
     if (c < nch) ws.offs[c] = run + x;
@@ -805,6 +807,7 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
+        HST_DCHECK(base[u] + cn[u] <= kSelCap, kDbgCandLds);
 #pragma unroll
         for (int x = 0; x < PX; ++x)
           if (lane + 64 * x < cn[u]) {

@@ -11,6 +11,46 @@ namespace hst {
 
 constexpr int kWave = 64;
 
+// Checks of the debug build (compiled with HST_DEBUG into libhst_debug.so,
+// as relocatable device code so that one word serves every kernel).  A
+// failed check records its code in hst_debug_word (the first failure wins)
+// and execution goes on with the value clamped into range, so the kernel
+// completes normally; hst_debug_status() reads and clears the word.  In the
+// release build the checks compile to nothing and the value passes through.
+#ifdef HST_DEBUG
+extern __device__ uint32_t hst_debug_word;
+__device__ __forceinline__ void hst_dfail(uint32_t code) { atomicCAS(&hst_debug_word, 0u, code); }
+__device__ __forceinline__ int hst_dclamp(int v, int lo, int hi, uint32_t code) {
+  if (v < lo || v > hi) {
+    hst_dfail(code);
+    return v < lo ? lo : hi;
+  }
+  return v;
+}
+#define HST_DCHECK(cond, code) \
+  do {                         \
+    if (!(cond)) hst_dfail(code); \
+  } while (0)
+#define HST_DCLAMP(v, lo, hi, code) hst_dclamp((v), (lo), (hi), (code))
+#else
+#define HST_DCHECK(cond, code) \
+  do {                         \
+  } while (0)
+#define HST_DCLAMP(v, lo, hi, code) (v)
+#endif
+
+// Codes of the debug checks.
+enum : uint32_t {
+  kDbgChunkCount = 1,   // a scan chunk's candidate count above its slot capacity
+  kDbgCandLds = 2,      // a candidate copied past the LDS candidate region
+  kDbgRankSlot = 3,     // a rank entry past its LDS slots
+  kDbgRowLds = 4,       // a selected row written past the split's LDS rows
+  kDbgGatherRow = 5,    // a gathered row outside [0, n)
+  kDbgMergeLds = 6,     // the split merge's weights past its LDS region
+  kDbgSelectCount = 7,  // a selection that does not take exactly k_eff rows
+  kDbgSampleRow = 8,    // a sampled key outside [0, n)
+};
+
 // Native 128-bit vector (stays in registers where HIP's struct vector types
 // can end up in scratch memory when held in arrays).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -135,7 +135,9 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
       const int i = t + u * NT;
-      const long long row = base + sample_pos(i < S ? i : S - 1, S, n);
+      const int sp = sample_pos(i < S ? i : S - 1, S, n);
+      HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
+      const long long row = base + sp;
       if (fullg) {
         if constexpr (TG == 8) {
           const uint2 v = *reinterpret_cast<const uint2*>(ids + row * L + l0);
@@ -319,7 +321,9 @@ prep_qcodes_kernel(const T* __restrict__ q, const T* __restrict__ R, const uint3
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
       const int i = t + u * NT;
-      const long long row = base + sample_pos(i < S ? i : S - 1, S, n);
+      const int sp = sample_pos(i < S ? i : S - 1, S, n);
+      HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
+      const long long row = base + sp;
       sc16[u] = reinterpret_cast<const uint16_t*>(codes)[row * 8 + j];
     }
   }

@@ -413,6 +413,7 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
                                                    slot, sc);
+  HST_DCHECK(count <= kSoftCap, kDbgChunkCount);
   if (filt && threadIdx.x == 0) a.counts[static_cast<long long>(bh) * a.nchunks + chunk] = count;
 }
 

@@ -108,6 +108,18 @@ const char* hst_status_string(int status);
 int hst_last_hip_error(void);
 
 /*
+ * Debug builds only (libhst_debug.so, compiled with HST_DEBUG): the code of
+ * the first failed bounds check of any kernel since the last call (0 if
+ * none; the codes are listed in csrc/hst_common.h), which the call then
+ * clears.  A failed check clamps the value it guards, so kernels always
+ * complete; their results are then not to be trusted.  This call
+ * synchronises the device (a blocking copy), unlike every other entry point.
+ * The release library sets *code = 0 and returns HST_ERR_UNSUPPORTED.
+ * code: host pointer, must not be NULL (HST_ERR_INVALID_ARG).
+ */
+hst_status hst_debug_status(uint32_t* code);
+
+/*
  * Workspace bytes the given op needs for this shape.  L, P describe the
  * soft-LSH tables (ignored otherwise), code_bits the binary codes (ignored
  * otherwise), k the idx row capacity (select, attention, decode).
