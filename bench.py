@@ -580,13 +580,15 @@ def main():
         kname = "scan_lane_kernel<2>"
         ktag = "scan_hamming_filter"
     ksrc = os.path.join(ROOT, "hash_scored_top_amd", "csrc", "scan.hip")
-    # its average launch duration: a captured graph of R filter launches
-    # (input copies 0..R-1, after one prepare) replayed back to back between
-    # two events, three times; the threshold the first launch publishes stays
-    # set for the others (it holds the same value), so they do not wait for it
-    reps = max(1, iters // R)
+    # its average launch duration: a captured graph of 8R filter launches
+    # (input copies 0..R-1 in turn, after one prepare) replayed back to back
+    # between two events, three times; the threshold the first launch
+    # publishes stays set for the others (it holds the same value), so they
+    # do not wait for it
+    per_graph = 8 * R  # launches per replay: few replays, so replay gaps barely count
+    reps = max(2, iters // per_graph)
     stages[0](0)
-    gf = capture(lambda: [stages[1](i) for i in range(R)])
+    gf = capture(lambda: [stages[1](i % R) for i in range(per_graph)])
     gf.replay()
     torch.cuda.synchronize()
     tf = []
@@ -597,10 +599,10 @@ def main():
             gf.replay()
         ev[1].record(stream)
         torch.cuda.synchronize()
-        tf.append(ev[0].elapsed_time(ev[1]) * 1e3 / (reps * R))
+        tf.append(ev[0].elapsed_time(ev[1]) * 1e3 / (reps * per_graph))
     del gf
     kus = float(np.median(tf))
-    klaunches = 3 * reps * R
+    klaunches = 3 * reps * per_graph
     log(f"filter kernel {kus:.2f} us per launch ({klaunches} back-to-back launches)")
     achieved = kbytes / (kus * 1e-6) / 1e9
     traffic = traffic_record(ktag, w.name, ksrc)
