@@ -79,8 +79,8 @@ hst_status check_route(const hst_shape* s, int L, int P) {
   if (L != 16 && L != 32 && L != 64 && L != 128) return HST_ERR_UNSUPPORTED;
   if ((static_cast<long long>(L) << P) * 4 > 131072) return HST_ERR_UNSUPPORTED;
   if (hst::route_chunks(s->Nmax) > hst::kRouteMaxCards) return HST_ERR_UNSUPPORTED;
-  if (hst::card_route_smem(L, P, hst::route_chunks(s->Nmax)) > 160 * 1024 - 2048)
-    return HST_ERR_UNSUPPORTED;  // the card step holds table, keys and histogram in LDS
+  if (hst::card_route_smem(hst::route_chunks(s->Nmax)) > 160 * 1024 - 2048)
+    return HST_ERR_UNSUPPORTED;  // the card cut holds keys, candidates and histogram in LDS
   return HST_OK;
 }
 

@@ -15,6 +15,7 @@ constexpr int kHistBins = 2048;    // bins of a selection's histogram of candida
 constexpr int kRunLen = 8;         // the sample is kSample / kRunLen runs of consecutive keys
 constexpr int kMaxChunks = 4096;   // scan chunks per head (bounds Nmax)
 constexpr int kMaxSplits = 256;    // attention splits per kv head (bounds the merge LDS)
+constexpr int kCardKeys = 64;     // keys one index card of the routed step summarises
 constexpr int kPrepBlocks = 8;     // prep workgroups per head (at least): each gathers 1/8 of the sample
 
 enum ScanKind { kScanSoftFast = 0, kScanSoftAny = 1, kScanHamming = 2, kScanGivenF32 = 3, kScanGivenI32 = 4 };
@@ -70,6 +71,12 @@ struct FusedArgs {
   const void* pk;
   const void* pv;
   int np;
+  // index cards of the routed step (soft-LSH prep only): when cpart is set,
+  // each prep workgroup also scores the first ceil(n_b / kCardKeys) cards of
+  // its head on its own tables, cpart[B*Hkv][xparts][ncards] (no weight)
+  const uint8_t* cids;  // [B*Hkv][ncards][L] card bucket ids
+  float* cpart;
+  int ncards;
 };
 __host__ __device__ inline int a_nsplit(const FusedArgs& a) { return a.nsplit; }
 
@@ -144,10 +151,10 @@ hipError_t launch_card_sums(const hst_shape& s, const void* K, const void* vnorm
 hipError_t launch_route_scan(const hst_shape& s, const float* tables, const int32_t* chunks, int C,
                              const uint8_t* ids, const void* vnorm, int norm_f16, int L, int P,
                              int out_stride, float* out, hipStream_t st);
-size_t card_route_smem(int L, int P, int Nc);
-hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint8_t* cids,
-                             const void* cw, int norm_f16, int L, int P, int C, int32_t* chunks,
-                             hipStream_t st);
+size_t card_route_smem(int Nc);
+// cpart: the prep workgroups' partial card scores, xparts parts per head
+hipError_t launch_card_route(const hst_shape& s, const float* cpart, int xparts, const void* cw,
+                             int norm_f16, int C, int32_t* chunks, hipStream_t st);
 hipError_t launch_token_route(const hst_shape& s, const float* scores, int nitems,
                               const int32_t* chunks, int C, int k, const int32_t* kps,
                               int32_t* out, hipStream_t st);

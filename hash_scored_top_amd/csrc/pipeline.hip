@@ -200,7 +200,7 @@ hipError_t build_cards_softlsh(const hst_shape& s, const void* K, const void* vn
 // Workspace of the routed step: tables, the attention partials, the kept
 // chunks and the scores of their keys.
 struct RouteLayout {
-  size_t tables, attn, chunks, tscore, bytes;
+  size_t tables, cpart, attn, chunks, tscore, bytes;
 };
 
 static RouteLayout route_layout(const hst_shape& s, int L, int P, int kcap) {
@@ -213,6 +213,7 @@ static RouteLayout route_layout(const hst_shape& s, int L, int P, int kcap) {
     return at;
   };
   r.tables = take(BH * (static_cast<size_t>(L) << P) * 4);
+  r.cpart = take(BH * prep_parts(kScanSoftFast, L) * static_cast<size_t>(route_chunks(s.Nmax)) * 4);
   r.attn = take(fused_layout(s, HST_OP_SPARSE_ATTENTION, 0, 0, kcap).bytes);
   r.chunks = take(BH * kRouteMaxChunks * 4);
   r.tscore = take(BH * kRouteMaxChunks * 64 * 4);
@@ -236,13 +237,17 @@ hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const 
   int32_t* chunks = reinterpret_cast<int32_t*>(base + r.chunks);
   float* tscore = reinterpret_cast<float*>(base + r.tscore);
   const int f16 = norm_dtype == HST_F16;
-  // query tables
+  // query tables, and every card scored on each prep workgroup's tables
   const FusedLayout fs = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   FusedArgs as = make_args(s, fs, nullptr, L, P, tau, 1);
   as.tables = tables;
+  as.xparts = prep_parts(kScanSoftFast, L);
+  as.cids = cids;
+  as.cpart = reinterpret_cast<float*>(base + r.cpart);
+  as.ncards = route_chunks(s.Nmax);
   HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, 0, nullptr, st));
-  // every card scored, the C best chunks kept; then the k best keys inside
-  HST_CHECK(launch_card_route(s, tables, cids, cw, f16, L, P, C, chunks, st));
+  // the C best chunks kept; then the k best keys inside
+  HST_CHECK(launch_card_route(s, as.cpart, as.xparts, cw, f16, C, chunks, st));
   HST_CHECK(launch_route_scan(s, tables, chunks, C, ids, vnorm, f16, L, P, C * 64, tscore, st));
   HST_CHECK(launch_token_route(s, tscore, C * 64, chunks, C, kcap, kps, idx, st));
   // exact attention over the original rows

@@ -19,7 +19,9 @@
 // part of the hash (its TG tables, its 16 code bits), reading only that slice
 // of each sampled key's metadata; the scan adds the parts up and derives the
 // candidate threshold theta from them (scan.hip).  theta only bounds the work
-// of the selection: the selected set never depends on it.
+// of the selection: the selected set never depends on it.  For the routed
+// step the soft-LSH workgroups score the head's index cards the same way,
+// and the card cut adds the parts up (route.hip).
 #include "fused_device.h"
 #include "hst_launch.h"
 
@@ -125,29 +127,39 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     qv[u] = to_f32(qsrc[e < G * d ? e : G * d - 1]);
   }
 
-  // sampled keys' ids of this table group (TG bytes per key), loads issued now
+  // The items this group scores on its tables, their ids (TG bytes each)
+  // loaded now: the key sample, or for the routed step the head's index cards
+  // (the first ceil(n / kCardKeys) rows of a.cids; the card cut applies the
+  // card weights).
   int n;
-  const int S = sample_size(a, seq_lens, k_per_seq, b, n);
+  const int S0 = sample_size(a, seq_lens, k_per_seq, b, n);
+  const bool cards = a.cpart != nullptr;
+  const int S = cards ? (n + kCardKeys - 1) / kCardKeys : S0;  // items
   const long long base = static_cast<long long>(bh) * a.Nmax;
+  const uint8_t* isrc = cards ? a.cids : ids;
+  const auto item_row = [&](int i) -> long long {
+    if (cards) return static_cast<long long>(bh) * a.ncards + i;
+    const int sp = sample_pos(i, S, n);
+    HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
+    return base + sp;
+  };
   uint32_t sid[kSPer][TG / 4];
   uint32_t svr[kSPer];
   if (S > 0) {
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
       const int i = t + u * NT;
-      const int sp = sample_pos(i < S ? i : S - 1, S, n);
-      HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
-      const long long row = base + sp;
+      const long long row = item_row(i < S ? i : S - 1);
       if (fullg) {
         if constexpr (TG == 8) {
-          const uint2 v = *reinterpret_cast<const uint2*>(ids + row * L + l0);
+          const uint2 v = *reinterpret_cast<const uint2*>(isrc + row * L + l0);
           sid[u][0] = v.x;
           sid[u][1] = v.y;
         } else {
-          sid[u][0] = *reinterpret_cast<const uint32_t*>(ids + row * L + l0);
+          sid[u][0] = *reinterpret_cast<const uint32_t*>(isrc + row * L + l0);
         }
       }
-      if (j == 0)
+      if (j == 0 && !cards)
         svr[u] = norm_f16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(vnorm)[row])
                           : static_cast<const uint32_t*>(vnorm)[row];
     }
@@ -249,9 +261,19 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   if (S == 0) return;
   __syncthreads();
 
-  // partial sample scores on this group's tables
+  // partial item scores on this group's tables
   const uint32_t idm = static_cast<uint32_t>(nb - 1);
-  float* part = a.spart + (static_cast<long long>(bh) * a.xparts + j) * kSample;
+  float* part = cards ? a.cpart + (static_cast<long long>(bh) * a.xparts + j) * a.ncards
+                      : a.spart + (static_cast<long long>(bh) * a.xparts + j) * kSample;
+  const auto score_row = [&](int i) {
+    const uint8_t* row = isrc + item_row(i) * L + l0;
+    float s2[2] = {0.f, 0.f};
+    for (int ll = 0; ll < lg; ++ll) {
+      const int c = static_cast<int>(row[ll] & idm);
+      s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
+    }
+    return s2[0] + s2[1];
+  };
 #pragma unroll
   for (int u = 0; u < kSPer; ++u) {
     const int i = t + u * NT;
@@ -263,18 +285,15 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
         const int c = static_cast<int>((sid[u][ll >> 2] >> (8 * (ll & 3))) & idm);
         s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
       }
+      part[i] = s2[0] + s2[1];
     } else {
-      const uint8_t* row = ids + (base + sample_pos(i, S, n)) * L + l0;
-      for (int ll = 0; ll < lg; ++ll) {
-        const int c = static_cast<int>(row[ll] & idm);
-        s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
-      }
+      part[i] = score_row(i);
     }
-    part[i] = s2[0] + s2[1];
-    if (j == 0)
+    if (j == 0 && !cards)
       a.svn[static_cast<long long>(bh) * kSample + i] =
           norm_f16 ? f16_bits_to_f32(static_cast<uint16_t>(svr[u])) : __uint_as_float(svr[u]);
   }
+  for (int i = kSPer * NT + t; i < S; i += NT) part[i] = score_row(i);  // cards past the first kSPer * NT
 }
 
 // ---------------------------------------------------------------------------

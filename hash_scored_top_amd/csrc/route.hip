@@ -19,8 +19,10 @@
 //                      bucket), scores the 64 keys of each of 16 chosen
 //                      chunks, one key per thread.
 //   card_route_kernel  one 1024-thread workgroup per (sequence, kv head):
-//                      the table (table-major in LDS) scores every card,
-//                      and the exact top C is cut and compacted.
+//                      every card's score from the partial scores the
+//                      prep workgroups wrote (each on its own tables, see
+//                      prep.hip) times the card weight, then the exact
+//                      top C is cut and compacted.
 //   token_route_kernel one 1024-thread workgroup per (sequence, kv head):
 //                      the exact top k of the scored keys, mapped from
 //                      positions in the kept chunks to key indices.
@@ -36,7 +38,8 @@
 
 namespace hst {
 
-constexpr int kChunkTok = 64;       // tokens per chunk
+constexpr int kChunkTok = kCardKeys;  // tokens per chunk
+constexpr int kMaxCardParts = 16;     // partial card scores per head (prep workgroups)
 constexpr int kTopNT = 1024;        // threads of the small top-k
 constexpr int kRouteNT = 1024;      // threads of the routed scan (16 chunks)
 
@@ -297,23 +300,22 @@ struct PosIdx {
   __device__ __forceinline__ int32_t operator[](int r) const { return r; }
 };
 
-// Chunk routing for one (sequence, kv head): the head's table (table-major
-// in LDS) scores every card, and the C best cards (score descending, chunk
-// ascending) are written ascending to chunks[bh][0..C), then -1.  REGS: the
-// selection on register-held keys, two cards per lane (Nc <= 2048); else the
-// count-histogram cut (more cards would spill the registers).
-template <int L, bool REGS>
+// Chunk routing for one (sequence, kv head): the score of card c is its
+// weight times the sum of the xparts partial scores the prep workgroups
+// wrote (each over its own group of tables, added in group order), and the
+// C best cards (score descending, chunk ascending) are written ascending to
+// chunks[bh][0..C), then -1.  REGS: the selection on register-held keys, two
+// cards per lane (Nc <= 2048); else the count-histogram cut (more cards
+// would spill the registers).
+template <bool REGS>
 __global__ void __launch_bounds__(kTopNT)
-card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ cids,
-                  const void* __restrict__ cw, int norm_f16, const int32_t* __restrict__ seq_lens,
-                  int Hkv, int Nmax, int Nc, int P, int C, int32_t* __restrict__ chunks) {
+card_route_kernel(const float* __restrict__ cpart, int xparts, const void* __restrict__ cw, int norm_f16,
+                  const int32_t* __restrict__ seq_lens, int Hkv, int Nmax, int Nc, int C,
+                  int32_t* __restrict__ chunks) {
   extern __shared__ __align__(16) unsigned char sm[];
-  const int nb = 1 << P;
-  const size_t tbytes = static_cast<size_t>(L) * (nb + 1) * 4;
-  const size_t cbytes = static_cast<size_t>(Nc) * 4;
-  float* tl = reinterpret_cast<float*>(sm);  // table, then the cut's candidates (count-histogram cut)
-  uint32_t* key = reinterpret_cast<uint32_t*>(sm + (tbytes > cbytes ? tbytes : cbytes));
-  uint32_t* hist = key + Nc;                                                  // 4096
+  uint32_t* cand = reinterpret_cast<uint32_t*>(sm);  // the count-histogram cut's candidates
+  uint32_t* key = cand + Nc;
+  uint32_t* hist = key + Nc;  // 4096
   __shared__ uint32_t red[kTopNT / 64];
   __shared__ BlockScratch<kTopNT> tsc;
   __shared__ uint64_t red64[kTopNT / 64];
@@ -321,31 +323,29 @@ card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ 
   const int bh = blockIdx.x, b = bh / Hkv, t = threadIdx.x;
   const int n = seq_len(seq_lens, b, Nmax);
   const int nc = (n + kChunkTok - 1) / kChunkTok;
-  const float* Tg = tables + static_cast<long long>(bh) * nb * L;
-  load_table_t<kTopNT>(Tg, tl, L, nb);
-  __syncthreads();
-  for (int c = t; c < Nc; c += kTopNT) {
-    uint32_t k = 0;
-    if (c < nc) {
+  const float* pp = cpart + static_cast<long long>(bh) * xparts * Nc;
+  for (int c0 = 0; c0 < Nc; c0 += 2 * kTopNT) {
+    // two cards per thread, every part of both in flight together
+    float pv[2][kMaxCardParts];
+    float w[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = min(c0 + t + u * kTopNT, max(nc - 1, 0));
       const long long row = static_cast<long long>(bh) * Nc + c;
-      const u32x4* ip = reinterpret_cast<const u32x4*>(cids + row * L);
-      float s = 0.0f;
-#pragma unroll 2
-      for (int i = 0; i < L / 16; ++i) {
-        const u32x4 v = ip[i];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int by = 0; by < 4; ++by) {
-            const int l = i * 16 + q * 4 + by;
-            s += tl[l * (nb + 1) + ((v[q] >> (8 * by)) & 0xffu)];
-          }
-      }
-      const float w = norm_f16 ? f16_bits_to_f32(static_cast<const uint16_t*>(cw)[row])
-                               : static_cast<const float*>(cw)[row];
-      k = score_key(w * s);
+      for (int x = 0; x < kMaxCardParts; ++x) pv[u][x] = x < xparts ? pp[static_cast<long long>(x) * Nc + c] : 0.f;
+      w[u] = norm_f16 ? f16_bits_to_f32(static_cast<const uint16_t*>(cw)[row]) : static_cast<const float*>(cw)[row];
     }
-    key[c] = k;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + t + u * kTopNT;
+      if (c >= Nc) continue;
+      float s = 0.0f;
+#pragma unroll
+      for (int x = 0; x < kMaxCardParts; ++x)
+        if (x < xparts) s += pv[u][x];
+      key[c] = c < nc ? score_key(w[u] * s) : 0u;
+    }
   }
   __syncthreads();
   const uint32_t valid = block_count_nonzero(key, Nc, red);
@@ -357,7 +357,7 @@ card_route_kernel(const float* __restrict__ tables, const uint8_t* __restrict__ 
     for (int p = ks + t; p < C; p += kTopNT) orow[p] = -1;
   } else {
     const Cut cut = block_cut(key, Nc, valid, static_cast<uint32_t>(min(C, nc)),
-                              CutScratch{hist, reinterpret_cast<uint32_t*>(sm), red, vars});
+                              CutScratch{hist, cand, red, vars});
     block_cut_compact(key, Nc, cut, orow, C, red64, &total, [](int r) { return r; });
   }
 }
@@ -470,39 +470,26 @@ hipError_t launch_route_scan(const hst_shape& s, const float* tables, const int3
   return hipGetLastError();
 }
 
-size_t card_route_smem(int L, int P, int Nc) {
-  const size_t tb = static_cast<size_t>(L) * ((1u << P) + 1) * 4, cb = static_cast<size_t>(Nc) * 4;
-  return (tb > cb ? tb : cb) + static_cast<size_t>(Nc) * 4 + 4096 * 4;  // table, keys, histogram
+size_t card_route_smem(int Nc) {
+  return static_cast<size_t>(Nc) * 8 + 4096 * 4;  // candidates, keys, histogram
 }
 
-hipError_t launch_card_route(const hst_shape& s, const float* tables, const uint8_t* cids,
-                             const void* cw, int norm_f16, int L, int P, int C, int32_t* chunks,
-                             hipStream_t st) {
+hipError_t launch_card_route(const hst_shape& s, const float* cpart, int xparts, const void* cw,
+                             int norm_f16, int C, int32_t* chunks, hipStream_t st) {
   const int Nc = route_chunks(s.Nmax);
-  const size_t smem = card_route_smem(L, P, Nc);
+  if (xparts < 1 || xparts > kMaxCardParts) return hipErrorInvalidValue;
+  const size_t smem = card_route_smem(Nc);
   hipError_t e;
-  const bool regs = Nc <= 2 * kTopNT;
-#define HST_CARD_LP(LL, RG)                                                                    \
-  do {                                                                                         \
-    e = route_lds_limit(card_route_kernel<LL, RG>, smem);                                      \
-    if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL((card_route_kernel<LL, RG>), dim3(s.B * s.Hkv), dim3(kTopNT), smem, st,  \
-                       tables, cids, cw, norm_f16, s.seq_lens, s.Hkv, s.Nmax, Nc, P, C, chunks); \
+#define HST_CARD(RG)                                                                                \
+  do {                                                                                              \
+    e = route_lds_limit(card_route_kernel<RG>, smem);                                               \
+    if (e != hipSuccess) return e;                                                                  \
+    hipLaunchKernelGGL((card_route_kernel<RG>), dim3(s.B * s.Hkv), dim3(kTopNT), smem, st, cpart,    \
+                       xparts, cw, norm_f16, s.seq_lens, s.Hkv, s.Nmax, Nc, C, chunks);             \
   } while (0)
-#define HST_CARD_L(LL)                    \
-  case LL:                                \
-    if (regs) HST_CARD_LP(LL, true);      \
-    else HST_CARD_LP(LL, false);          \
-    break;
-  switch (L) {
-    HST_CARD_L(16)
-    HST_CARD_L(32)
-    HST_CARD_L(64)
-    HST_CARD_L(128)
-    default: return hipErrorInvalidValue;
-  }
-#undef HST_CARD_LP
-#undef HST_CARD_L
+  if (Nc <= 2 * kTopNT) HST_CARD(true);
+  else HST_CARD(false);
+#undef HST_CARD
   return hipGetLastError();
 }
 
