@@ -49,6 +49,7 @@ enum : uint32_t {
   kDbgMergeLds = 6,     // the split merge's weights past its LDS region
   kDbgSelectCount = 7,  // a selection that does not take exactly k_eff rows
   kDbgSampleRow = 8,    // a sampled key outside [0, n)
+  kDbgCardRow = 9,      // an index card outside the head's card rows
 };
 
 // Native 128-bit vector (stays in registers where HIP's struct vector types

@@ -138,7 +138,10 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const long long base = static_cast<long long>(bh) * a.Nmax;
   const uint8_t* isrc = cards ? a.cids : ids;
   const auto item_row = [&](int i) -> long long {
-    if (cards) return static_cast<long long>(bh) * a.ncards + i;
+    if (cards) {
+      HST_DCHECK(i >= 0 && i < a.ncards, kDbgCardRow);
+      return static_cast<long long>(bh) * a.ncards + i;
+    }
     const int sp = sample_pos(i, S, n);
     HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
     return base + sp;

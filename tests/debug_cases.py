@@ -43,6 +43,15 @@ def run_cases(hst):
         res[f"{w.name}_out"] = out.cpu().numpy()
         res[f"{w.name}_lse"] = lse.cpu().numpy()
         res[f"{w.name}_out_given"] = o2.cpu().numpy()
+        if w is SOFT:  # the routed step: index cards scored by the prepare kernel, card and token cuts
+            k = w.k_max()
+            C = min(256, 4 * -(-k // 64))
+            cards = hst.hst_build_cards_softlsh(K, vn, W, w.L, w.P, seq_lens=sl)
+            rstep = hst.DecodeSoftLSHRouted(K, w.Hq, w.L, w.P, w.tau, k, C, vn.dtype, seq_lens=sl, k_per_seq=kp)
+            ridx, rout, rlse = rstep(q, K, V, W, ids, vn, cards[1], cards[2])
+            res["routed_idx"] = ridx.cpu().numpy()
+            res["routed_out"] = rout.cpu().numpy()
+            res["routed_lse"] = rlse.cpu().numpy()
     w = HAM
     x = WL.make_full(w)
     K, V, q, R = (to_dev(x[n], w.kv_dtype, DEV) for n in ("K", "V", "q", "R"))

@@ -3,8 +3,8 @@ recording into one device word, see csrc/hst_common.h) on the decode path.
 
 A child process loads it (HST_LIBRARY=debug) and runs tests/debug_cases.py:
 soft-LSH hashing and decode over a ragged bf16 batch and the fp32 tiny case,
-attention over given rows, binary codes and their decode step, and a
-stand-alone top-k with ties.  No check may fail, and every result must equal
+the routed step on the ragged batch, attention over given rows, binary codes
+and their decode step, and a stand-alone top-k with ties.  No check may fail, and every result must equal
 the release library's on the same inputs (the checks only observe)."""
 import os
 import subprocess
