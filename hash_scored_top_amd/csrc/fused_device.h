@@ -249,6 +249,15 @@ struct HistInfo {
   }
 };
 
+// Histogram bin width for keys from theta up to khi: [theta, khi] spans fewer
+// than kHistBins / 2 bins.
+__device__ __forceinline__ int hist_shift(uint32_t theta, uint32_t khi) {
+  const uint32_t d = khi > theta ? khi - theta : 0u;
+  int sh = 0;
+  while ((d >> sh) >= static_cast<uint32_t>(kHistBins / 2)) ++sh;
+  return sh;
+}
+
 // Bin of the k-th largest candidate from the histogram, counted from the top
 // bin down.  hb: this thread's bins, kHistBins / NT of them, in descending
 // bin order starting at bin kHistBins - 1 - threadIdx.x * (kHistBins / NT).

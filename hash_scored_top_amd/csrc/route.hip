@@ -281,17 +281,41 @@ __device__ Cut block_cut(const uint32_t* key, int nitems, uint32_t valid, uint32
   return block_radix_cut(key, nitems, want, sc);
 }
 
-__device__ __forceinline__ uint32_t block_count_nonzero(const uint32_t* key, int nitems,
-                                                        uint32_t* red) {
+// Count, smallest and largest of the non-zero keys in LDS (0 marks no item),
+// in one pass.  red3: 3 * kTopNT / 64 words of LDS.
+struct KeyStats {
+  uint32_t valid, kmin, kmax;
+};
+__device__ __forceinline__ KeyStats block_key_stats(const uint32_t* key, int nitems, uint32_t* red3) {
+  constexpr int NW = kTopNT / 64;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  uint32_t v = 0;
-  for (int r = t; r < nitems; r += kTopNT) v += key[r] != 0;
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  uint32_t v = 0, mn = 0xffffffffu, mx = 0u;
+  for (int r = t; r < nitems; r += kTopNT) {
+    const uint32_t k = key[r];
+    if (k != 0u) {
+      ++v;
+      mn = min(mn, k);
+      mx = max(mx, k);
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    v += static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m));
+    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), m)));
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), m)));
+  }
   __syncthreads();
-  if (lane == 0) red[wv] = v;
+  if (lane == 0) {
+    red3[wv] = v;
+    red3[NW + wv] = mn;
+    red3[2 * NW + wv] = mx;
+  }
   __syncthreads();
-  uint32_t s = 0;
-  for (int w = 0; w < kTopNT / 64; ++w) s += red[w];
+  KeyStats s{0u, 0xffffffffu, 0u};
+  for (int w = 0; w < NW; ++w) {
+    s.valid += red3[w];
+    s.kmin = min(s.kmin, red3[NW + w]);
+    s.kmax = max(s.kmax, red3[2 * NW + w]);
+  }
   return s;
 }
 
@@ -316,7 +340,7 @@ card_route_kernel(const float* __restrict__ cpart, int xparts, const void* __res
   uint32_t* cand = reinterpret_cast<uint32_t*>(sm);  // the count-histogram cut's candidates
   uint32_t* key = cand + Nc;
   uint32_t* hist = key + Nc;  // 4096
-  __shared__ uint32_t red[kTopNT / 64];
+  __shared__ uint32_t red[3 * (kTopNT / 64)];
   __shared__ BlockScratch<kTopNT> tsc;
   __shared__ uint64_t red64[kTopNT / 64];
   __shared__ uint32_t vars[4], total;
@@ -348,12 +372,17 @@ card_route_kernel(const float* __restrict__ cpart, int xparts, const void* __res
     }
   }
   __syncthreads();
-  const uint32_t valid = block_count_nonzero(key, Nc, red);
+  const KeyStats kst = block_key_stats(key, Nc, red);
+  const uint32_t valid = kst.valid;
   int32_t* orow = chunks + static_cast<long long>(bh) * C;
   if constexpr (REGS) {
-    // the C best cards (fewer if fewer chunks exist), ascending, then -1
+    // the C best cards (fewer if fewer chunks exist), ascending, then -1, by
+    // the selection's histogram over the keys' own range (radix passes only
+    // when a bin is too full to rank)
     const int ks = min(min(C, nc), static_cast<int>(valid));
-    if (ks > 0) select_lds_regs<kTopNT, 2>(key, PosIdx{}, Nc, ks, 0, ks, orow, nullptr, hist, tsc);
+    const HistInfo hi{kst.kmin, hist_shift(kst.kmin, kst.kmax), true};
+    if (ks > 0)
+      select_lds_core<kTopNT, 2, PosIdx, true>(key, PosIdx{}, Nc, ks, 0, ks, orow, nullptr, hist, tsc, hi);
     for (int p = ks + t; p < C; p += kTopNT) orow[p] = -1;
   } else {
     const Cut cut = block_cut(key, Nc, valid, static_cast<uint32_t>(min(C, nc)),
@@ -376,7 +405,7 @@ token_route_kernel(const float* __restrict__ scores, int nitems,
                    const int32_t* __restrict__ chunks, int C, int k,
                    const int32_t* __restrict__ k_per_seq, int Hkv, int32_t* __restrict__ out) {
   extern __shared__ __align__(16) uint32_t keybuf[];  // [nitems] keys, [2048] hist
-  __shared__ uint32_t red[kTopNT / 64];
+  __shared__ uint32_t red[3 * (kTopNT / 64)];
   __shared__ BlockScratch<kTopNT> tsc;
   const int bh = blockIdx.x, b = bh / Hkv, t = threadIdx.x;
   uint32_t* key = keybuf;
@@ -408,12 +437,15 @@ token_route_kernel(const float* __restrict__ scores, int nitems,
     }
   }
   __syncthreads();
-  const uint32_t valid = block_count_nonzero(key, nitems, red);
+  const KeyStats kst = block_key_stats(key, nitems, red);
+  const uint32_t valid = kst.valid;
   int kb = k_per_seq != nullptr ? k_per_seq[b] : k;
   kb = max(0, min(kb, k));
   // the kb best (fewer if fewer keys exist: a missing key's order key 0 is
   // below every real one, so it is never among them), by the selection on
-  // register-held keys; positions map to key indices through the kept chunks
+  // register-held keys, radix passes from the keys' common prefix (a
+  // histogram over [min, max] crowds these skewed scores into a few bins);
+  // positions map to key indices through the kept chunks
   const int ks = min(kb, static_cast<int>(valid));
   int32_t* orow = out + static_cast<long long>(bh) * k;
   if (ks > 0)

@@ -263,15 +263,6 @@ __device__ __forceinline__ ScanWork scan_work(bool filt, int BH, int nch) {
   return w;
 }
 
-// Histogram bin width for candidates keyed from theta up: [theta, khi] (the
-// sample's largest key) spans fewer than kHistBins / 2 bins.
-__device__ __forceinline__ int hist_shift(uint32_t theta, uint32_t khi) {
-  const uint32_t d = khi > theta ? khi - theta : 0u;
-  int sh = 0;
-  while ((d >> sh) >= static_cast<uint32_t>(kHistBins / 2)) ++sh;
-  return sh;
-}
-
 // Candidate threshold of head bh: the sample scores are the sums of the
 // parts prep wrote (times the sampled value norm for soft-LSH), and theta is
 // a lower bound of the sample score at a high-margin rank.  The bin width of
