@@ -81,7 +81,9 @@ __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int 
   return m;
 }
 
-template <typename T, int TG>
+// CARDS: the routed step's variant, which scores the index cards (a.cpart
+// set) instead of the key sample.
+template <typename T, int TG, bool CARDS>
 __global__ void __launch_bounds__(kPrepNT)
 prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8_t* __restrict__ ids,
                    const void* __restrict__ vnorm, int norm_f16, const int32_t* __restrict__ seq_lens,
@@ -133,7 +135,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   // card weights).
   int n;
   const int S0 = sample_size(a, seq_lens, k_per_seq, b, n);
-  const bool cards = a.cpart != nullptr;
+  constexpr bool cards = CARDS;
   const int S = cards ? (n + kCardKeys - 1) / kCardKeys : S0;  // items
   const long long base = static_cast<long long>(bh) * a.Nmax;
   const uint8_t* isrc = cards ? a.cids : ids;
@@ -296,7 +298,8 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
       a.svn[static_cast<long long>(bh) * kSample + i] =
           norm_f16 ? f16_bits_to_f32(static_cast<uint16_t>(svr[u])) : __uint_as_float(svr[u]);
   }
-  for (int i = kSPer * NT + t; i < S; i += NT) part[i] = score_row(i);  // cards past the first kSPer * NT
+  if constexpr (CARDS)  // cards past the first kSPer * NT (the sample has at most kSample keys)
+    for (int i = kSPer * NT + t; i < S; i += NT) part[i] = score_row(i);
 }
 
 // ---------------------------------------------------------------------------
@@ -419,7 +422,7 @@ hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* 
   dim3 grid(s.B * s.Hkv, (a.L + TG - 1) / TG);
 #define HST_PREP(TT, TGV)                                                                      \
   do {                                                                                         \
-    auto kern = prep_tables_kernel<TT, TGV>;                                                   \
+    auto kern = a.cpart != nullptr ? prep_tables_kernel<TT, TGV, true> : prep_tables_kernel<TT, TGV, false>; \
     const size_t smem = tab_smem(G, s.d, static_cast<int>(sizeof(TT)), a.P, TGV).bytes;        \
     hipError_t e = set_smem(kern, smem);                                                       \
     if (e != hipSuccess) return e;                                                             \
