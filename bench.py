@@ -573,8 +573,9 @@ def main():
     if w.scheme == "softlsh":
         f16 = "true" if w.norm_dtype == "f16" else "false"
         span = scan_span_of(w, dev)
+        full = "true" if (w.L == 64 and w.P == 8) else "false"  # the full-table variant
         kname = (f"scan_softlsh_kernel<{w.L // 16}, 2, true, {f16}, "
-                 f"{'true' if span > 2048 else 'false'}>")
+                 f"{'true' if span > 2048 else 'false'}, {full}>")
         ktag = "scan_softlsh_filter"
     else:
         kname = "scan_lane_kernel<2>"

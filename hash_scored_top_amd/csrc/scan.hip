@@ -53,6 +53,17 @@ __device__ __forceinline__ float lds_f32_at(uint32_t addr) {
   return *(const __attribute__((address_space(3))) float*)static_cast<size_t>(addr);
 }
 
+// Element i of a global array, loaded as a global (not flat) access also
+// where the compiler cannot infer the pointer's address space.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p, long long i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((const __attribute__((address_space(1))) T*)p)[i];
+#else
+  return static_cast<const T*>(p)[i];
+#endif
+}
+
 // F16: value norms stored as binary16 (else float32); the raw bits are loaded
 // and converted only when used, so a load never waits for its own result.
 template <int LANES, int NT, int U, bool F16>
@@ -105,9 +116,8 @@ struct SoftScorer {
     for (int u = 0; u < U; ++u) {
       const int j0 = jb + u * KPI;
       const long long j = base + (j0 < jend ? j0 : jend - 1);
-      w[u] = idv[j * LANES + sub];
-      nr[u] = F16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(vnorm)[j])
-                  : static_cast<const uint32_t*>(vnorm)[j];
+      w[u] = ld_global<uint4>(idv, j * LANES + sub);
+      nr[u] = F16 ? static_cast<uint32_t>(ld_global<uint16_t>(vnorm, j)) : ld_global<uint32_t>(vnorm, j);
     }
   }
   // scores of the batch held in (w, nr) into out[j - j0]
@@ -201,6 +211,44 @@ __device__ __forceinline__ void soft_score_tiles(const S& sco, long long base, i
     if (it + 2 < NTILES) sco.load(wa, na, base, t1 + S::TILE + sco.grp, jend);
     if (it + 1 < NTILES && t1 < jend) sco.compute(wb, nb, t1 + sco.grp, jend, j0, out);
   }
+}
+
+// The same with the first two batches already loaded, (wa, na) and (wb, nb):
+// each set is reloaded right after its lookups, so one batch stays in flight
+// during each batch's lookups as above.
+template <int NTILES, class S, int U>
+__device__ __forceinline__ void soft_score_tiles2(const S& sco, long long base, int j0, int jend,
+                                                  uint4 (&wa)[U], uint32_t (&na)[U], uint4 (&wb)[U],
+                                                  uint32_t (&nb)[U], float* out) {
+#pragma unroll
+  for (int it = 0; it < NTILES; it += 2) {
+    const int t0 = j0 + it * S::TILE, t1 = t0 + S::TILE;
+    if (t0 < jend) sco.compute(wa, na, t0 + sco.grp, jend, j0, out);
+    if (it + 2 < NTILES) sco.load(wa, na, base, t1 + S::TILE + sco.grp, jend);
+    if (it + 1 < NTILES && t1 < jend) sco.compute(wb, nb, t1 + sco.grp, jend, j0, out);
+    if (it + 3 < NTILES) sco.load(wb, nb, base, t1 + 2 * S::TILE + sco.grp, jend);
+  }
+}
+
+// Table copy of exactly NT * 4 vectors: its loads, then the loads of the
+// scorer's second batch, then the LDS stores and a barrier that orders LDS
+// only.  The stores wait for the table's loads alone (the memory counter
+// counts loads in issue order), and the barrier does not wait for the
+// batch, which is still in flight when the lookups start.
+template <int NT, class S, int U>
+__device__ __forceinline__ void copy_table_then_load(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                     const S& sco, uint4 (&wb)[U], uint32_t (&nb)[U],
+                                                     long long base, int jb, int jend) {
+  u32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = src[u * NT + threadIdx.x];
+  sco.load(wb, nb, base, jb, jend);
+  asm volatile("" ::: "memory");  // the loads above stay ahead of the stores
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dst[u * NT + threadIdx.x] = v[u];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // The chunk's scores sit in LDS (tile[0..cnt)): write them out (coalesced)
@@ -353,7 +401,7 @@ __device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanT
 // Soft-LSH scan, L a multiple of 16.  grid (B*Hkv*nch [+ B*Hkv when filtering]);
 // chunk c of a head holds keys [c*span, (c+1)*span), span at most the default
 // chunk length (LONG false) or kSoftCap (LONG true).
-template <int LANES, int U, bool FILTER, bool F16, bool LONG>
+template <int LANES, int U, bool FILTER, bool F16, bool LONG, bool FULL>
 __global__ void __launch_bounds__(kScanNT) __attribute__((amdgpu_waves_per_eu(8, 8)))  // two workgroups per CU
 scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vnorm,
                     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq,
@@ -390,14 +438,25 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   sco.setup();
   uint4 w[U];
   uint32_t nr[U];
-  sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
-  {
-    const int nflt = S::L << a.P;  // a multiple of 16: L is
-    copy_to_lds<NT, 4>(reinterpret_cast<u32x4*>(tbl),
-                       reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt), nflt / 4);
+  const int nflt = S::L << a.P;               // a multiple of 16: L is
+  const u32x4* tsrc = reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt);
+  if constexpr (FULL && NTILES >= 2) {  // a full table (L = 64, P = 8): two batches in flight during its copy
+    // The metadata arguments are read-only and unaliased, so their loads
+    // count as invariant and the compiler may sink them past the barrier to
+    // their first use; pointers it cannot see through keep them where issued.
+    asm volatile("" : "+s"(sco.idv), "+s"(sco.vnorm));
+    uint4 w2[U];
+    uint32_t nr2[U];
+    sco.load(w, nr, base, j0 + sco.grp, jend);
+    copy_table_then_load<NT>(reinterpret_cast<u32x4*>(tbl), tsrc, sco, w2, nr2, base, j0 + S::TILE + sco.grp,
+                             jend);
+    soft_score_tiles2<NTILES>(sco, base, j0, jend, w, nr, w2, nr2, tile);
+  } else {
+    sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
+    copy_to_lds<NT, 4>(reinterpret_cast<u32x4*>(tbl), tsrc, nflt / 4);
+    __syncthreads();
+    soft_score_tiles<NTILES>(sco, base, j0, jend, w, nr, tile);
   }
-  __syncthreads();
-  soft_score_tiles<NTILES>(sco, base, j0, jend, w, nr, tile);
   __syncthreads();
   const uint32_t theta = filt ? theta_wait(a, bh, tl) : 0u;
   uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kSoftCap;
@@ -623,8 +682,12 @@ static hipError_t launch_scan_soft_f(dim3 grid, const FusedArgs& a, const uint8_
                                      float* sout, int nch, hipStream_t st) {
   const size_t smem = scan_smem(a.region_bytes, kSoftCap);
   // chunks up to the default length take the default tile count
-  auto kern = a.span > kSoftChunk ? scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, true>
-                                  : scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, false>;
+  auto kern = a.span > kSoftChunk ? scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, true, false>
+                                  : scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, false, false>;
+  if constexpr (LANES == 4)
+    if (a.P == 8)  // the full table: 16 * kScanNT vectors
+      kern = a.span > kSoftChunk ? scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, true, true>
+                                 : scan_softlsh_kernel<LANES, kScanSoftU, FILTER, F16, false, true>;
   hipError_t e = lds_limit(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(kScanNT), smem, st, ids, vnorm, sl, kps, sout, nch, a);
