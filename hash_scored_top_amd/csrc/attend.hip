@@ -129,17 +129,38 @@ __device__ __forceinline__ void merge_splits(const FusedArgs& a, int bh, long lo
   float pv[PL];
 #pragma unroll
   for (int u = 0; u < PL; ++u) pv[u] = has0 && u < nsplit ? load_dev(po0 + static_cast<long long>(u) * D) : 0.f;
-  // wave g forms the weights of query head g (lanes over the splits)
+  // wave g forms the weights of query head g (lanes over the splits).  The
+  // (m, l) pairs of the first 64 * SPL splits are loaded together, in one
+  // round trip; splits past those (nsplit > 128) are read twice.
+  constexpr int SPL = 2;
   for (int g = wave; g < G; g += NW) {
     const float* pml = a.part_ml + (qh0 + g) * nsplit * 2;
+    float mv[SPL], lv[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int s = lane + 64 * u;
+      mv[u] = s < nsplit ? load_dev(pml + 2 * s) : -INFINITY;
+      lv[u] = s < nsplit ? load_dev(pml + 2 * s + 1) : 0.f;
+    }
     float M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, load_dev(pml + 2 * s));
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) M = fmaxf(M, mv[u]);
+    for (int s = lane + 64 * SPL; s < nsplit; s += 64) M = fmaxf(M, load_dev(pml + 2 * s));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float L = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float mv = load_dev(pml + 2 * s);
-      const float w = mv == -INFINITY || M == -INFINITY ? 0.f : exp2f(mv - M);
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int s = lane + 64 * u;
+      if (s < nsplit) {
+        const float w = mv[u] == -INFINITY || M == -INFINITY ? 0.f : exp2f(mv[u] - M);
+        wt[g * nsplit + s] = w;
+        L += w * lv[u];
+      }
+    }
+    for (int s = lane + 64 * SPL; s < nsplit; s += 64) {
+      const float m1 = load_dev(pml + 2 * s);
+      const float w = m1 == -INFINITY || M == -INFINITY ? 0.f : exp2f(m1 - M);
       wt[g * nsplit + s] = w;
       L += w * load_dev(pml + 2 * s + 1);
     }

@@ -215,16 +215,20 @@ __device__ __forceinline__ void soft_score_tiles(const S& sco, long long base, i
 
 // The same with the first two batches already loaded, (wa, na) and (wb, nb):
 // each set is reloaded right after its lookups, so one batch stays in flight
-// during each batch's lookups as above.
-template <int NTILES, class S, int U>
+// during each batch's lookups as above.  late() runs once, before the
+// lookups of tile NTILES - 2 (or of the only tile).
+template <int NTILES, class S, int U, class F>
 __device__ __forceinline__ void soft_score_tiles2(const S& sco, long long base, int j0, int jend,
                                                   uint4 (&wa)[U], uint32_t (&na)[U], uint4 (&wb)[U],
-                                                  uint32_t (&nb)[U], float* out) {
+                                                  uint32_t (&nb)[U], float* out, F&& late) {
+  constexpr int kLate = NTILES >= 2 ? NTILES - 2 : 0;
 #pragma unroll
   for (int it = 0; it < NTILES; it += 2) {
     const int t0 = j0 + it * S::TILE, t1 = t0 + S::TILE;
+    if (it == kLate) late();
     if (t0 < jend) sco.compute(wa, na, t0 + sco.grp, jend, j0, out);
     if (it + 2 < NTILES) sco.load(wa, na, base, t1 + S::TILE + sco.grp, jend);
+    if (it + 1 == kLate) late();
     if (it + 1 < NTILES && t1 < jend) sco.compute(wb, nb, t1 + sco.grp, jend, j0, out);
     if (it + 3 < NTILES) sco.load(wb, nb, base, t1 + 2 * S::TILE + sco.grp, jend);
   }
@@ -384,10 +388,12 @@ __device__ void theta_publish(const FusedArgs& a, int bh, const int32_t* seq_len
 // Chunk workgroup: the head's threshold, once published (see above).  Past
 // the bounded wait the chunk filters with threshold 0 (every key a
 // candidate), which leaves the selection exact.
-__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanTail<kScanNT>& tl) {
+// pre: the threshold word as thread 0 read it earlier (0 if not read).
+__device__ __forceinline__ uint32_t theta_wait(const FusedArgs& a, int bh, ScanTail<kScanNT>& tl,
+                                               uint64_t pre = 0) {
   if (threadIdx.x == 0) {
-    uint64_t v = 0;
-    for (int i = 0; i < kThetaSpin; ++i) {
+    uint64_t v = pre;
+    for (int i = 0; (v >> 32) == 0 && i < kThetaSpin; ++i) {
       v = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (v >> 32) break;
       __builtin_amdgcn_s_sleep(4);
@@ -438,6 +444,7 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
   sco.setup();
   uint4 w[U];
   uint32_t nr[U];
+  uint64_t thv = 0;  // the threshold word, when read ahead
   const int nflt = S::L << a.P;               // a multiple of 16: L is
   const u32x4* tsrc = reinterpret_cast<const u32x4*>(a.tables + static_cast<long long>(bh) * nflt);
   if constexpr (FULL && NTILES >= 2) {  // a full table (L = 64, P = 8): two batches in flight during its copy
@@ -450,7 +457,12 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
     sco.load(w, nr, base, j0 + sco.grp, jend);
     copy_table_then_load<NT>(reinterpret_cast<u32x4*>(tbl), tsrc, sco, w2, nr2, base, j0 + S::TILE + sco.grp,
                              jend);
-    soft_score_tiles2<NTILES>(sco, base, j0, jend, w, nr, w2, nr2, tile);
+    // thread 0 reads the threshold word before the last full tile: a chunk
+    // that finishes late then finds theta without another round trip
+    soft_score_tiles2<NTILES>(sco, base, j0, jend, w, nr, w2, nr2, tile, [&] {
+      if (filt && threadIdx.x == 0)
+        thv = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
   } else {
     sco.load(w, nr, base, j0 + sco.grp, jend);  // first batch in flight during the table load
     copy_to_lds<NT, 4>(reinterpret_cast<u32x4*>(tbl), tsrc, nflt / 4);
@@ -458,7 +470,7 @@ scan_softlsh_kernel(const uint8_t* __restrict__ ids, const void* __restrict__ vn
     soft_score_tiles<NTILES>(sco, base, j0, jend, w, nr, tile);
   }
   __syncthreads();
-  const uint32_t theta = filt ? theta_wait(a, bh, tl) : 0u;
+  const uint32_t theta = filt ? theta_wait(a, bh, tl, thv) : 0u;
   uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kSoftCap;
   const int count = scan_chunk_epilogue<NT, false>(reinterpret_cast<const uint32_t*>(tile), jend - j0, j0, base,
                                                    reinterpret_cast<uint32_t*>(scores_out), theta, filt,
