@@ -39,6 +39,15 @@ static hipError_t set_smem(K kern, size_t bytes) {
   return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
 }
 
+// A workgroup barrier that orders LDS accesses only: unlike __syncthreads()
+// it does not wait for this thread's global loads (the sample loads stay in
+// flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sample size of head b (0 when no top-k follows or nothing is selected).
 __device__ __forceinline__ int sample_size(const FusedArgs& a, const int32_t* seq_lens,
                                            const int32_t* k_per_seq, int b, int& n) {
@@ -148,25 +157,33 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     HST_DCHECK(sp >= 0 && sp < n, kDbgSampleRow);
     return base + sp;
   };
+  // The loads are unconditional (an item this group does not read from its
+  // row reads the first W word instead), so that the memory counter knows how
+  // many are in flight: the LDS stores of W and q below wait for W and q
+  // alone, and the sample loads stay in flight until the scoring.
   uint32_t sid[kSPer][TG / 4];
-  uint32_t svr[kSPer];
-  if (S > 0) {
+  uint32_t svr[kSPer], svh[kSPer];  // low and high halves of the sampled value norms
+  {
+    const bool rd_id = S > 0 && fullg, rd_vn = S > 0 && j == 0 && !cards;
+    const unsigned char* dflt = reinterpret_cast<const unsigned char*>(wsrc);
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
       const int i = t + u * NT;
-      const long long row = item_row(i < S ? i : S - 1);
-      if (fullg) {
-        if constexpr (TG == 8) {
-          const uint2 v = *reinterpret_cast<const uint2*>(isrc + row * L + l0);
-          sid[u][0] = v.x;
-          sid[u][1] = v.y;
-        } else {
-          sid[u][0] = *reinterpret_cast<const uint32_t*>(isrc + row * L + l0);
-        }
+      const long long row = S > 0 ? item_row(i < S ? i : S - 1) : 0;
+      const unsigned char* ip = rd_id ? isrc + row * L + l0 : dflt;
+      if constexpr (TG == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(ip);
+        sid[u][0] = v.x;
+        sid[u][1] = v.y;
+      } else {
+        sid[u][0] = *reinterpret_cast<const uint32_t*>(ip);
       }
-      if (j == 0 && !cards)
-        svr[u] = norm_f16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(vnorm)[row])
-                          : static_cast<const uint32_t*>(vnorm)[row];
+      // the norm's two halves (binary16: the same half twice), both loaded
+      // whatever the storage type, so the count of loads is fixed
+      const unsigned char* vp =
+          rd_vn ? static_cast<const unsigned char*>(vnorm) + row * (norm_f16 ? 2 : 4) : dflt;
+      svr[u] = *reinterpret_cast<const uint16_t*>(vp);
+      svh[u] = *reinterpret_cast<const uint16_t*>(vp + (norm_f16 ? 0 : 2));
     }
   }
 
@@ -183,7 +200,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     const int e = u * NT + t;
     if (e < G * d) qn[e] = static_cast<double>(qv[u]);
   }
-  __syncthreads();
+  lds_barrier();
 
   // projections of the raw queries z[g][r] = W_r . q_g, r = ll * P + p: four
   // lanes per dot (interleaved 16-byte blocks of the row), each with its own
@@ -220,7 +237,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
     if (lane == 0) nrm[g] = sqrt(s2);
   }
-  __syncthreads();
+  lds_barrier();
 
   // one thread per (query head g, table ll, plane p): the logistic pair of
   // the plane (one exp: with e = exp(-|x|), sigma(|x|) = 1 / (1 + e) and
@@ -233,7 +250,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     const double big = 1.0 / (1.0 + e), small = e * big;
     lp[r] = x >= 0.0 ? make_double2(big, small) : make_double2(small, big);
   }
-  __syncthreads();
+  lds_barrier();
   // one thread per (query head g, table ll, half of the planes, bit pattern
   // b of the half): the product over the half's planes in plane order,
   // half[(g*hw + c)*8 + ll]
@@ -248,23 +265,33 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
       if (k < m) v *= ((b >> k) & 1) ? pp[k].x : pp[k].y;
     half[(g * hw + c) * TG + ll] = v;
   }
-  __syncthreads();
+  lds_barrier();
   // entries (bucket c, table l0 + ll), summed over the query heads in order;
   // to HBM (bucket-major) and to LDS as tl[c*TG + ((ll + c) % TG)] (rotated so
   // lanes with different buckets use different banks)
-  float* Tg = a.tables + static_cast<long long>(bh) * nb * L;
   for (int e = t; e < nb * lg; e += NT) {
     const int c = e / lg, ll = e % lg;
     double acc = 0.0;
     for (int g = 0; g < G; ++g)
       acc += half[(g * hw + (c & (nlo - 1))) * TG + ll] *
              half[(g * hw + nlo + (c >> plo)) * TG + ll];
-    const float v = static_cast<float>(acc);
-    Tg[c * L + l0 + ll] = v;
-    tl[c * TG + ((ll + c) & (TG - 1))] = v;
+    tl[c * TG + ((ll + c) & (TG - 1))] = static_cast<float>(acc);
   }
-  if (S == 0) return;
-  __syncthreads();
+  lds_barrier();
+  // the group's table to HBM, bucket-major (after the scoring below, which
+  // waits for the sample loads: stores issued before it would be waited for
+  // too)
+  float* Tg = a.tables + static_cast<long long>(bh) * nb * L;
+  const auto table_out = [&]() {
+    for (int e = t; e < nb * lg; e += NT) {
+      const int c = e / lg, ll = e % lg;
+      Tg[c * L + l0 + ll] = tl[c * TG + ((ll + c) & (TG - 1))];
+    }
+  };
+  if (S == 0) {
+    table_out();
+    return;
+  }
 
   // partial item scores on this group's tables
   const uint32_t idm = static_cast<uint32_t>(nb - 1);
@@ -296,10 +323,11 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     }
     if (j == 0 && !cards)
       a.svn[static_cast<long long>(bh) * kSample + i] =
-          norm_f16 ? f16_bits_to_f32(static_cast<uint16_t>(svr[u])) : __uint_as_float(svr[u]);
+          norm_f16 ? f16_bits_to_f32(static_cast<uint16_t>(svr[u])) : __uint_as_float(svr[u] | (svh[u] << 16));
   }
   if constexpr (CARDS)  // cards past the first kSPer * NT (the sample has at most kSample keys)
     for (int i = kSPer * NT + t; i < S; i += NT) part[i] = score_row(i);
+  table_out();
 }
 
 // ---------------------------------------------------------------------------
