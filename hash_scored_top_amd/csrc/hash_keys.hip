@@ -36,6 +36,16 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// A float64 moved across lanes by one DPP control (both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                     static_cast<uint32_t>(lo)));
+}
+
 template <typename Kern>
 static hipError_t set_lds_limit(Kern kern, size_t bytes) {
   return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);
@@ -531,6 +541,7 @@ __global__ void __launch_bounds__(256)
 value_norm_bf16_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ seq_lens, int Hkv,
                        int Nmax, void* __restrict__ vnorm) {
   constexpr int LPK = D / 8;           // lanes per key
+  static_assert(LPK == 8 || LPK == 16, "8 or 16 lanes per key");
   constexpr int RPI = 256 / LPK;       // rows per load instruction of the workgroup
   const int bh = blockIdx.y;
   const int b = bh / Hkv;
@@ -546,6 +557,10 @@ value_norm_bf16_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ s
     j = j < n ? j : n - 1;
     w[u] = *reinterpret_cast<const u32x4*>(Vw + j * (D / 2) + sub * 4);
   }
+  // lane 0 of each LPK-lane row group ends with the row's sum: row_shl moves
+  // within the 16-lane DPP row give lane 0 the operands of an xor butterfly
+  // (lane s adds lane s + m, whose bit m is clear on every lane lane 0 reads)
+  // without the LDS crossbar
 #pragma unroll
   for (int u = 0; u < kNormU; ++u) {
     double acc = 0.0;
@@ -555,8 +570,10 @@ value_norm_bf16_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ s
       acc = fma(lo, lo, acc);
       acc = fma(hi, hi, acc);
     }
-#pragma unroll
-    for (int m = LPK / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPK);
+    if constexpr (LPK == 16) acc += dpp_f64<0x108>(acc);  // row_shl 8
+    acc += dpp_f64<0x104>(acc);                            // row_shl 4
+    acc += dpp_f64<0x102>(acc);                            // row_shl 2
+    acc += dpp_f64<0x101>(acc);                            // row_shl 1
     const long long j = base + u * RPI + threadIdx.x / LPK;
     if (j < n && sub == 0) {
       const double r = sqrt(acc);
