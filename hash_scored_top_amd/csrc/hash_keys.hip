@@ -36,16 +36,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// A float64 moved across lanes by one DPP control (both halves).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
-  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                                                     static_cast<uint32_t>(lo)));
-}
-
 template <typename Kern>
 static hipError_t set_lds_limit(Kern kern, size_t bytes) {
   return raise_lds_limit(reinterpret_cast<const void*>(kern), bytes);

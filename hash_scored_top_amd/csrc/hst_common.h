@@ -71,6 +71,17 @@ __device__ __forceinline__ double to_f64(bf16 x) { return static_cast<double>(to
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// A float64 moved across lanes by one DPP control (both halves; a lane
+// whose source lane is outside its row reads 0).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                     static_cast<uint32_t>(lo)));
+}
+
 // Sum over each aligned group of W = 16 or 8 lanes, left in every lane
 // of the group: DPP quad permutes and row mirrors, no LDS traffic.
 template <int W>

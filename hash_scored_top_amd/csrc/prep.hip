@@ -68,22 +68,19 @@ __device__ __forceinline__ void reset_scan_state(const FusedArgs& a, int bh) {
 // soft-LSH tables (+ partial sample scores)
 
 struct TabSmem {
-  int wrows, qn, z, sg, lpair, half, tl, bytes;
+  int wrows, qn, lpair, half, tl, bytes;
 };
 
 // LDS map of one group of TG tables: W rows (padded by 16 bytes), q [G][d]
-// and the query norms [G] (float64), z [G][TG*P] (float64, unnormalised), the
-// logistic pairs [G][TG*P] (float64 x 2), half products [G][hw][TG]
-// (float64), the group's float32 table [2^P][TG].
+// (float64), the logistic pairs [G][TG*P] (float64 x 2), half products
+// [G][hw][TG] (float64), the group's float32 table [2^P][TG].
 __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int TG) {
   const int plo = P < 4 ? P : 4;
   const int hw = (1 << plo) + (1 << (P - plo));
   TabSmem m{};
   m.wrows = 0;
   m.qn = m.wrows + TG * P * (d * esize + 16);
-  m.sg = m.qn + G * d * 8;  // the G query norms
-  m.z = m.sg + G * 8;
-  m.lpair = m.z + G * TG * P * 8;
+  m.lpair = m.qn + G * d * 8;
   m.half = m.lpair + G * TG * P * 16;
   m.tl = m.half + G * hw * TG * 8;
   m.bytes = m.tl + (TG << P) * 4;
@@ -111,8 +108,6 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P, TG);
   const int rowb = d * static_cast<int>(sizeof(T)) + 16;
   double* qn = reinterpret_cast<double*>(sm + mp.qn);
-  double* zl = reinterpret_cast<double*>(sm + mp.z);
-  double* nrm = reinterpret_cast<double*>(sm + mp.sg);
   double* half = reinterpret_cast<double*>(sm + mp.half);
   float* tl = reinterpret_cast<float*>(sm + mp.tl);
 
@@ -204,16 +199,22 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
 
   // projections of the raw queries z[g][r] = W_r . q_g, r = ll * P + p: four
   // lanes per dot (interleaved 16-byte blocks of the row), each with its own
-  // partial sum; meanwhile waves g < G take the query norms (z / ||q|| is the
-  // projection of the normalised query)
-  for (int pr0 = 0; pr0 < G * R * 4; pr0 += NT) {  // uniform trip count (shuffles below)
+  // partial sums of the dot and of q_g's squares (the same four lanes read
+  // all of q_g), added over the four lanes by DPP quad permutations; then
+  // lane 0 of the four forms the logistic pair of the plane from
+  // z / ||q|| (the projection of the normalised query): one exp, with
+  // e = exp(-|x|), sigma(|x|) = 1 / (1 + e) and sigma(-|x|) = e / (1 + e),
+  // kept as (bit set, bit clear)
+  double2* lp = reinterpret_cast<double2*>(sm + mp.lpair);
+  for (int pr0 = 0; pr0 < G * R * 4; pr0 += NT) {  // uniform trip count (lane moves below)
     const int pq = pr0 + t, pr = pq >> 2, part = pq & 3;
-    double acc = 0.0;
+    double acc = 0.0, qsq = 0.0;
     if (pr < G * R) {
       const int g = pr / R, r = pr % R;
       const unsigned char* wr = sm + mp.wrows + r * rowb;
       const double* qq = qn + g * d;
       double ac[4] = {0.0, 0.0, 0.0, 0.0};  // four independent chains
+      double q2[4] = {0.0, 0.0, 0.0, 0.0};
       for (int cb = part; cb < d / E; cb += 4) {
         const u32x4 wv = *reinterpret_cast<const u32x4*>(wr + cb * 16);
         const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -222,33 +223,25 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
           float f;
           if (sizeof(T) == 2) f = (x & 1) ? bf16_hi(ww[x >> 1]) : bf16_lo(ww[x >> 1]);
           else f = __uint_as_float(ww[x]);
-          ac[x & 3] += static_cast<double>(f) * qq[cb * E + x];
+          const double qv = qq[cb * E + x];
+          ac[x & 3] += static_cast<double>(f) * qv;
+          q2[x & 3] += qv * qv;
         }
       }
       acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
+      qsq = (q2[0] + q2[1]) + (q2[2] + q2[3]);
     }
-    const double a1 = acc + __shfl_xor(acc, 1, 64);
-    const double a2 = a1 + __shfl_xor(a1, 2, 64);
-    if (pr < G * R && part == 0) zl[pr] = a2;  // zl[g * R + r]
-  }
-  for (int g = wave; g < G; g += NT / 64) {
-    double s2 = 0.0;
-    for (int c = lane; c < d; c += 64) s2 += qn[g * d + c] * qn[g * d + c];
-    for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
-    if (lane == 0) nrm[g] = sqrt(s2);
-  }
-  lds_barrier();
-
-  // one thread per (query head g, table ll, plane p): the logistic pair of
-  // the plane (one exp: with e = exp(-|x|), sigma(|x|) = 1 / (1 + e) and
-  // sigma(-|x|) = e / (1 + e)), kept in the z slot as (bit set, bit clear)
-  double2* lp = reinterpret_cast<double2*>(sm + mp.lpair);
-  for (int r = t; r < G * R; r += NT) {
-    const double nq = nrm[r / R];
-    const double x = nq > 0.0 ? 2.0 * (zl[r] / nq) * a.inv_tau : 0.0;
-    const double e = exp(-fabs(x));
-    const double big = 1.0 / (1.0 + e), small = e * big;
-    lp[r] = x >= 0.0 ? make_double2(big, small) : make_double2(small, big);
+    const double a1 = acc + dpp_f64<0xB1>(acc);  // quad [1,0,3,2]: the xor-1 lane
+    const double z = a1 + dpp_f64<0x4E>(a1);     // quad [2,3,0,1]: the xor-2 lane
+    const double s1 = qsq + dpp_f64<0xB1>(qsq);
+    const double n2 = s1 + dpp_f64<0x4E>(s1);
+    if (pr < G * R && part == 0) {
+      const double nq = sqrt(n2);
+      const double x = nq > 0.0 ? 2.0 * (z / nq) * a.inv_tau : 0.0;
+      const double e = exp(-fabs(x));
+      const double big = 1.0 / (1.0 + e), small = e * big;
+      lp[pr] = x >= 0.0 ? make_double2(big, small) : make_double2(small, big);
+    }
   }
   lds_barrier();
   // one thread per (query head g, table ll, half of the planes, bit pattern
