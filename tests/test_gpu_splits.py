@@ -4,9 +4,9 @@ The attention splits of a kv head each select the head's rows, gather their
 part of the index row, and the last one to finish merges the others (SOCKET
 overview page, "Core mechanism: soft LSH", item 4: exact attention over the
 selected subset, split-K with a log-sum-exp merge).  The split count follows
-the rows per head: a single split (k = 40), the usual many splits, and splits
+the rows per head: a single split (k = 40), the usual many splits, splits
 of more than 1024 rows each when the heads are many (so that one round of
-workgroups holds them all).  Each case checks every slab: the index row
+workgroups holds them all), and more than 128 splits of one head.  Each case checks every slab: the index row
 (ascending, -1 padded, equal to the oracle's up to near-ties for soft-LSH,
 bit-exact for binary codes) and the attention over the GPU's own selected set.
 """
@@ -29,6 +29,10 @@ ONE_SPLIT = dataclasses.replace(WL.WORKLOADS["llama8b_softlsh_b8_n32k"], name="o
                                 Hkv=2, N=6000, needles=4, ragged=(3000, 6000), sparsity=150.0, seed=211)
 WIDE_SOFT = dataclasses.replace(WL.WORKLOADS["llama8b_softlsh_b8_n32k"], name="wide_soft", B=8, Hq=32,
                                 Hkv=8, N=8400, needles=4, ragged=None, sparsity=2.0, seed=212)
+# one kv head, half its keys selected: about 157 splits of 64 rows, more
+# than the 128 whose (m, l) pairs the merging split loads in one round trip
+MANY_SPLITS = dataclasses.replace(WL.WORKLOADS["llama8b_softlsh_b8_n32k"], name="many_splits", B=1, Hq=4,
+                                  Hkv=1, N=20000, needles=4, ragged=None, sparsity=2.0, seed=214)
 WIDE_HAM = dataclasses.replace(WL.WORKLOADS["hata_hamming_b16_n64k"], name="wide_ham", B=16, Hq=16,
                                Hkv=8, N=6000, needles=4, ragged=None, sparsity=2.0, seed=213)
 
@@ -47,7 +51,7 @@ def _check_rows(idx, kb, n):
     return got
 
 
-@pytest.mark.parametrize("w", [ONE_SPLIT, WIDE_SOFT], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [ONE_SPLIT, WIDE_SOFT, MANY_SPLITS], ids=lambda w: w.name)
 def test_softlsh_step_split_regimes(w):
     import hash_scored_top_amd as hst
     x = WL.make_full(w)
