@@ -36,7 +36,7 @@ struct HeadState {
 static_assert(sizeof(HeadState) == 64, "head state stride");
 
 struct FusedLayout {
-  size_t off_heads, off_tables, off_qcodes, off_spart, off_svn, off_counts, off_slots, off_part_o,
+  size_t off_heads, off_tables, off_qcodes, off_spart, off_counts, off_slots, off_part_o,
       off_part_ml, bytes;
   int chunk;    // candidate slots per scan chunk (the stride of the slot array)
   int nchunks;  // scan chunks per head at the default chunk length (the most there can be)
@@ -55,7 +55,6 @@ struct FusedArgs {
   float* spart;      // [B*Hkv][xparts][kSample]: partial sample scores, one part per prep workgroup
                      //   (soft-LSH: tables of the workgroup; binary codes: its 16 code bits;
                      //   given scores: part 0 holds the order keys' bits)
-  float* svn;        // [B*Hkv][kSample]: value norms of the sampled keys (soft-LSH)
   uint32_t* counts;  // [B*Hkv][nchunks]
   uint2* slots;      // [B*Hkv][nchunks][chunk] (order key, index), chunk c holding keys [c*span, (c+1)*span)
   float* part_o;     // [B*Hq][nsplit][d]
@@ -100,8 +99,7 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap);
 
 // kernel launchers (prep.hip, scan.hip, attend.hip)
 hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* q, const void* W,
-                            const uint8_t* ids, const void* vnorm, int norm_f16,
-                            const int32_t* kps, hipStream_t st);
+                            const uint8_t* ids, const int32_t* kps, hipStream_t st);
 hipError_t launch_prep_hamming(const hst_shape& s, const FusedArgs& a, const void* q, const void* R,
                                const uint32_t* codes, const int32_t* kps, hipStream_t st);
 hipError_t launch_prep_given(const hst_shape& s, const FusedArgs& a, int score_dtype,

@@ -41,7 +41,6 @@ FusedLayout fused_layout(const hst_shape& s, int op, int L, int P, int kcap) {
   if (select) {
     f.xparts = prep_parts(f.kind, L);
     f.off_spart = take(BH * static_cast<size_t>(f.xparts) * kSample * 4);
-    if (soft) f.off_svn = take(BH * static_cast<size_t>(kSample) * 4);
   }
   if (select) {
     f.off_counts = take(BH * f.nchunks * 4);
@@ -95,7 +94,6 @@ static FusedArgs make_args(const hst_shape& s, const FusedLayout& f, void* ws, i
     a.tables = reinterpret_cast<float*>(p + f.off_tables);
     a.qcodes = reinterpret_cast<uint32_t*>(p + f.off_qcodes);
     a.spart = reinterpret_cast<float*>(p + f.off_spart);
-    a.svn = reinterpret_cast<float*>(p + f.off_svn);
     a.counts = reinterpret_cast<uint32_t*>(p + f.off_counts);
     a.slots = reinterpret_cast<uint2*>(p + f.off_slots);
     a.part_o = reinterpret_cast<float*>(p + f.off_part_o);
@@ -137,7 +135,7 @@ hipError_t decode_prepare_softlsh(const hst_shape& s, const void* q, const void*
                                   double tau, const uint8_t* ids, const void* vnorm, int norm_dtype,
                                   int kcap, const int32_t* kps, void* ws, hipStream_t st) {
   const FusedArgs a = soft_args(s, ws, L, P, tau, kcap, ids, vnorm, norm_dtype, nullptr);
-  return launch_prep_soft(s, a, q, W, ids, vnorm, norm_dtype == HST_F16, kps, st);
+  return launch_prep_soft(s, a, q, W, ids, kps, st);
 }
 
 hipError_t decode_filter_softlsh(const hst_shape& s, int L, int P, const uint8_t* ids,
@@ -180,7 +178,7 @@ hipError_t fused_decode_softlsh_mass(const hst_shape& s, const void* q, const vo
   int32_t* cand = reinterpret_cast<int32_t*>(base + align256(f.bytes));
   const size_t ncand = static_cast<size_t>(s.B) * s.Hkv * static_cast<size_t>(kcap) * 4;
   double* logits = reinterpret_cast<double*>(base + align256(f.bytes) + align256(ncand));
-  HST_CHECK(launch_prep_soft(s, a, q, W, ids, vnorm, f16, kps, st));
+  HST_CHECK(launch_prep_soft(s, a, q, W, ids, kps, st));
   HST_CHECK(launch_scan(s, a, f.kind, ids, vnorm, f16, nullptr, 1, kps, st));
   HST_CHECK(launch_select_only(s, a, cand, nullptr, 0, f.chunk, st));
   HST_CHECK(launch_select_mass(s, q, K, cand, kcap, p, scale, idx, counts, logits, st));
@@ -245,7 +243,7 @@ hipError_t fused_decode_softlsh_routed(const hst_shape& s, const void* q, const 
   as.cids = cids;
   as.cpart = reinterpret_cast<float*>(base + r.cpart);
   as.ncards = route_chunks(s.Nmax);
-  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, 0, nullptr, st));
+  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, st));
   // the C best chunks kept; then the k best keys inside
   HST_CHECK(launch_card_route(s, as.cpart, as.xparts, cw, f16, C, chunks, st));
   HST_CHECK(launch_route_scan(s, tables, chunks, C, ids, vnorm, f16, L, P, C * 64, tscore, st));
@@ -310,7 +308,7 @@ hipError_t fused_decode_softlsh_shared(const hst_shape& s, int Np, const void* q
   const FusedLayout fs = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   FusedArgs as = make_args(s, fs, nullptr, L, P, tau, 1);
   as.tables = tables;
-  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, 0, nullptr, st));
+  HST_CHECK(launch_prep_soft(s, as, q, W, nullptr, nullptr, st));
   if (s.seq_lens != nullptr) HST_CHECK(launch_shared_lens(s, Np, vlens, st));
   HST_CHECK(launch_scan_shared(s, as, Np, ids_p, vn_p, ids_s, vn_s, norm_dtype == HST_F16, scores,
                                st));
@@ -432,7 +430,7 @@ hipError_t fused_score_softlsh(const hst_shape& s, const void* q, const void* W,
                                float* scores, void* ws, hipStream_t st) {
   const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   const FusedArgs a = make_args(s, f, ws, L, P, tau, 1);
-  HST_CHECK(launch_prep_soft(s, a, q, W, nullptr, nullptr, 0, nullptr, st));
+  HST_CHECK(launch_prep_soft(s, a, q, W, nullptr, nullptr, st));
   return launch_scan(s, a, f.kind, ids, vnorm, norm_dtype == HST_F16, scores, 0, nullptr, st);
 }
 
@@ -449,7 +447,7 @@ hipError_t fused_tables_softlsh(const hst_shape& s, const void* q, const void* W
   const FusedLayout f = fused_layout(s, HST_OP_SCORE_SOFTLSH, L, P, 1);
   FusedArgs a = make_args(s, f, nullptr, L, P, tau, 1);
   a.tables = tables;
-  return launch_prep_soft(s, a, q, W, nullptr, nullptr, 0, nullptr, st);
+  return launch_prep_soft(s, a, q, W, nullptr, nullptr, st);
 }
 
 hipError_t fused_scan_softlsh(const hst_shape& s, const float* tables, int L, int P,

@@ -91,8 +91,9 @@ __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int 
 // set) instead of the key sample.
 template <typename T, int TG, bool CARDS>
 __global__ void __launch_bounds__(kPrepNT)
+__attribute__((amdgpu_waves_per_eu(TG == 4 ? 8 : 1)))  // four groups of 4 tables per CU (64 VGPRs)
 prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8_t* __restrict__ ids,
-                   const void* __restrict__ vnorm, int norm_f16, const int32_t* __restrict__ seq_lens,
+                   const int32_t* __restrict__ seq_lens,
                    const int32_t* __restrict__ k_per_seq, FusedArgs a) {
   constexpr int NT = kPrepNT;
   constexpr int E = 16 / static_cast<int>(sizeof(T));
@@ -157,9 +158,8 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   // many are in flight: the LDS stores of W and q below wait for W and q
   // alone, and the sample loads stay in flight until the scoring.
   uint32_t sid[kSPer][TG / 4];
-  uint32_t svr[kSPer], svh[kSPer];  // low and high halves of the sampled value norms
   {
-    const bool rd_id = S > 0 && fullg, rd_vn = S > 0 && j == 0 && !cards;
+    const bool rd_id = S > 0 && fullg;
     const unsigned char* dflt = reinterpret_cast<const unsigned char*>(wsrc);
 #pragma unroll
     for (int u = 0; u < kSPer; ++u) {
@@ -173,12 +173,6 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
       } else {
         sid[u][0] = *reinterpret_cast<const uint32_t*>(ip);
       }
-      // the norm's two halves (binary16: the same half twice), both loaded
-      // whatever the storage type, so the count of loads is fixed
-      const unsigned char* vp =
-          rd_vn ? static_cast<const unsigned char*>(vnorm) + row * (norm_f16 ? 2 : 4) : dflt;
-      svr[u] = *reinterpret_cast<const uint16_t*>(vp);
-      svh[u] = *reinterpret_cast<const uint16_t*>(vp + (norm_f16 ? 0 : 2));
     }
   }
 
@@ -314,9 +308,6 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     } else {
       part[i] = score_row(i);
     }
-    if (j == 0 && !cards)
-      a.svn[static_cast<long long>(bh) * kSample + i] =
-          norm_f16 ? f16_bits_to_f32(static_cast<uint16_t>(svr[u])) : __uint_as_float(svr[u] | (svh[u] << 16));
   }
   if constexpr (CARDS)  // cards past the first kSPer * NT (the sample has at most kSample keys)
     for (int i = kSPer * NT + t; i < S; i += NT) part[i] = score_row(i);
@@ -432,8 +423,7 @@ int prep_parts(int kind, int L) {
 }
 
 hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* q, const void* W,
-                            const uint8_t* ids, const void* vnorm, int norm_f16,
-                            const int32_t* kps, hipStream_t st) {
+                            const uint8_t* ids, const int32_t* kps, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
   // x = (sequence, kv head): workgroups are handed to the XCDs round robin in
   // linear order, so the parts of one head (B*Hkv apart) share an XCD and its
@@ -448,7 +438,7 @@ hipError_t launch_prep_soft(const hst_shape& s, const FusedArgs& a, const void* 
     hipError_t e = set_smem(kern, smem);                                                       \
     if (e != hipSuccess) return e;                                                             \
     hipLaunchKernelGGL(kern, grid, dim3(kPrepNT), smem, st, static_cast<const TT*>(q),         \
-                       static_cast<const TT*>(W), ids, vnorm, norm_f16, s.seq_lens, kps, a);   \
+                       static_cast<const TT*>(W), ids, s.seq_lens, kps, a);                  \
   } while (0)
   if (s.kv_dtype == HST_F32) {
     if (TG == 8) HST_PREP(float, 8);

@@ -316,7 +316,8 @@ __device__ __forceinline__ ScanWork scan_work(bool filt, int BH, int nch) {
 }
 
 // Candidate threshold of head bh: the sample scores are the sums of the
-// parts prep wrote (times the sampled value norm for soft-LSH), and theta is
+// parts prep wrote (times the sampled key's value norm, read from a.meta_vn,
+// for soft-LSH), and theta is
 // a lower bound of the sample score at a high-margin rank.  The bin width of
 // the selection's candidate histogram (shift) spreads [theta, the sample's
 // largest key] over half the bins.  Every thread of the workgroup calls;
@@ -345,10 +346,23 @@ __device__ uint32_t sample_theta(const FusedArgs& a, int bh, int n, int k_eff, u
     for (int e = 0; e < PER; ++e)
 #pragma unroll
       for (int x = 0; x < kMaxParts; ++x) pv[e][x] = part[(x < X ? x : X - 1) * kSample + t + e * NT];
+    // soft-LSH: the sampled keys' value norms, read at their positions
+    // (issued with the parts; this workgroup starts before the chunk
+    // workgroups' key stream)
     float vn[PER];
-    if (KIND != kScanHamming)
+    if (KIND != kScanHamming) {
+      uint32_t vb[PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) vn[e] = a.svn[static_cast<long long>(bh) * kSample + t + e * NT];
+      for (int e = 0; e < PER; ++e) {
+        const int i = t + e * NT;
+        const long long row = static_cast<long long>(bh) * a.Nmax + sample_pos(i < S ? i : S - 1, S, n);
+        vb[e] = a.meta_f16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(a.meta_vn)[row])
+                           : static_cast<const uint32_t*>(a.meta_vn)[row];
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        vn[e] = a.meta_f16 ? f16_bits_to_f32(static_cast<uint16_t>(vb[e])) : __uint_as_float(vb[e]);
+    }
     const int G = a.Hq / a.Hkv;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -748,6 +762,10 @@ hipError_t launch_scan(const hst_shape& s, const FusedArgs& a_in, int kind, cons
   const uint8_t* ids = static_cast<const uint8_t*>(src);
   float* sout = static_cast<float*>(scores_out);
   const int32_t* sl = s.seq_lens;
+  if (kind == kScanSoftFast || kind == kScanSoftAny) {  // the threshold reads the sampled norms
+    a.meta_vn = vnorm;
+    a.meta_f16 = norm_f16;
+  }
   switch (kind) {
     case kScanSoftFast:
       switch (a.L) {
