@@ -550,7 +550,13 @@ value_norm_bf16_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ s
   // lane 0 of each LPK-lane row group ends with the row's sum: row_shl moves
   // within the 16-lane DPP row give lane 0 the operands of an xor butterfly
   // (lane s adds lane s + m, whose bit m is clear on every lane lane 0 reads)
-  // without the LDS crossbar
+  // without the LDS crossbar.  Row u's sum then moves to lane u % LPK of the
+  // group (row_shr), so that each lane takes the square root and the
+  // rounding of kNormU / LPK rows instead of every lane doing all of them.
+  constexpr int RPL = kNormU / LPK;  // rows per lane
+  double mine[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) mine[m] = 0.0;
 #pragma unroll
   for (int u = 0; u < kNormU; ++u) {
     double acc = 0.0;
@@ -564,9 +570,14 @@ value_norm_bf16_kernel(const bf16* __restrict__ V, const int32_t* __restrict__ s
     acc += dpp_f64<0x104>(acc);                            // row_shl 4
     acc += dpp_f64<0x102>(acc);                            // row_shl 2
     acc += dpp_f64<0x101>(acc);                            // row_shl 1
-    const long long j = base + u * RPI + threadIdx.x / LPK;
-    if (j < n && sub == 0) {
-      const double r = sqrt(acc);
+    const double moved = u % LPK == 0 ? acc : dpp_f64_row_shr(acc, u % LPK);
+    if (sub == u % LPK) mine[u / LPK] = moved;
+  }
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) {
+    const long long j = base + (m * LPK + sub) * RPI + threadIdx.x / LPK;
+    if (j < n) {
+      const double r = sqrt(mine[m]);
       const long long o = static_cast<long long>(bh) * Nmax + j;
       if (F16OUT)
         static_cast<uint16_t*>(vnorm)[o] = f64_to_f16_bits(r);

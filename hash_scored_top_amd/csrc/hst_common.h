@@ -72,14 +72,36 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // A float64 moved across lanes by one DPP control (both halves; a lane
-// whose source lane is outside its row reads 0).
+// whose source lane is outside its row reads 0, by bound_ctrl).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u), CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(u), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(u >> 32), CTRL, 0xf, 0xf, true);
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
                                                      static_cast<uint32_t>(lo)));
+}
+
+// dpp_f64 with row_shr:s (1 <= s <= 15): lane i of a 16-lane row takes lane
+// i - s of the row (lanes i < s read 0).  s must fold to a constant.
+__device__ __forceinline__ double dpp_f64_row_shr(double v, int s) {
+  switch (s) {
+    case 1: return dpp_f64<0x111>(v);
+    case 2: return dpp_f64<0x112>(v);
+    case 3: return dpp_f64<0x113>(v);
+    case 4: return dpp_f64<0x114>(v);
+    case 5: return dpp_f64<0x115>(v);
+    case 6: return dpp_f64<0x116>(v);
+    case 7: return dpp_f64<0x117>(v);
+    case 8: return dpp_f64<0x118>(v);
+    case 9: return dpp_f64<0x119>(v);
+    case 10: return dpp_f64<0x11a>(v);
+    case 11: return dpp_f64<0x11b>(v);
+    case 12: return dpp_f64<0x11c>(v);
+    case 13: return dpp_f64<0x11d>(v);
+    case 14: return dpp_f64<0x11e>(v);
+    default: return dpp_f64<0x11f>(v);
+  }
 }
 
 // Sum over each aligned group of W = 16 or 8 lanes, left in every lane
