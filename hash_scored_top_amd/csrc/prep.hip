@@ -71,19 +71,20 @@ struct TabSmem {
   int wrows, qn, lpair, half, tl, bytes;
 };
 
-// LDS map of one group of TG tables: W rows (padded by 16 bytes), q [G][d]
+// LDS map of one group of TG tables: W rows (padded by 64 bytes), q [G][d]
 // (float64), the logistic pairs [G][TG*P] (float64 x 2), half products
-// [G][hw][TG] (float64), the group's float32 table [2^P][TG].
+// [G][hw][TG] (float64), the group's float32 table [TG][2^P + 1]
+// (table-major, rows padded by one word).
 __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int TG) {
   const int plo = P < 4 ? P : 4;
   const int hw = (1 << plo) + (1 << (P - plo));
   TabSmem m{};
   m.wrows = 0;
-  m.qn = m.wrows + TG * P * (d * esize + 16);
+  m.qn = m.wrows + TG * P * (d * esize + 64);
   m.lpair = m.qn + G * d * 8;
   m.half = m.lpair + G * TG * P * 16;
   m.tl = m.half + G * hw * TG * 8;
-  m.bytes = m.tl + (TG << P) * 4;
+  m.bytes = m.tl + TG * ((1 << P) + 1) * 4;
   return m;
 }
 
@@ -107,7 +108,10 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
 
   const int plo = P < 4 ? P : 4, phi = P - plo, nlo = 1 << plo, hw = nlo + (1 << phi);
   const TabSmem mp = tab_smem(G, d, static_cast<int>(sizeof(T)), P, TG);
-  const int rowb = d * static_cast<int>(sizeof(T)) + 16;
+  // W rows padded by 64 bytes: the four lanes of a dot product read blocks
+  // cb, cb + 4, ... of four consecutive rows at once, and a row stride of 16
+  // words (mod the 64 banks) keeps those sixteen 16-byte reads apart
+  const int rowb = d * static_cast<int>(sizeof(T)) + 64;
   double* qn = reinterpret_cast<double*>(sm + mp.qn);
   double* half = reinterpret_cast<double*>(sm + mp.half);
   float* tl = reinterpret_cast<float*>(sm + mp.tl);
@@ -253,16 +257,18 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     half[(g * hw + c) * TG + ll] = v;
   }
   lds_barrier();
-  // entries (bucket c, table l0 + ll), summed over the query heads in order;
-  // to HBM (bucket-major) and to LDS as tl[c*TG + ((ll + c) % TG)] (rotated so
-  // lanes with different buckets use different banks)
-  for (int e = t; e < nb * lg; e += NT) {
-    const int c = e / lg, ll = e % lg;
+  // entries (bucket c, table l0 + ll), summed over the query heads in order,
+  // to LDS table-major as tl[ll*(2^P + 1) + c]: a lookup's bank follows its
+  // bucket over all 64 banks (bucket-major rows of TG words used 16), and
+  // the pad puts the TG entries of one bucket in different banks
+  const int tls = nb + 1;  // LDS row of one table
+  for (int e = t; e < nb * lg; e += NT) {  // consecutive lanes, consecutive buckets
+    const int ll = e / nb, c = e % nb;
     double acc = 0.0;
     for (int g = 0; g < G; ++g)
       acc += half[(g * hw + (c & (nlo - 1))) * TG + ll] *
              half[(g * hw + nlo + (c >> plo)) * TG + ll];
-    tl[c * TG + ((ll + c) & (TG - 1))] = static_cast<float>(acc);
+    tl[ll * tls + c] = static_cast<float>(acc);
   }
   lds_barrier();
   // the group's table to HBM, bucket-major (after the scoring below, which
@@ -272,7 +278,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   const auto table_out = [&]() {
     for (int e = t; e < nb * lg; e += NT) {
       const int c = e / lg, ll = e % lg;
-      Tg[c * L + l0 + ll] = tl[c * TG + ((ll + c) & (TG - 1))];
+      Tg[c * L + l0 + ll] = tl[ll * tls + c];
     }
   };
   if (S == 0) {
@@ -289,7 +295,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     float s2[2] = {0.f, 0.f};
     for (int ll = 0; ll < lg; ++ll) {
       const int c = static_cast<int>(row[ll] & idm);
-      s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
+      s2[ll & 1] += tl[ll * tls + c];
     }
     return s2[0] + s2[1];
   };
@@ -302,7 +308,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
 #pragma unroll
       for (int ll = 0; ll < TG; ++ll) {
         const int c = static_cast<int>((sid[u][ll >> 2] >> (8 * (ll & 3))) & idm);
-        s2[ll & 1] += tl[c * TG + ((ll + c) & (TG - 1))];
+        s2[ll & 1] += tl[ll * tls + c];
       }
       part[i] = s2[0] + s2[1];
     } else {
