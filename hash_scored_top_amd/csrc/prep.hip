@@ -73,7 +73,7 @@ struct TabSmem {
 
 // LDS map of one group of TG tables: W rows (padded by 64 bytes), q [G][d]
 // (float64), the logistic pairs [G][TG*P] (float64 x 2), half products
-// [G][hw][TG] (float64), the group's float32 table [TG][2^P + 1]
+// [G][TG][hw] (float64), the group's float32 table [TG][2^P + 1]
 // (table-major, rows padded by one word).
 __host__ __device__ inline TabSmem tab_smem(int G, int d, int esize, int P, int TG) {
   const int plo = P < 4 ? P : 4;
@@ -244,7 +244,8 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
   lds_barrier();
   // one thread per (query head g, table ll, half of the planes, bit pattern
   // b of the half): the product over the half's planes in plane order,
-  // half[(g*hw + c)*8 + ll]
+  // half[(g*TG + ll)*hw + c] (the table phase reads consecutive buckets'
+  // halves of one table from consecutive lanes)
   for (int e = t; e < G * lg * hw; e += NT) {
     const int g = e / (lg * hw), rem = e % (lg * hw), ll = rem / hw, c = rem % hw;
     const bool hi = c >= nlo;
@@ -254,7 +255,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       if (k < m) v *= ((b >> k) & 1) ? pp[k].x : pp[k].y;
-    half[(g * hw + c) * TG + ll] = v;
+    half[(g * TG + ll) * hw + c] = v;
   }
   lds_barrier();
   // entries (bucket c, table l0 + ll), summed over the query heads in order,
@@ -266,8 +267,7 @@ prep_tables_kernel(const T* __restrict__ q, const T* __restrict__ W, const uint8
     const int ll = e / nb, c = e % nb;
     double acc = 0.0;
     for (int g = 0; g < G; ++g)
-      acc += half[(g * hw + (c & (nlo - 1))) * TG + ll] *
-             half[(g * hw + nlo + (c >> plo)) * TG + ll];
+      acc += half[(g * TG + ll) * hw + (c & (nlo - 1))] * half[(g * TG + ll) * hw + nlo + (c >> plo)];
     tl[ll * tls + c] = static_cast<float>(acc);
   }
   lds_barrier();
