@@ -589,6 +589,22 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   if (j0 >= n) return;
   const int jend = min(j0 + a.span, n);
   const long long base = static_cast<long long>(bh) * a.Nmax;
+  // codes / given scores: the first four keys of each thread are loaded
+  // before the query codes, so both arrive in one round trip
+  uint4 c[4];
+  uint32_t gv[4];
+  const auto load4 = [&](int jb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = jb + u * NT;
+      if (j < jend) {
+        if (KIND == kScanHamming) c[u] = static_cast<const uint4*>(src)[base + j];
+        else gv[u] = static_cast<const uint32_t*>(src)[base + j];
+      }
+    }
+  };
+  const int jfirst = j0 + static_cast<int>(threadIdx.x);
+  if (KIND != kScanSoftAny) load4(jfirst);
   if (KIND == kScanSoftAny) {
     const int nflt = a.L << a.P;
     const float* s = a.tables + static_cast<long long>(bh) * nflt;
@@ -608,18 +624,9 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
       tile[j - j0] = __float_as_uint(acc * vn);
     }
   } else {
-    // four keys per thread in flight
-    for (int jb = j0 + static_cast<int>(threadIdx.x); jb < jend; jb += 4 * NT) {
-      uint4 c[4];
-      uint32_t gv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = jb + u * NT;
-        if (j < jend) {
-          if (KIND == kScanHamming) c[u] = static_cast<const uint4*>(src)[base + j];
-          else gv[u] = static_cast<const uint32_t*>(src)[base + j];
-        }
-      }
+    // four keys per thread in flight (the first four already loaded)
+    for (int jb = jfirst; jb < jend; jb += 4 * NT) {
+      if (jb != jfirst) load4(jb);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = jb + u * NT;
