@@ -605,6 +605,11 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
   };
   const int jfirst = j0 + static_cast<int>(threadIdx.x);
   if (KIND != kScanSoftAny) load4(jfirst);
+  // the threshold word, read ahead: workgroups that start after the
+  // threshold workgroups have published it skip the epilogue's round trip
+  uint64_t thv = 0;
+  if (filt && threadIdx.x == 0)
+    thv = __hip_atomic_load(&a.heads[bh].thr_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (KIND == kScanSoftAny) {
     const int nflt = a.L << a.P;
     const float* s = a.tables + static_cast<long long>(bh) * nflt;
@@ -644,7 +649,7 @@ scan_lane_kernel(const void* __restrict__ src, const void* __restrict__ vnorm, i
     }
   }
   __syncthreads();
-  const uint32_t theta = filt ? theta_wait(a, bh, tl) : 0u;
+  const uint32_t theta = filt ? theta_wait(a, bh, tl, thv) : 0u;
   uint2* slot = a.slots + (static_cast<long long>(bh) * a.nchunks + chunk) * kLaneCap;
   const int count = scan_chunk_epilogue<NT, KINT>(tile, jend - j0, j0, base, scores_out, theta, filt,
                                                   slot, sc);
