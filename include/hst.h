@@ -414,13 +414,15 @@ hst_status hst_workspace_size_shared(const hst_shape* shape, int Np, int L,
  * workspace, so a caller may put other work between them but must not reuse
  * the workspace in between.
  *   prepare: the query tables [SOCKET, core mechanism item 2] (or the query
- *            codes [HATA, section 3]) and the scores of a fixed sample of
- *            2048 keys per (sequence, kv head), which bound the top-k
- *            threshold from below;
- *   filter:  every key scored once [SOCKET, item 3; HATA, section 3]; the
- *            keys scoring at or above the threshold are kept as candidates,
- *            in index order, with a histogram of their scores (the exactness
- *            of the selection never depends on the threshold);
+ *            codes [HATA, section 3]) and, per table group (code slice),
+ *            the parts of the scores of a fixed sample of 2048 keys per
+ *            (sequence, kv head);
+ *   filter:  the sample's scores (the parts added up, times the sampled
+ *            keys' value norms for soft-LSH) give a threshold below the
+ *            k-th score; every key is scored once [SOCKET, item 3; HATA,
+ *            section 3]; the keys scoring at or above the threshold are kept
+ *            as candidates, in index order (the exactness of the selection
+ *            never depends on the threshold);
  *   finish:  the exact top-k of the candidates (or of every key, rescored,
  *            when fewer than k_b keys passed the threshold) and exact
  *            attention over them [SOCKET, item 4]; idx, out, lse as for the
