@@ -772,10 +772,13 @@ __device__ __forceinline__ int candidates_to_lds(const FusedArgs& a, int bh, int
   // unused), and the counts, issued first, arrive without waiting for the
   // slots
   constexpr int PX = NT >= 1024 ? 2 : 3;  // (1024-thread workgroups hold 128 VGPRs)
-  const int cnt0 = static_cast<int>(threadIdx.x) < nch ? static_cast<int>(cnt[threadIdx.x]) : 0;
+  // (the loads are bounded by the workspace's chunk count, not by nch, so
+  // they do not wait for the sequence length; entries past nch are unused)
+  const int cnt_ld = static_cast<int>(threadIdx.x) < a.nchunks ? static_cast<int>(cnt[threadIdx.x]) : 0;
+  const int cnt0 = static_cast<int>(threadIdx.x) < nch ? cnt_ld : 0;
   // (chunk indices clamped, so the loads are unconditional)
   uint2 pre[8][PX];
-  const int clast = nch > 0 ? nch - 1 : 0;
+  const int clast = a.nchunks > 0 ? a.nchunks - 1 : 0;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int c = min(wave + u * NW, clast);
